@@ -1,0 +1,286 @@
+/*
+ * Plain CPU oracle for the BitNet b1.58 BitLinear forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The product path (the
+ * HIP library) never calls it and shares no code, header, table or helper
+ * with it; both sides are written independently from the method's definition
+ * and from the packed-format specification.
+ *
+ * Everything here is the plain definition written out: straight loops, no
+ * intrinsics, no blocking, no fusion.  Built with -ffp-contract=off and no
+ * fast-math, so every float operation below is one IEEE-754 operation in
+ * round-to-nearest-even, in the order written.
+ *
+ * What each function follows (page title, then section):
+ *  - oracle_absmean, oracle_ternarize:
+ *      "Key Technologies Enabling the BitNET Family", Advanced Quantization
+ *      Methodologies (absmean ternary weights);
+ *      "BitNet / Ternary / Binary - Les LLMs 1-bit", Apercu de l'entrainement
+ *      d'un BitLinear (beta = mean |w|; clamp(round(w / (beta + 1e-8)), -1, 1)).
+ *  - oracle_quant_act:
+ *      "Key Technologies Enabling the BitNET Family", Advanced Quantization
+ *      Methodologies (8-bit activations, absmax, per token); Hacker News
+ *      Reader item 39537919 (activations are int8 at inference).
+ *  - oracle_matmul_i32:
+ *      "BitNet / Ternary / Binary - Les LLMs 1-bit", TL;DR and Mecanisme
+ *      technique (products become add / subtract / skip); Hacker News Reader
+ *      item 39537919, the reply that corrects the "elementwise additions"
+ *      wording (sum of activations with weight +1 minus those with weight -1).
+ *  - oracle_dequant_f32, oracle_f32_to_bf16: rescaling by the two quantizer
+ *      scales; implied by the quantizer pair above, not printed on the pages.
+ *  - oracle_pack_t2 / oracle_unpack_t2: 2 bits per ternary weight
+ *      ("BitNet Technical Notes", Appendix glossary: bit-packing at 2 bits per
+ *      ternary weight; "BitNet: Inference framework for 1-bit LLMs", post #139:
+ *      two bits hold a spare fourth value).  The bit layout itself is this
+ *      project's own choice and is written here from its specification.
+ *
+ * Readings where the pages are silent (each stated in the design notes):
+ *  - beta: mean |w| in fp64, summed in a fixed order (consecutive chunks of
+ *    4096 elements in row-major order, each chunk summed in index order, the
+ *    chunk sums added in ascending chunk order), then rounded once to fp32.
+ *  - rounding: half to even (torch.round semantics, the IEEE default).
+ *  - activations: gamma = max |x|; g = max(gamma, 1e-5); q = clamp(rint(x *
+ *    (127 / g)), -127, 127); ds = g / 127.
+ *  - dequant: y = (float)acc * (ds * beta).
+ *
+ * Parity status: every function here is pinned by the CPU test suite
+ * (hand-worked example, brute force, closed forms, invariants, the pages'
+ * popcount forms); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_BETA_CHUNK 4096
+#define ORACLE_EPS_W 1e-8f
+#define ORACLE_EPS_X 1e-5f
+
+/* ---------------------------------------------------------------- weights */
+
+/* beta = mean |w| over the whole tensor (per-tensor, no grouping). */
+float oracle_absmean(const float *w, int64_t count)
+{
+    double total = 0.0;
+    for (int64_t c0 = 0; c0 < count; c0 += ORACLE_BETA_CHUNK) {
+        int64_t c1 = c0 + ORACLE_BETA_CHUNK;
+        if (c1 > count)
+            c1 = count;
+        double part = 0.0;
+        for (int64_t i = c0; i < c1; ++i)
+            part += fabs((double)w[i]);
+        total += part;
+    }
+    return (float)(total / (double)count);
+}
+
+/* t = clamp(round_half_even(w / (beta + 1e-8)), -1, 1), elementwise. */
+void oracle_ternarize(const float *w, int64_t count, float beta, int8_t *t)
+{
+    float d = beta + ORACLE_EPS_W;
+    for (int64_t i = 0; i < count; ++i) {
+        float r = rintf(w[i] / d);
+        if (r > 1.0f)
+            r = 1.0f;
+        if (r < -1.0f)
+            r = -1.0f;
+        t[i] = (int8_t)r;
+    }
+}
+
+/* ------------------------------------------------------------ activations */
+
+static float bf16_bits_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static void quant_row(const float *x, int64_t K, int8_t *q, float *ds, int32_t *rowsum)
+{
+    float gamma = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        float a = fabsf(x[k]);
+        if (a > gamma)
+            gamma = a;
+    }
+    float g = gamma > ORACLE_EPS_X ? gamma : ORACLE_EPS_X;
+    float qs = 127.0f / g;
+    int32_t s = 0;
+    for (int64_t k = 0; k < K; ++k) {
+        float v = rintf(x[k] * qs);
+        if (v > 127.0f)
+            v = 127.0f;
+        if (v < -127.0f)
+            v = -127.0f;
+        q[k] = (int8_t)v;
+        s += q[k];
+    }
+    *ds = g / 127.0f;
+    *rowsum = s;
+}
+
+/* Per-token absmax int8 quantization of fp32 activations x[M][K]. */
+void oracle_quant_act_f32(const float *x, int64_t M, int64_t K, int8_t *q, float *ds,
+                          int32_t *rowsum)
+{
+    for (int64_t m = 0; m < M; ++m)
+        quant_row(x + m * K, K, q + m * K, ds + m, rowsum + m);
+}
+
+/* Same, for activations given as bf16 bit patterns (converted exactly). */
+void oracle_quant_act_bf16(const uint16_t *xb, int64_t M, int64_t K, int8_t *q, float *ds,
+                           int32_t *rowsum)
+{
+    float *row = (float *)malloc((size_t)(K > 0 ? K : 1) * sizeof(float));
+    if (!row)
+        return;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t k = 0; k < K; ++k)
+            row[k] = bf16_bits_to_f32(xb[m * K + k]);
+        quant_row(row, K, q + m * K, ds + m, rowsum + m);
+    }
+    free(row);
+}
+
+/* -------------------------------------------------------------- products */
+
+/* acc[m][n] = sum_k q[m][k] * t[n][k]   (naive triple loop, exact int32).
+ * threads > 1 splits the n loop over OpenMP threads (timing only; the
+ * result does not depend on it). */
+void oracle_matmul_i32(const int8_t *q, const int8_t *t, int64_t M, int64_t N, int64_t K,
+                       int32_t *acc, int threads)
+{
+    if (threads < 1)
+        threads = 1;
+#pragma omp parallel for num_threads(threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t m = 0; m < M; ++m) {
+            int32_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int32_t)q[m * K + k] * (int32_t)t[n * K + k];
+            acc[m * N + n] = s;
+        }
+}
+
+/* The same sums for a list of (m, n) pairs only (large shapes, sampled). */
+void oracle_matmul_i32_pairs(const int8_t *q, const int8_t *t, int64_t K, const int64_t *ms,
+                             const int64_t *ns, int64_t count, int32_t *out)
+{
+    for (int64_t p = 0; p < count; ++p) {
+        const int8_t *qa = q + ms[p] * K;
+        const int8_t *ta = t + ns[p] * K;
+        int32_t s = 0;
+        for (int64_t k = 0; k < K; ++k)
+            s += (int32_t)qa[k] * (int32_t)ta[k];
+        out[p] = s;
+    }
+}
+
+/* y[m][n] = (float)acc[m][n] * (ds[m] * beta). */
+void oracle_dequant_f32(const int32_t *acc, const float *ds, float beta, int64_t M, int64_t N,
+                        float *y)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        float s = ds[m] * beta;
+        for (int64_t n = 0; n < N; ++n)
+            y[m * N + n] = (float)acc[m * N + n] * s;
+    }
+}
+
+/* fp32 -> bf16 bit pattern, round to nearest, ties to even. */
+void oracle_f32_to_bf16(const float *y, int64_t count, uint16_t *out)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        uint32_t u;
+        memcpy(&u, &y[i], sizeof u);
+        if ((u & 0x7fffffffu) > 0x7f800000u) { /* NaN: keep it a quiet NaN */
+            out[i] = (uint16_t)((u >> 16) | 0x0040u);
+            continue;
+        }
+        uint32_t lower = u & 0xffffu;
+        uint32_t upper = u >> 16;
+        if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+            upper += 1u;
+        out[i] = (uint16_t)upper;
+    }
+}
+
+/* ------------------------------------------------------- packed formats
+ *
+ * Format T2 (2 bits per weight).  Weights W[N][K] are cut into tiles of
+ * 16 rows x 256 columns; tile (nb, kb) is 1024 bytes at byte offset
+ * (nb * ceil(K/256) + kb) * 1024.  Inside a tile, byte 16*L + 4*d + b
+ * (L in 0..63, d in 0..3, b in 0..3) holds four 2-bit fields; field i
+ * (bits 2i and 2i+1) is the code of weight
+ *     n = 16*nb + (L mod 16),
+ *     k = 256*kb + 64*i + 16*(L div 16) + 4*d + b.
+ * Code: +1 -> 01, 0 -> 00, -1 -> 11 (two's complement of t in two bits);
+ * 10 is never written.  Positions with n >= N or k >= K hold 00.
+ */
+int64_t oracle_t2_bytes(int64_t N, int64_t K)
+{
+    return ((N + 15) / 16) * ((K + 255) / 256) * 1024;
+}
+
+void oracle_pack_t2(const int8_t *t, int64_t N, int64_t K, uint8_t *packed)
+{
+    int64_t Kt = (K + 255) / 256;
+    memset(packed, 0, (size_t)oracle_t2_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t nb = n / 16, kb = k / 256;
+            int64_t r = n % 16, c = k % 256;
+            int64_t i = c / 64, g = (c % 64) / 16, d = (c % 16) / 4, b = c % 4;
+            int64_t L = 16 * g + r;
+            int64_t byte = (nb * Kt + kb) * 1024 + 16 * L + 4 * d + b;
+            uint8_t code = (uint8_t)(t[n * K + k] & 3);
+            packed[byte] |= (uint8_t)(code << (2 * i));
+        }
+}
+
+/* Inverse of oracle_pack_t2.  Returns the number of fields holding the
+ * never-written code 10 (0 for a well-formed buffer); such fields decode
+ * as 0 here. */
+int64_t oracle_unpack_t2(const uint8_t *packed, int64_t N, int64_t K, int8_t *t)
+{
+    int64_t Kt = (K + 255) / 256, bad = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t nb = n / 16, kb = k / 256;
+            int64_t r = n % 16, c = k % 256;
+            int64_t i = c / 64, g = (c % 64) / 16, d = (c % 16) / 4, b = c % 4;
+            int64_t L = 16 * g + r;
+            int64_t byte = (nb * Kt + kb) * 1024 + 16 * L + 4 * d + b;
+            int code = (packed[byte] >> (2 * i)) & 3;
+            if (code == 1)
+                t[n * K + k] = 1;
+            else if (code == 3)
+                t[n * K + k] = -1;
+            else {
+                if (code == 2)
+                    ++bad;
+                t[n * K + k] = 0;
+            }
+        }
+    return bad;
+}
+
+/* --------------------------------------------------------- whole forward */
+
+/* y = dequant(Q(x) . T(w)^T): the BitLinear forward for bf16 activations
+ * x[M][K] and latent weights w[N][K].  Writes the intermediate values too
+ * (any of q, ds, rowsum, t, acc may be used by the caller for checks). */
+void oracle_bitlinear_forward(const uint16_t *xb, int64_t M, int64_t K, const float *w, int64_t N,
+                              int8_t *q, float *ds, int32_t *rowsum, int8_t *t, float *beta,
+                              int32_t *acc, float *y, int threads)
+{
+    *beta = oracle_absmean(w, N * K);
+    oracle_ternarize(w, N * K, *beta, t);
+    oracle_quant_act_bf16(xb, M, K, q, ds, rowsum);
+    oracle_matmul_i32(q, t, M, N, K, acc, threads);
+    oracle_dequant_f32(acc, ds, *beta, M, N, y);
+}

@@ -1,0 +1,436 @@
+"""Pins for the CPU oracle: checks that do not re-use the oracle's own code.
+
+Each test ties one oracle function to something fixed outside it: the
+hand-worked example, exact rational arithmetic, closed forms of the Gaussian
+workload, textbook identities, independent library routines (numpy / torch)
+or the pages' own popcount formulations of the ternary product.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+
+def f32(v):
+    return np.float32(v)
+
+
+def next_up(v):
+    return np.nextafter(np.float32(v), np.float32(np.inf))
+
+
+# ------------------------------------------------------------- hand example
+@pytest.fixture(scope="module")
+def hand(golden_dir):
+    with open(os.path.join(golden_dir, "hand_4x4.json")) as f:
+        return json.load(f)
+
+
+def test_hand_example_every_step(hand):
+    w = np.array(hand["w"], dtype=np.float32)
+    x = np.array(hand["x"], dtype=np.float32)
+    beta = oracle.absmean(w)
+    assert beta == f32(hand["beta"])
+    t = oracle.ternarize(w, beta)
+    np.testing.assert_array_equal(t, np.array(hand["t"]))
+    # round-half-to-even is pinned: half-away-from-zero gives different codes
+    assert not np.array_equal(t, np.array(hand["t_if_half_away_from_zero"]))
+    q, ds, rs = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, np.array(hand["q"]))
+    assert not np.array_equal(q, np.array(hand["q_if_half_away_from_zero"]))
+    np.testing.assert_array_equal(ds, np.array(hand["ds"], dtype=np.float32))
+    np.testing.assert_array_equal(rs, np.array(hand["rowsum"]))
+    acc = oracle.matmul_i32(q, t)
+    np.testing.assert_array_equal(acc, np.array(hand["acc"]))
+    y = oracle.dequant(acc, ds, beta)
+    np.testing.assert_array_equal(y, np.array(hand["y"], dtype=np.float32))
+
+
+def test_hand_example_through_bf16_entry(hand):
+    x = np.array(hand["x"], dtype=np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)  # every value is bf16-exact
+    assert np.array_equal(workloads.bf16_bits_to_f32(xb), x)
+    out = oracle.bitlinear_forward(xb, np.array(hand["w"], dtype=np.float32))
+    np.testing.assert_array_equal(out["y"], np.array(hand["y"], dtype=np.float32))
+    np.testing.assert_array_equal(out["acc"], np.array(hand["acc"]))
+
+
+# --------------------------------------------------------------------- beta
+def exact_mean_f32(w):
+    """Exact rational mean of |w|, correctly rounded to fp32 (via Fraction)."""
+    s = sum(Fraction(float(abs(v))) for v in w.ravel())
+    m = s / w.size
+    lo = np.float32(float(m))  # double rounding can be off by one fp32 ulp
+    best = min((lo, np.nextafter(lo, np.float32(-1)), np.nextafter(lo, np.float32(2))),
+               key=lambda c: abs(Fraction(float(c)) - m))
+    return best
+
+
+@pytest.mark.parametrize("count", [1, 7, 4096, 4097, 3 * 4096 + 17])
+def test_absmean_vs_exact_rational(count):
+    rng = np.random.default_rng(count)
+    w = (rng.standard_normal(count) * 0.02).astype(np.float32)
+    assert abs(int(oracle.absmean(w).view(np.int32)) - int(exact_mean_f32(w).view(np.int32))) <= 1
+
+
+def test_absmean_vs_numpy_fp64_mean():
+    w = workloads.gen_weights(512, 512, seed=0)
+    ref = np.float32(np.mean(np.abs(w.astype(np.float64))))
+    assert abs(int(oracle.absmean(w).view(np.int32)) - int(ref.view(np.int32))) <= 1
+
+
+def test_absmean_symmetry_and_exact_scaling():
+    w = workloads.gen_weights(64, 300, seed=3)
+    b = oracle.absmean(w)
+    assert oracle.absmean(-w) == b
+    assert oracle.absmean(w * np.float32(2.0)) == np.float32(2.0) * b
+    assert oracle.absmean(w * np.float32(0.25)) == np.float32(0.25) * b
+
+
+def test_absmean_constant_tensor():
+    assert oracle.absmean(np.full(10000, -0.375, dtype=np.float32)) == f32(0.375)
+    assert oracle.absmean(np.zeros(100, dtype=np.float32)) == f32(0.0)
+
+
+def test_absmean_closed_form_gaussian():
+    # E|w| = sigma * sqrt(2/pi); sd of the mean = sigma*sqrt(1-2/pi)/sqrt(n)
+    n_rows, k = 512, 512
+    w = workloads.gen_weights(n_rows, k, seed=0)
+    sigma = workloads.W_STD
+    mean = sigma * math.sqrt(2.0 / math.pi)
+    sd = sigma * math.sqrt(1.0 - 2.0 / math.pi) / math.sqrt(n_rows * k)
+    assert abs(float(oracle.absmean(w)) - mean) < 5 * sd
+
+
+# ---------------------------------------------------------------- ternarize
+def test_ternarize_ties_round_half_even():
+    beta = f32(0.5)  # d = 0.5 exactly
+    w = np.array([0.25, -0.25, 0.75, -0.75, 1.25, -1.25, 0.0, -0.0, 0.1, 5.0, -5.0],
+                 dtype=np.float32)
+    # w/d = 0.5 -> 0, -0.5 -> 0, 1.5 -> 2 -> 1, -1.5 -> -1, 2.5 -> 2 -> 1, ...
+    np.testing.assert_array_equal(oracle.ternarize(w, beta), [0, 0, 1, -1, 1, -1, 0, 0, 0, 1, -1])
+
+
+def test_ternarize_epsilon_matters_at_workload_scale():
+    # at beta ~ 0.016 an ulp is ~1.9e-9, so the +1e-8 moves d by several ulps;
+    # an element at w = d_without_eps / 2 rounds differently with and without it
+    beta = f32(0.016)
+    d = f32(beta + f32(1e-8))
+    assert d != beta
+    w_tie_noeps = f32(beta * f32(0.5))  # exactly beta/2 (power-of-two scaling)
+    # w/beta = 0.5 exactly -> 0 either way; take the next float up: w/beta > 0.5
+    w = next_up(w_tie_noeps)
+    assert w / beta > f32(0.5)
+    assert np.rint(w / beta) == 1.0   # without the guard the code would be +1
+    assert oracle.ternarize(np.array([w]), beta)[0] == 0  # with it, w/d < 0.5
+
+
+def test_ternarize_zero_tensor():
+    w = np.zeros((4, 8), dtype=np.float32)
+    beta = oracle.absmean(w)
+    assert beta == 0.0
+    assert not oracle.ternarize(w, beta).any()
+
+
+def test_ternarize_invariants_gaussian():
+    w = workloads.gen_weights(512, 512, seed=0)
+    beta = oracle.absmean(w)
+    t = oracle.ternarize(w, beta)
+    assert set(np.unique(t)) <= {-1, 0, 1}
+    # sign(t) is sign(w) or 0
+    assert np.all((t == 0) | (np.sign(t) == np.sign(w)))
+    # monotone in w: sorting w sorts t
+    order = np.argsort(w.ravel(), kind="stable")
+    assert np.all(np.diff(t.ravel()[order].astype(np.int32)) >= 0)
+    # scale invariance (exact for power-of-two scales)
+    np.testing.assert_array_equal(oracle.ternarize(w * np.float32(8), oracle.absmean(w * np.float32(8))), t)
+    # zero fraction: P(|w| < beta/2) = 2*Phi(sqrt(2/pi)/2) - 1 = 0.31006 for Gaussian w
+    p0 = math.erf(math.sqrt(2.0 / math.pi) / 2.0 / math.sqrt(2.0))
+    n = t.size
+    assert abs(float(np.mean(t == 0)) - p0) < 5 * math.sqrt(p0 * (1 - p0) / n)
+
+
+def test_ternarize_against_torch_round():
+    # torch.round is half-to-even; an independent library routine for the codes
+    w = workloads.gen_weights(128, 384, seed=11)
+    beta = oracle.absmean(w)
+    ref = torch.clamp(torch.round(torch.from_numpy(w) / (torch.tensor(beta) + torch.tensor(1e-8, dtype=torch.float32))), -1, 1)
+    np.testing.assert_array_equal(oracle.ternarize(w, beta), ref.numpy().astype(np.int8))
+
+
+# ---------------------------------------------------------- activation quant
+def test_quant_act_exact_rational_bound():
+    x = workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(6, 700, seed=5, outliers=True))
+    q, ds, rs = oracle.quant_act(x)
+    for m in range(x.shape[0]):
+        gamma = float(np.max(np.abs(x[m])))
+        assert ds[m] == np.float32(np.float32(gamma) / np.float32(127.0))
+        for k in range(0, x.shape[1], 7):
+            r = Fraction(float(x[m, k])) * 127 / Fraction(gamma)
+            # fp32 rounding of 127/gamma and of the product stays far below 1/2
+            assert abs(Fraction(int(q[m, k])) - r) <= Fraction(1, 2) + Fraction(1, 10**4)
+        assert rs[m] == int(q[m].astype(np.int64).sum())
+
+
+def test_quant_act_invariants():
+    xb = workloads.gen_acts_bf16(16, 2560, seed=1, outliers=True)
+    x = workloads.bf16_bits_to_f32(xb)
+    q, ds, rs = oracle.quant_act(xb, bf16_bits=True)
+    q2, ds2, rs2 = oracle.quant_act(x)
+    np.testing.assert_array_equal(q, q2)
+    np.testing.assert_array_equal(ds, ds2)
+    assert q.min() >= -127 and q.max() <= 127
+    for m in range(x.shape[0]):
+        am = np.argmax(np.abs(x[m]))
+        assert abs(int(q[m, am])) == 127 and np.sign(q[m, am]) == np.sign(x[m, am])
+    assert np.all(np.sign(q) * np.sign(x) >= 0)  # never flips sign
+    assert np.all(q[x == 0] == 0)
+    err = np.abs(x - q.astype(np.float32) * ds[:, None])
+    assert np.all(err <= ds[:, None] * 0.5 * (1 + 1e-5))
+    for m in range(4):  # monotone within a token
+        order = np.argsort(x[m], kind="stable")
+        assert np.all(np.diff(q[m, order].astype(np.int32)) >= 0)
+
+
+def test_quant_act_zero_row_and_ties():
+    x = np.zeros((2, 5), dtype=np.float32)
+    x[1] = [254.0, 5.0, -3.0, 1.0, -1.0]
+    q, ds, rs = oracle.quant_act(x)
+    assert not q[0].any() and rs[0] == 0
+    assert ds[0] == np.float32(np.float32(1e-5) / np.float32(127.0))
+    np.testing.assert_array_equal(q[1], [127, 2, -2, 0, 0])  # 2.5->2, -1.5->-2, +-0.5->0
+
+
+# ------------------------------------------------------------------ products
+def brute_acc(q, t):
+    M, K = q.shape
+    N = t.shape[0]
+    return [[sum(int(q[m][k]) * int(t[n][k]) for k in range(K)) for n in range(N)] for m in range(M)]
+
+
+def addsub_skip(qrow, trow):
+    """The pages' form: activations where w=+1, minus those where w=-1, others skipped."""
+    s = 0
+    for a, w in zip(qrow, trow):
+        if w == 1:
+            s += int(a)
+        elif w == -1:
+            s -= int(a)
+    return s
+
+
+def masks(vals):
+    plus = sum(1 << i for i, v in enumerate(vals) if v == 1)
+    minus = sum(1 << i for i, v in enumerate(vals) if v == -1)
+    return plus, minus
+
+
+def popc(v):
+    return bin(v).count("1")
+
+
+def dot_sign_value(a, b):
+    """Sign/value 2-bit code, popcount form (post #132 of the BitNet HN thread)."""
+    va, sa = masks(a)[0] | masks(a)[1], masks(a)[1]
+    vb, sb = masks(b)[0] | masks(b)[1], masks(b)[1]
+    actv = va & vb
+    sign = sa ^ sb
+    return popc(actv & ~sign) - popc(actv & sign)
+
+
+def dot_bitplanes(a, b):
+    """Two bit-planes per operand: Cp=(Ap&Bp)|(An&Bn), Cn=(An&Bp)|(Ap&Bn)."""
+    ap, an = masks(a)
+    bp, bn = masks(b)
+    cp = (ap & bp) | (an & bn)
+    cn = (an & bp) | (ap & bn)
+    return popc(cp) - popc(cn)
+
+
+def dot_sign_magnitude(a, b):
+    """sum = popcount(mag) - 2*popcount(mag & sgn) with mag = Am&Bm, sgn = As^Bs."""
+    ap, an = masks(a)
+    bp, bn = masks(b)
+    mag = (ap | an) & (bp | bn)
+    sgn = an ^ bn
+    return popc(mag) - 2 * popc(mag & sgn)
+
+
+def dot_int8_bitplanes(qrow, trow):
+    """int8 activations as two's-complement bit-planes against +1/-1 weight masks."""
+    plus, minus = masks(trow)
+    total = 0
+    for bit in range(8):
+        plane = sum(1 << i for i, v in enumerate(qrow) if (int(v) & 0xFF) >> bit & 1)
+        weight = -(1 << 7) if bit == 7 else (1 << bit)
+        total += weight * (popc(plus & plane) - popc(minus & plane))
+    return total
+
+
+def test_matmul_brute_and_pages_forms_ternary_acts():
+    rng = np.random.default_rng(7)
+    for K in (1, 3, 31, 64, 65):
+        q = rng.integers(-1, 2, size=(3, K)).astype(np.int8)
+        t = rng.integers(-1, 2, size=(5, K)).astype(np.int8)
+        acc = oracle.matmul_i32(q, t)
+        assert acc.tolist() == brute_acc(q, t)
+        for m in range(3):
+            for n in range(5):
+                a, b = q[m].tolist(), t[n].tolist()
+                assert acc[m, n] == addsub_skip(a, b)
+                assert acc[m, n] == dot_sign_value(a, b)
+                assert acc[m, n] == dot_bitplanes(a, b)
+                assert acc[m, n] == dot_sign_magnitude(a, b)
+
+
+def test_matmul_int8_acts_brute_and_bitplanes():
+    rng = np.random.default_rng(8)
+    q = rng.integers(-127, 128, size=(4, 97)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(6, 97)).astype(np.int8)
+    acc = oracle.matmul_i32(q, t)
+    assert acc.tolist() == brute_acc(q, t)
+    for m in range(4):
+        for n in range(6):
+            assert acc[m, n] == addsub_skip(q[m], t[n])
+            assert acc[m, n] == dot_int8_bitplanes(q[m].tolist(), t[n].tolist())
+
+
+def test_matmul_exhaustive_k4():
+    # every ternary row of length 4 against every activation row over {-127,-1,0,1,127}^4
+    import itertools
+    trows = np.array(list(itertools.product((-1, 0, 1), repeat=4)), dtype=np.int8)
+    qrows = np.array(list(itertools.product((-127, -1, 0, 1, 127), repeat=4)), dtype=np.int8)
+    acc = oracle.matmul_i32(qrows, trows)
+    ref = qrows.astype(np.int64) @ trows.astype(np.int64).T
+    np.testing.assert_array_equal(acc, ref)
+
+
+def test_matmul_extremes_no_overflow():
+    K = 28672
+    q = np.full((2, K), 127, dtype=np.int8)
+    q[1] = -127
+    t = np.ones((3, K), dtype=np.int8)
+    t[1] = -1
+    t[2, ::2] = 0
+    acc = oracle.matmul_i32(q, t, threads=4)
+    np.testing.assert_array_equal(acc, [[127 * K, -127 * K, 127 * K // 2], [-127 * K, 127 * K, -127 * K // 2]])
+
+
+def test_matmul_threads_and_pairs_agree():
+    rng = np.random.default_rng(9)
+    q = rng.integers(-127, 128, size=(5, 300)).astype(np.int8)
+    t = rng.integers(-1, 2, size=(40, 300)).astype(np.int8)
+    a1 = oracle.matmul_i32(q, t, threads=1)
+    a4 = oracle.matmul_i32(q, t, threads=4)
+    np.testing.assert_array_equal(a1, a4)
+    np.testing.assert_array_equal(a1, q.astype(np.int64) @ t.astype(np.int64).T)
+    ms = rng.integers(0, 5, size=50)
+    ns = rng.integers(0, 40, size=50)
+    np.testing.assert_array_equal(oracle.matmul_i32_pairs(q, t, ms, ns), a1[ms, ns])
+
+
+# ------------------------------------------------------------------- dequant
+def test_dequant_error_bound_and_zero():
+    rng = np.random.default_rng(10)
+    acc = rng.integers(-3_000_000, 3_000_000, size=(3, 50)).astype(np.int32)
+    acc[0, :5] = 0
+    ds = rng.uniform(0.01, 1.0, size=3).astype(np.float32)
+    beta = np.float32(0.0159)
+    y = oracle.dequant(acc, ds, beta)
+    assert np.all(y[0, :5] == 0)
+    exact = acc.astype(np.float64) * ds.astype(np.float64)[:, None] * float(beta)
+    rel = np.abs(y.astype(np.float64) - exact) / np.maximum(np.abs(exact), 1e-30)
+    assert np.all(rel[acc != 0] <= 2.0 ** -23)  # two roundings of half an ulp each
+
+
+def test_bf16_rounding_against_torch():
+    rng = np.random.default_rng(12)
+    y = np.concatenate([
+        rng.standard_normal(5000).astype(np.float32) * 100,
+        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0, -0.0, np.inf, -np.inf,
+                  1e-40, -1e-40, 3.4e38], dtype=np.float32),
+    ])
+    ref = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.to_bf16_bits(y), ref)
+    nan = oracle.to_bf16_bits(np.array([np.nan], dtype=np.float32))
+    assert (nan[0] & 0x7F80) == 0x7F80 and (nan[0] & 0x7F) != 0
+
+
+# ------------------------------------------------------------------- packing
+def test_pack_layout_single_weights():
+    # a single nonzero weight lands exactly where the format specification says
+    N, K = 35, 700
+    Kt = (K + 255) // 256
+    for (n, k, tv) in [(0, 0, 1), (0, 1, -1), (17, 255, 1), (34, 699, -1), (5, 64 + 16 + 4 + 1, 1),
+                       (20, 256 + 3 * 64 + 2 * 16 + 3 * 4 + 2, -1)]:
+        t = np.zeros((N, K), dtype=np.int8)
+        t[n, k] = tv
+        p = oracle.pack_t2(t)
+        nb, kb, r, c = n // 16, k // 256, n % 16, k % 256
+        i, g, d, b = c // 64, (c % 64) // 16, (c % 16) // 4, c % 4
+        byte = (nb * Kt + kb) * 1024 + 16 * (16 * g + r) + 4 * d + b
+        expect = np.zeros_like(p)
+        expect[byte] = (1 if tv == 1 else 3) << (2 * i)
+        np.testing.assert_array_equal(p, expect)
+
+
+def test_pack_exhaustive_byte_patterns_round_trip():
+    import itertools
+    # four weights sharing one byte: k = b + 64*i for i in 0..3 (same n, g, d, b)
+    for b in (0, 3):
+        for combo in itertools.product((-1, 0, 1), repeat=4):
+            t = np.zeros((1, 256), dtype=np.int8)
+            for i, v in enumerate(combo):
+                t[0, 64 * i + b] = v
+            p = oracle.pack_t2(t)
+            assert np.count_nonzero(p) <= 1
+            back, bad = oracle.unpack_t2(p, 1, 256)
+            assert bad == 0
+            np.testing.assert_array_equal(back, t)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (16, 256), (17, 257), (50, 700), (64, 2560)])
+def test_pack_round_trip_random(N, K):
+    rng = np.random.default_rng(N * 1000 + K)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    p = oracle.pack_t2(t)
+    assert p.size == ((N + 15) // 16) * ((K + 255) // 256) * 1024 == oracle.t2_bytes(N, K)
+    back, bad = oracle.unpack_t2(p, N, K)
+    assert bad == 0
+    np.testing.assert_array_equal(back, t)
+    # no field ever holds the unused code 10
+    fields = np.stack([(p >> s) & 3 for s in (0, 2, 4, 6)])
+    assert not np.any(fields == 2)
+    # padding holds only zero codes: count nonzero fields == count nonzero weights
+    assert int(np.count_nonzero(fields)) == int(np.count_nonzero(t))
+
+
+def test_unpack_reports_invalid_code():
+    p = np.zeros(1024, dtype=np.uint8)
+    p[0] = 0b10
+    t, bad = oracle.unpack_t2(p, 16, 256)
+    assert bad == 1 and not t.any()
+
+
+# ------------------------------------------------------------ whole forward
+def test_forward_single_4x512():
+    lin = workloads.SINGLE_4x512.linears[0]
+    w = workloads.gen_weights(lin.N, lin.K, seed=0)
+    xb = workloads.gen_acts_bf16(lin.M, lin.K, seed=1)
+    out = oracle.bitlinear_forward(xb, w)
+    x = workloads.bf16_bits_to_f32(xb).astype(np.float64)
+    # the quantized product approximates the fp64 product of x and beta*t
+    approx = x @ (float(out["beta"]) * out["t"].astype(np.float64)).T
+    err = np.abs(out["y"] - approx)
+    # per element the int8 rounding error is at most ds/2 per term
+    bound = (out["ds"][:, None].astype(np.float64) / 2) * float(out["beta"]) * np.abs(out["t"]).sum(1)[None, :]
+    assert np.all(err <= bound * (1 + 1e-6) + 1e-6)
+    np.testing.assert_array_equal(out["y_bf16"],
+                                  torch.from_numpy(out["y"]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
