@@ -1,0 +1,202 @@
+"""Python binding of libbitlinear: the BitNet b1.58 BitLinear forward on MI355X.
+
+Argument marshalling only.  Every function here forwards torch tensors' device
+pointers and the current HIP stream to the C ABI declared in
+``include/bitlinear.h`` and raises ``BitLinearError`` on a non-zero status.
+There is no fallback: if the HIP library is not built, every call raises.
+
+Functions carry the C names:
+    bitlinear_quant_act(x, x_q, x_ds, x_rowsum=None)
+    bitlinear_pack_weights(w, packed, w_beta, workspace)
+    bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
+    bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
+plus allocation helpers (``act_stride``, ``packed_bytes`` ...) and two
+conveniences that allocate outputs (``quant_act``, ``pack_weights``,
+``linear``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libbitlinear.so")
+
+OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
+F32, BF16, I32 = 0, 1, 2
+MAX_K, MAX_N, MAX_M, GEMV_MAX_M = 131072, 1 << 20, 1 << 20, 64
+
+EXPORTS = (
+    "bitlinear_version", "bitlinear_last_error", "bitlinear_act_stride", "bitlinear_packed_bytes",
+    "bitlinear_pack_workspace_bytes", "bitlinear_gemv_workspace_bytes",
+    "bitlinear_gemm_workspace_bytes", "bitlinear_quant_act", "bitlinear_pack_weights",
+    "bitlinear_gemv", "bitlinear_gemm",
+)
+
+_DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("status %d: %s" % (status, message))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libbitlinear.so is not built (%s); run "
+                          "`python -m bitlinear_matmul_02_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, p, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.bitlinear_version.restype = i32
+    L.bitlinear_version.argtypes = []
+    L.bitlinear_last_error.restype = ctypes.c_char_p
+    L.bitlinear_last_error.argtypes = []
+    for name in ("bitlinear_act_stride",):
+        getattr(L, name).restype = i64
+        getattr(L, name).argtypes = [i64]
+    for name in ("bitlinear_packed_bytes", "bitlinear_pack_workspace_bytes"):
+        getattr(L, name).restype = i64
+        getattr(L, name).argtypes = [i64, i64]
+    for name in ("bitlinear_gemv_workspace_bytes", "bitlinear_gemm_workspace_bytes"):
+        getattr(L, name).restype = i64
+        getattr(L, name).argtypes = [i64, i64, i64]
+    L.bitlinear_quant_act.restype = i32
+    L.bitlinear_quant_act.argtypes = [p, i32, i64, i64, p, p, p, p]
+    L.bitlinear_pack_weights.restype = i32
+    L.bitlinear_pack_weights.argtypes = [p, i64, i64, p, p, p, p]
+    for name in ("bitlinear_gemv", "bitlinear_gemm"):
+        getattr(L, name).restype = i32
+        getattr(L, name).argtypes = [p, p, i64, i64, p, p, i64, p, i32, p, sz, p]
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().bitlinear_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != OK:
+        raise BitLinearError(status, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# --------------------------------------------------------------- size helpers
+def act_stride(K: int) -> int:
+    return int(lib().bitlinear_act_stride(K))
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().bitlinear_packed_bytes(N, K))
+
+
+def pack_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().bitlinear_pack_workspace_bytes(N, K))
+
+
+def gemv_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().bitlinear_gemv_workspace_bytes(M, N, K))
+
+
+def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(lib().bitlinear_gemm_workspace_bytes(M, N, K))
+
+
+# --------------------------------------------------------------- the C calls
+def bitlinear_quant_act(x, x_q, x_ds, x_rowsum=None, stream=None) -> None:
+    """x [M][K] bf16/fp32 -> x_q [M][act_stride(K)] int8, x_ds [M] fp32, x_rowsum [M] int32."""
+    M, K = x.shape
+    _check(lib().bitlinear_quant_act(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(x_q), _ptr(x_ds),
+                                     _ptr(x_rowsum), _stream(stream)))
+
+
+def bitlinear_pack_weights(w, packed, w_beta, workspace, stream=None) -> None:
+    """w [N][K] fp32 latent weights -> packed 2-bit tiles + w_beta [1] fp32."""
+    N, K = w.shape
+    _check(lib().bitlinear_pack_weights(_ptr(w), N, K, _ptr(packed), _ptr(w_beta), _ptr(workspace),
+                                        _stream(stream)))
+
+
+def _product(fn, x_q, x_ds, M, K, packed, w_beta, N, y, workspace, stream):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(_ptr(x_q), _ptr(x_ds), M, K, _ptr(packed), _ptr(w_beta), N, _ptr(y), _DTYPE[y.dtype],
+              _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None) -> None:
+    """y [M][N] = dequant(x_q . T^T) for M <= 64 tokens (y dtype fp32, bf16 or int32)."""
+    _product(lib().bitlinear_gemv, x_q, x_ds, x_ds.shape[0], K, packed, w_beta, N, y, workspace,
+             stream)
+
+
+def bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None) -> None:
+    """The same product for any number of tokens, on the int8 matrix cores."""
+    _product(lib().bitlinear_gemm, x_q, x_ds, x_ds.shape[0], K, packed, w_beta, N, y, workspace,
+             stream)
+
+
+# ------------------------------------------------------------- conveniences
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor | None:
+    """A zero-filled workspace of at least nbytes, cached per device (not stream safe)."""
+    if nbytes <= 0:
+        return None
+    key = torch.device(device)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
+        _ws_cache[key] = buf
+    return buf
+
+
+def quant_act(x, with_rowsum: bool = False, stream=None):
+    M, K = x.shape
+    x_q = torch.empty((M, act_stride(K)), dtype=torch.int8, device=x.device)
+    x_ds = torch.empty((M,), dtype=torch.float32, device=x.device)
+    rs = torch.empty((M,), dtype=torch.int32, device=x.device) if with_rowsum else None
+    bitlinear_quant_act(x, x_q, x_ds, rs, stream)
+    return (x_q, x_ds, rs) if with_rowsum else (x_q, x_ds)
+
+
+def pack_weights(w, stream=None):
+    N, K = w.shape
+    packed = torch.empty((packed_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    beta = torch.empty((1,), dtype=torch.float32, device=w.device)
+    ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    bitlinear_pack_weights(w, packed, beta, ws, stream)
+    return packed, beta
+
+
+def linear(x, packed, w_beta, N: int, out_dtype=torch.float32, stream=None):
+    """BitLinear forward: quantize x [M][K], then gemv (M <= 64) or gemm."""
+    M, K = x.shape
+    x_q, x_ds = quant_act(x, stream=stream)
+    y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if M <= GEMV_MAX_M:
+        ws = workspace(gemv_workspace_bytes(M, N, K), x.device)
+        bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, ws, stream)
+    else:
+        ws = workspace(gemm_workspace_bytes(M, N, K), x.device)
+        bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, ws, stream)
+    return y

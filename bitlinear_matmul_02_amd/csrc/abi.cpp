@@ -1,0 +1,148 @@
+// C ABI of libbitlinear: argument validation, error reporting, dispatch.
+// Nothing here touches the GPU before every argument has been checked, so an
+// invalid call enqueues nothing (and works without a GPU present).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "bl_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return BITLINEAR_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BITLINEAR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool k_ok(int64_t K) { return K >= 1 && K <= BITLINEAR_MAX_K; }
+bool n_ok(int64_t N) { return N >= 1 && N <= BITLINEAR_MAX_N; }
+
+int64_t act_stride(int64_t K) { return bl::ceil_div(K, bl::kTileK) * bl::kTileK; }
+
+// Checks shared by gemv and gemm.
+int check_product(const char* fn, const int8_t* x_q, const float* x_ds, int64_t M, int64_t max_m,
+                  int64_t K, const void* packed, const float* w_beta, int64_t N, void* y,
+                  int y_dtype, void* ws, size_t ws_bytes, int64_t need_ws) {
+  if (M < 0 || M > max_m) return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld outside [0, %lld]", fn, (long long)M, (long long)max_m);
+  if (!k_ok(K)) return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld outside [1, %d]", fn, (long long)K, BITLINEAR_MAX_K);
+  if (!n_ok(N)) return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld outside [1, %d]", fn, (long long)N, BITLINEAR_MAX_N);
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+    return fail(BITLINEAR_ERR_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
+  if (M == 0) return BITLINEAR_OK;
+  if (!x_q || !x_ds || !packed || !w_beta || !y) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x_q, 16) || !aligned(packed, 16))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: x_q and packed must be 16-byte aligned", fn);
+  if (!aligned(x_ds, 4) || !aligned(w_beta, 4) || !aligned(y, y_dtype == BITLINEAR_BF16 ? 2 : 4))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: x_ds, w_beta or y not element aligned", fn);
+  if (need_ws > 0) {
+    if (!ws) return fail(BITLINEAR_ERR_ARG, "%s: this shape needs a %lld-byte workspace", fn, (long long)need_ws);
+    if ((int64_t)ws_bytes < need_ws)
+      return fail(BITLINEAR_ERR_ARG, "%s: workspace of %zu bytes, %lld needed", fn, ws_bytes, (long long)need_ws);
+    if (!aligned(ws, 16)) return fail(BITLINEAR_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+  }
+  return BITLINEAR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_version(void) { return (1 << 16) | 0; }
+
+const char* bitlinear_last_error(void) { return g_err; }
+
+int64_t bitlinear_act_stride(int64_t K) { return k_ok(K) ? act_stride(K) : -1; }
+
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K) {
+  if (!n_ok(N) || !k_ok(K)) return -1;
+  return bl::ceil_div(N, bl::kTileN) * bl::ceil_div(K, bl::kTileK) * bl::kTileBytes;
+}
+
+int64_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
+  if (!n_ok(N) || !k_ok(K)) return -1;
+  return 8 * bl::ceil_div(N * K, bl::kBetaChunk);
+}
+
+int64_t bitlinear_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || M > BITLINEAR_GEMV_MAX_M || !n_ok(N) || !k_ok(K)) return -1;
+  return M == 0 ? 0 : bl::gemv_ws_bytes(M, N, K);
+}
+
+int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || M > BITLINEAR_MAX_M || !n_ok(N) || !k_ok(K)) return -1;
+  return M == 0 ? 0 : bl::gemm_ws_bytes(M, N, K);
+}
+
+int bitlinear_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* x_q, float* x_ds,
+                        int32_t* x_rowsum, void* stream) {
+  const char* fn = "bitlinear_quant_act";
+  if (x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_F32)
+    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32", fn);
+  if (M < 0 || M > BITLINEAR_MAX_M) return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+  if (!k_ok(K)) return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld outside [1, %d]", fn, (long long)K, BITLINEAR_MAX_K);
+  if (M == 0) return ok();
+  if (!x || !x_q || !x_ds) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x, x_dtype == BITLINEAR_BF16 ? 2 : 4) || !aligned(x_q, 16) || !aligned(x_ds, 4) ||
+      (x_rowsum && !aligned(x_rowsum, 4)))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned pointer (x_q needs 16 bytes)", fn);
+  return hip_status(bl::launch_quant_act(x, x_dtype, M, K, act_stride(K), x_q, x_ds, x_rowsum,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, void* packed, float* w_beta,
+                           void* workspace, void* stream) {
+  const char* fn = "bitlinear_pack_weights";
+  if (!n_ok(N) || !k_ok(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld, K=%lld out of range", fn, (long long)N, (long long)K);
+  if (!w || !packed || !w_beta || !workspace) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(w, 4) || !aligned(packed, 16) || !aligned(w_beta, 4) || !aligned(workspace, 8))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bl::launch_pack_t2(w, N, K, static_cast<uint8_t*>(packed), w_beta,
+                                       static_cast<double*>(workspace), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_gemv(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed,
+                   const float* w_beta, int64_t N, void* y, int y_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const char* fn = "bitlinear_gemv";
+  const int64_t need = (M >= 1 && M <= BITLINEAR_GEMV_MAX_M && n_ok(N) && k_ok(K)) ? bl::gemv_ws_bytes(M, N, K) : 0;
+  int st = check_product(fn, x_q, x_ds, M, BITLINEAR_GEMV_MAX_M, K, packed, w_beta, N, y, y_dtype,
+                         workspace, workspace_bytes, need);
+  if (st != BITLINEAR_OK || M == 0) return st == BITLINEAR_OK ? ok() : st;
+  return hip_status(bl::launch_gemv_t2(x_q, act_stride(K), x_ds, M, K, static_cast<const uint8_t*>(packed),
+                                       w_beta, N, y, y_dtype, workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_gemm(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed,
+                   const float* w_beta, int64_t N, void* y, int y_dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const char* fn = "bitlinear_gemm";
+  const int64_t need = (M >= 1 && M <= BITLINEAR_MAX_M && n_ok(N) && k_ok(K)) ? bl::gemm_ws_bytes(M, N, K) : 0;
+  int st = check_product(fn, x_q, x_ds, M, BITLINEAR_MAX_M, K, packed, w_beta, N, y, y_dtype,
+                         workspace, workspace_bytes, need);
+  if (st != BITLINEAR_OK || M == 0) return st == BITLINEAR_OK ? ok() : st;
+  return hip_status(bl::launch_gemm_t2(x_q, act_stride(K), x_ds, M, K, static_cast<const uint8_t*>(packed),
+                                       w_beta, N, y, y_dtype, workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

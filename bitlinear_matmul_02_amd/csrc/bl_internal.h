@@ -1,0 +1,87 @@
+// Internal declarations shared by the HIP translation units of libbitlinear.
+// gfx950 only: wave64, int8 MFMA 16x16x64, correctly rounded fp32 division.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bitlinear.h"
+
+namespace bl {
+
+// Geometry of the 2-bit tiled weight format: a tile is 16 rows x 256 columns,
+// 1024 bytes, read by one wave as 64 lanes x 16 bytes.
+constexpr int kTileN = 16;
+constexpr int kTileK = 256;
+constexpr int kTileBytes = 1024;
+constexpr int kBetaChunk = 4096;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- launches
+// Each returns hipSuccess or the launch error; arguments are already valid.
+hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldq,
+                            int8_t* q, float* ds, int32_t* rowsum, hipStream_t s);
+
+hipError_t launch_pack_t2(const float* w, int64_t N, int64_t K, uint8_t* packed, float* beta,
+                          double* partials, hipStream_t s);
+
+// Decode-shaped product (M <= 64).  `ws` may be null when gemv_ws_bytes is 0.
+int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
+                          const uint8_t* packed, const float* beta, int64_t N, void* y,
+                          int y_dtype, void* ws, hipStream_t s);
+
+// Prefill-shaped product (any M).
+int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
+                          const uint8_t* packed, const float* beta, int64_t N, void* y,
+                          int y_dtype, void* ws, hipStream_t s);
+
+// ------------------------------------------------------- device helpers
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Field i of four packed words as MFMA int8 operand bytes: each output byte is
+// 64 * t (t in {-1, 0, 1}) because the 2-bit two's-complement code is moved to
+// the top two bits of its byte and the rest is masked off.
+__device__ inline v4i t2_field(const u4 w, int i) {
+  const int sh = 6 - 2 * i;
+  v4i r;
+  r.x = (int)((w.x << sh) & 0xC0C0C0C0u);
+  r.y = (int)((w.y << sh) & 0xC0C0C0C0u);
+  r.z = (int)((w.z << sh) & 0xC0C0C0C0u);
+  r.w = (int)((w.w << sh) & 0xC0C0C0C0u);
+  return r;
+}
+
+// One 16x16x64 int8 matrix-core step: acc += A(16x64) * B(64x16).
+__device__ inline v4i mfma16(v4i a, v4i b, v4i acc) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+}
+
+// Dequantize one accumulator (scaled by 64 by t2_field) and store it.
+__device__ inline void store_out(void* y, int y_dtype, int64_t idx, int acc64, float scale) {
+  const int acc = acc64 >> 6;  // exact: every term is a multiple of 64
+  if (y_dtype == BITLINEAR_I32) {
+    static_cast<int32_t*>(y)[idx] = acc;
+  } else {
+    const float v = (float)acc * scale;
+    if (y_dtype == BITLINEAR_F32)
+      static_cast<float*>(y)[idx] = v;
+    else
+      static_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
+  }
+}
+
+}  // namespace bl

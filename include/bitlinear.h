@@ -1,0 +1,160 @@
+/*
+ * bitlinear.h - C ABI of the MI355X (gfx950) BitNet b1.58 BitLinear forward.
+ *
+ * The operation is the BitLinear layer with ternary weights and 8-bit
+ * activations:
+ *   - weights: absmean ternarization, beta = mean |W| over the tensor and
+ *     T = clamp(round(W / (beta + 1e-8)), -1, 1)
+ *     ("Key Technologies Enabling the BitNET Family", Advanced Quantization
+ *     Methodologies; "BitNet / Ternary / Binary - Les LLMs 1-bit", Apercu de
+ *     l'entrainement d'un BitLinear);
+ *   - activations: per-token absmax quantization to int8 (same section of the
+ *     first page; Hacker News Reader item 39537919: int8 at inference);
+ *   - product: every weight adds, subtracts or skips one activation, summed in
+ *     int32 ("BitNet / Ternary / Binary - Les LLMs 1-bit", TL;DR; Hacker News
+ *     Reader item 39537919, the reply on summing activations with weight +1
+ *     minus those with weight -1);
+ *   - output: y = acc * (ds * beta), the inverse of both quantizer scales.
+ * The layer shape follows the page's BitLinear(in_features, out_features,
+ * bias=False): weights are [N][K] = [out][in], no bias, Y[M][N] = f(X[M][K]).
+ *
+ * Conventions for every call below
+ *   - Pointers to tensors are DEVICE pointers owned by the caller; the library
+ *     never frees or keeps them.  They must be 16-byte aligned unless a call
+ *     says otherwise.  Tensors are row-major and dense.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     compute call only enqueues work on it and returns; nothing synchronizes
+ *     with the host and nothing allocates device memory.
+ *   - Every call validates all arguments before enqueuing anything.  On error
+ *     it enqueues nothing, returns a negative status and
+ *     bitlinear_last_error() (per host thread) says why.  A launch failure
+ *     returns BITLINEAR_ERR_HIP.
+ *   - M = 0 (no tokens) is a valid no-op.  N = 0 or K = 0 is BITLINEAR_ERR_SHAPE.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ *   - Calls are thread-safe.  Calls sharing one workspace must not overlap.
+ */
+#ifndef BITLINEAR_H
+#define BITLINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BITLINEAR_OK 0
+#define BITLINEAR_ERR_ARG (-1)         /* null pointer, unknown dtype, short workspace */
+#define BITLINEAR_ERR_SHAPE (-2)       /* size outside the supported range */
+#define BITLINEAR_ERR_ALIGN (-3)       /* pointer not aligned as required */
+#define BITLINEAR_ERR_UNSUPPORTED (-4) /* valid request this build does not implement */
+#define BITLINEAR_ERR_HIP (-5)         /* the HIP runtime reported an error */
+
+/* Element types. */
+#define BITLINEAR_F32 0  /* IEEE fp32 */
+#define BITLINEAR_BF16 1 /* bfloat16, round-to-nearest-even when written */
+#define BITLINEAR_I32 2  /* raw int32 accumulators (output only) */
+
+/* Supported sizes. */
+#define BITLINEAR_MAX_K 131072       /* keeps 64 * 127 * K below 2^31 */
+#define BITLINEAR_MAX_N 1048576
+#define BITLINEAR_MAX_M 1048576
+#define BITLINEAR_GEMV_MAX_M 64
+
+/* Library version, (major << 16) | minor. */
+int bitlinear_version(void);
+
+/* Last error message of the calling host thread; never NULL. */
+const char *bitlinear_last_error(void);
+
+/*
+ * Bytes per row of the int8 activation buffer x_q: K rounded up to a multiple
+ * of 256.  Entries k >= K of each row are written as 0 by bitlinear_quant_act
+ * and must stay 0.  Returns -1 for K outside [1, BITLINEAR_MAX_K].
+ */
+int64_t bitlinear_act_stride(int64_t K);
+
+/*
+ * Size in bytes of the packed ternary weights for an N x K matrix:
+ * ceil(N/16) * ceil(K/256) * 1024 (2 bits per weight, padded to whole tiles).
+ * Returns -1 for N or K outside the supported range.
+ */
+int64_t bitlinear_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace bytes bitlinear_pack_weights needs: 8 * ceil(N*K / 4096). */
+int64_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * Workspace bytes bitlinear_gemv / bitlinear_gemm need for this shape (may be
+ * 0).  A workspace must be filled with zeros once before its first use; every
+ * call that returns BITLINEAR_OK leaves it filled with zeros again.
+ */
+int64_t bitlinear_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * Per-token absmax activation quantization.
+ *   x        [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32;
+ *            needs only element alignment (2 or 4 bytes).
+ *   x_q      [M][bitlinear_act_stride(K)] int8 out:
+ *            q = clamp(rint(x * (127 / g)), -127, 127), g = max(max_k |x|, 1e-5),
+ *            rint = round half to even; padding columns are written as 0.
+ *   x_ds     [M] fp32 out: g / 127 (the dequantization factor of the token).
+ *   x_rowsum [M] int32 out, sum_k q (may be NULL).
+ * Errors: ERR_ARG (null x/x_q/x_ds, unknown dtype), ERR_SHAPE (K or M out of
+ * range), ERR_ALIGN (x_q not 16-byte aligned, x not element aligned).
+ */
+int bitlinear_quant_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_t *x_q,
+                        float *x_ds, int32_t *x_rowsum, void *stream);
+
+/*
+ * Absmean ternarization and 2-bit packing of latent fp32 weights.
+ *   w         [N][K] fp32 latent weights (4-byte aligned).
+ *   packed    bitlinear_packed_bytes(N, K) bytes out, the tiled 2-bit format:
+ *             tile (nb, kb) of 16 rows x 256 columns is 1024 bytes at byte
+ *             offset (nb * ceil(K/256) + kb) * 1024; byte 16*L + 4*d + b of the
+ *             tile holds in bits 2i..2i+1 the code of weight
+ *             (n = 16*nb + L%16, k = 256*kb + 64*i + 16*(L/16) + 4*d + b),
+ *             code +1 -> 01, 0 -> 00, -1 -> 11; padding holds 00.
+ *   w_beta    [1] fp32 out: beta = mean |w|, summed in fp64 in a fixed order
+ *             (chunks of 4096 consecutive elements in row-major order, each
+ *             summed in index order, chunk sums added in ascending order) and
+ *             rounded once to fp32.  Codes use d = beta + 1e-8 (fp32),
+ *             t = clamp(rint(w / d), -1, 1).
+ *   workspace bitlinear_pack_workspace_bytes(N, K) bytes of scratch (8-byte
+ *             aligned; contents on entry do not matter).
+ * Errors: ERR_ARG (null pointer), ERR_SHAPE (N or K out of range), ERR_ALIGN.
+ */
+int bitlinear_pack_weights(const float *w, int64_t N, int64_t K, void *packed, float *w_beta,
+                           void *workspace, void *stream);
+
+/*
+ * Ternary matrix product with dequantization, for few tokens (decode).
+ *   x_q, x_ds  output of bitlinear_quant_act for M tokens and K inputs.
+ *   packed, w_beta  output of bitlinear_pack_weights for N x K weights.
+ *   y          [M][N] out, y_dtype BITLINEAR_F32 (y = acc * (ds * beta) in
+ *              fp32), BITLINEAR_BF16 (the same value rounded to nearest even)
+ *              or BITLINEAR_I32 (the raw accumulator acc = sum_k q * t).
+ *              Needs element alignment only.
+ *   workspace  bitlinear_gemv_workspace_bytes(M, N, K) bytes (NULL if 0).
+ * M must be in [0, BITLINEAR_GEMV_MAX_M].
+ * Errors: ERR_ARG, ERR_SHAPE, ERR_ALIGN as above.
+ */
+int bitlinear_gemv(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, const void *packed,
+                   const float *w_beta, int64_t N, void *y, int y_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/*
+ * The same product for any number of tokens (prefill), on the int8 matrix
+ * cores.  Arguments as bitlinear_gemv; M in [0, BITLINEAR_MAX_M].
+ */
+int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, const void *packed,
+                   const float *w_beta, int64_t N, void *y, int y_dtype, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITLINEAR_H */

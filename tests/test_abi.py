@@ -1,0 +1,138 @@
+"""The C-ABI library: it loads, exports what the header declares, and rejects
+invalid arguments before touching the GPU (so these run without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bitlinear_matmul_02_amd as bl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bitlinear.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = bl.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(bl.EXPORTS)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict(re.findall(r"#define (BITLINEAR_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
+    assert int(consts["BITLINEAR_OK"]) == bl.OK
+    assert int(consts["BITLINEAR_ERR_ARG"]) == bl.ERR_ARG
+    assert int(consts["BITLINEAR_ERR_SHAPE"]) == bl.ERR_SHAPE
+    assert int(consts["BITLINEAR_ERR_ALIGN"]) == bl.ERR_ALIGN
+    assert int(consts["BITLINEAR_ERR_HIP"]) == bl.ERR_HIP
+    assert int(consts["BITLINEAR_F32"]) == bl.F32
+    assert int(consts["BITLINEAR_BF16"]) == bl.BF16
+    assert int(consts["BITLINEAR_I32"]) == bl.I32
+    assert int(consts["BITLINEAR_MAX_K"]) == bl.MAX_K
+    assert int(consts["BITLINEAR_GEMV_MAX_M"]) == bl.GEMV_MAX_M
+
+
+def test_size_helpers():
+    assert bl.act_stride(1) == 256
+    assert bl.act_stride(256) == 256
+    assert bl.act_stride(257) == 512
+    assert bl.act_stride(0) == -1
+    assert bl.act_stride(bl.MAX_K + 1) == -1
+    assert bl.packed_bytes(16, 256) == 1024
+    assert bl.packed_bytes(17, 257) == 4 * 1024
+    assert bl.packed_bytes(6912, 2560) == 6912 * 2560 // 4
+    assert bl.packed_bytes(28672, 8192) == 28672 * 8192 // 4
+    assert bl.packed_bytes(0, 10) == -1
+    assert bl.pack_workspace_bytes(512, 512) == 8 * 64
+    assert bl.pack_workspace_bytes(3, 5) == 8
+    for M in (1, 8, 32, 64):
+        for N, K in ((6912, 2560), (2560, 6912), (28672, 8192), (8192, 28672), (5, 7)):
+            assert bl.gemv_workspace_bytes(M, N, K) >= 0
+    assert bl.gemv_workspace_bytes(65, 16, 256) == -1
+    assert bl.gemm_workspace_bytes(2048, 6912, 2560) >= 0
+    assert bl.lib().bitlinear_version() >> 16 == 1
+
+
+FAKE = 1 << 20  # an aligned address that is never dereferenced: validation fails first
+
+
+def call_product(fn, q=FAKE, ds=FAKE, M=1, K=256, packed=FAKE, beta=FAKE, N=16, y=FAKE, ydt=bl.F32,
+                 ws=None, wsb=0):
+    return fn(q, ds, M, K, packed, beta, N, y, ydt, ws, wsb, None)
+
+
+@pytest.mark.parametrize("name", ["bitlinear_gemv", "bitlinear_gemm"])
+def test_product_validation(name):
+    fn = getattr(bl.lib(), name)
+    assert call_product(fn, q=None) == bl.ERR_ARG
+    assert "null" in bl.last_error()
+    assert call_product(fn, beta=None) == bl.ERR_ARG
+    assert call_product(fn, ydt=7) == bl.ERR_ARG
+    assert call_product(fn, K=0) == bl.ERR_SHAPE
+    assert call_product(fn, K=bl.MAX_K + 1) == bl.ERR_SHAPE
+    assert call_product(fn, N=0) == bl.ERR_SHAPE
+    assert call_product(fn, M=-1) == bl.ERR_SHAPE
+    assert call_product(fn, q=FAKE + 8) == bl.ERR_ALIGN
+    assert call_product(fn, packed=FAKE + 4) == bl.ERR_ALIGN
+    assert call_product(fn, y=FAKE + 2) == bl.ERR_ALIGN
+    assert call_product(fn, M=0) == bl.OK  # no tokens: nothing to do, nothing enqueued
+    assert bl.last_error() == ""
+
+
+def test_gemv_token_limit_and_workspace_checks():
+    fn = bl.lib().bitlinear_gemv
+    assert call_product(fn, M=65) == bl.ERR_SHAPE
+    # find a shape whose plan splits K over workgroups (needs a workspace)
+    need = bl.gemv_workspace_bytes(1, 2560, 6912)
+    if need > 0:
+        assert call_product(fn, M=1, K=6912, N=2560, ws=None) == bl.ERR_ARG
+        assert "workspace" in bl.last_error()
+        assert call_product(fn, M=1, K=6912, N=2560, ws=FAKE, wsb=need - 1) == bl.ERR_ARG
+        assert call_product(fn, M=1, K=6912, N=2560, ws=FAKE + 4, wsb=need) == bl.ERR_ALIGN
+
+
+def test_quant_act_validation():
+    fn = bl.lib().bitlinear_quant_act
+    assert fn(FAKE, 5, 1, 16, FAKE, FAKE, None, None) == bl.ERR_ARG
+    assert fn(None, bl.BF16, 1, 16, FAKE, FAKE, None, None) == bl.ERR_ARG
+    assert fn(FAKE, bl.BF16, 1, 0, FAKE, FAKE, None, None) == bl.ERR_SHAPE
+    assert fn(FAKE, bl.BF16, -3, 16, FAKE, FAKE, None, None) == bl.ERR_SHAPE
+    assert fn(FAKE + 1, bl.BF16, 1, 16, FAKE, FAKE, None, None) == bl.ERR_ALIGN
+    assert fn(FAKE + 2, bl.F32, 1, 16, FAKE, FAKE, None, None) == bl.ERR_ALIGN
+    assert fn(FAKE, bl.BF16, 1, 16, FAKE + 8, FAKE, None, None) == bl.ERR_ALIGN
+    assert fn(FAKE, bl.BF16, 0, 16, FAKE, FAKE, None, None) == bl.OK
+
+
+def test_pack_validation():
+    fn = bl.lib().bitlinear_pack_weights
+    assert fn(None, 16, 16, FAKE, FAKE, FAKE, None) == bl.ERR_ARG
+    assert fn(FAKE, 16, 16, FAKE, FAKE, None, None) == bl.ERR_ARG
+    assert fn(FAKE, 0, 16, FAKE, FAKE, FAKE, None) == bl.ERR_SHAPE
+    assert fn(FAKE, 16, bl.MAX_K + 1, FAKE, FAKE, FAKE, None) == bl.ERR_SHAPE
+    assert fn(FAKE, 16, 16, FAKE + 8, FAKE, FAKE, None) == bl.ERR_ALIGN
+    assert fn(FAKE, 16, 16, FAKE, FAKE, FAKE + 4, None) == bl.ERR_ALIGN
+
+
+def test_error_string_is_thread_local():
+    import threading
+    fn = bl.lib().bitlinear_gemv
+    assert call_product(fn, K=0) == bl.ERR_SHAPE
+    seen = {}
+
+    def other():
+        seen["msg"] = bl.last_error()
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "K=0" in bl.last_error()

@@ -1,0 +1,239 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every input is drawn on the host by ``workloads`` and fed byte-identically to
+both sides.  Integer results (int8 codes, packed bytes, int32 accumulators)
+must match bit for bit; dequantized outputs must be within 1e-3 relative
+(fp32) / 1e-2 (bf16) of the oracle, and are in fact expected bit-equal since
+both sides evaluate y = (float)acc * (ds * beta) with the same IEEE operations.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitlinear_matmul_02_amd as bl
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+RTOL_F32, RTOL_BF16 = 1e-3, 1e-2
+
+
+def to_dev_bf16(xb: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def rel_err_ok(got: np.ndarray, ref: np.ndarray, rtol: float) -> bool:
+    got = got.astype(np.float64)
+    ref = ref.astype(np.float64)
+    zero = ref == 0
+    if np.any(got[zero] != 0):
+        return False
+    return bool(np.all(np.abs(got[~zero] - ref[~zero]) <= rtol * np.abs(ref[~zero])))
+
+
+def gpu_pack(w: np.ndarray):
+    return bl.pack_weights(torch.from_numpy(w).to(DEV))
+
+
+def gpu_forward(xb, packed, beta, N, K, out_dtype, use_gemm):
+    x = to_dev_bf16(xb)
+    M = x.shape[0]
+    x_q, x_ds = bl.quant_act(x)
+    y = torch.empty((M, N), dtype=out_dtype, device=DEV)
+    if use_gemm:
+        ws = bl.workspace(bl.gemm_workspace_bytes(M, N, K), DEV)
+        bl.bitlinear_gemm(x_q, x_ds, K, packed, beta, N, y, ws)
+    else:
+        ws = bl.workspace(bl.gemv_workspace_bytes(M, N, K), DEV)
+        bl.bitlinear_gemv(x_q, x_ds, K, packed, beta, N, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def check_product(xb, w, use_gemm, dtypes=("i32", "f32", "bf16"), ref=None):
+    M, K = xb.shape
+    N = w.shape[0]
+    if ref is None:
+        ref = oracle.bitlinear_forward(xb, w, threads=8)
+    packed, beta = gpu_pack(w)
+    assert beta.cpu().numpy()[0] == ref["beta"]
+    if "i32" in dtypes:
+        acc = gpu_forward(xb, packed, beta, N, K, torch.int32, use_gemm).cpu().numpy()
+        np.testing.assert_array_equal(acc, ref["acc"])
+    if "f32" in dtypes:
+        y = gpu_forward(xb, packed, beta, N, K, torch.float32, use_gemm).cpu().numpy()
+        assert rel_err_ok(y, ref["y"], RTOL_F32)
+        np.testing.assert_array_equal(y, ref["y"])  # same IEEE ops on both sides
+    if "bf16" in dtypes:
+        yb = bf16_bits(gpu_forward(xb, packed, beta, N, K, torch.bfloat16, use_gemm))
+        assert rel_err_ok(workloads.bf16_bits_to_f32(yb), workloads.bf16_bits_to_f32(ref["y_bf16"]), RTOL_BF16)
+        np.testing.assert_array_equal(yb, ref["y_bf16"])
+
+
+# --------------------------------------------------------------- quant_act
+@pytest.mark.parametrize("M,K,outliers", [(1, 1, False), (1, 7, False), (3, 300, False), (4, 512, False),
+                                          (1, 2560, True), (2, 6912, True), (8, 8192, False),
+                                          (33, 28672, False), (5, 255, True), (2048, 64, False)])
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_quant_act_parity(M, K, outliers, src):
+    xb = workloads.gen_acts_bf16(M, K, seed=M * 7 + K, outliers=outliers)
+    if src == "bf16":
+        x = to_dev_bf16(xb)
+        q_ref, ds_ref, rs_ref = oracle.quant_act(xb, bf16_bits=True)
+    else:
+        xf = workloads.bf16_bits_to_f32(xb) * np.float32(1.37)  # values beyond bf16 precision
+        x = torch.from_numpy(xf).to(DEV)
+        q_ref, ds_ref, rs_ref = oracle.quant_act(xf)
+    x_q, x_ds, rs = bl.quant_act(x, with_rowsum=True)
+    torch.cuda.synchronize()
+    q = x_q.cpu().numpy()
+    assert q.shape == (M, bl.act_stride(K))
+    np.testing.assert_array_equal(q[:, :K], q_ref)
+    assert not q[:, K:].any()
+    np.testing.assert_array_equal(x_ds.cpu().numpy(), ds_ref)
+    np.testing.assert_array_equal(rs.cpu().numpy(), rs_ref)
+
+
+def test_quant_act_zero_row_and_unaligned_rows():
+    K = 13  # odd row length: rows are not 16-byte aligned -> scalar path
+    xb = workloads.gen_acts_bf16(3, K, seed=4)
+    xb[1] = 0
+    x = to_dev_bf16(xb)
+    x_q, x_ds, rs = bl.quant_act(x, with_rowsum=True)
+    q_ref, ds_ref, rs_ref = oracle.quant_act(xb, bf16_bits=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(x_q.cpu().numpy()[:, :K], q_ref)
+    np.testing.assert_array_equal(x_ds.cpu().numpy(), ds_ref)
+    assert rs_ref[1] == 0 and not q_ref[1].any()
+
+
+# -------------------------------------------------------------------- pack
+@pytest.mark.parametrize("N,K", [(1, 1), (16, 256), (17, 257), (35, 700), (512, 512), (640, 2560),
+                                 (6912, 2560), (2560, 6912), (3, 5000)])
+def test_pack_parity(N, K):
+    w = workloads.gen_weights(N, K, seed=N + 31 * K)
+    beta_ref = oracle.absmean(w)
+    packed_ref = oracle.pack_t2(oracle.ternarize(w, beta_ref))
+    packed, beta = gpu_pack(w)
+    torch.cuda.synchronize()
+    assert beta.cpu().numpy()[0] == beta_ref
+    np.testing.assert_array_equal(packed.cpu().numpy(), packed_ref)
+
+
+def test_pack_zero_and_tie_weights():
+    # all-zero weights: beta = 0, every code 0
+    w = np.zeros((20, 300), dtype=np.float32)
+    packed, beta = gpu_pack(w)
+    assert beta.cpu().item() == 0.0 and not packed.cpu().numpy().any()
+    # exact ties: mean |w| = 0.5 exactly, so d = 0.5 and w/d hits 0.5, 1.5, 2.5
+    pattern = np.array([0.25, -0.25, 0.25, -0.25, 0.75, -0.75, 1.25, -0.25], dtype=np.float32)
+    w = np.tile(pattern, (16, 32))
+    beta_ref = oracle.absmean(w)
+    assert beta_ref == np.float32(0.5)
+    packed, beta = gpu_pack(w)
+    assert beta.cpu().numpy()[0] == beta_ref
+    t_ref = oracle.ternarize(w, beta_ref)
+    np.testing.assert_array_equal(t_ref[0, :8], [0, 0, 0, 0, 1, -1, 1, 0])
+    np.testing.assert_array_equal(packed.cpu().numpy(), oracle.pack_t2(t_ref))
+
+
+# --------------------------------------------------------------- products
+def test_hand_example_on_gpu(golden_dir):
+    import json
+    import os
+    with open(os.path.join(golden_dir, "hand_4x4.json")) as f:
+        h = json.load(f)
+    w = np.array(h["w"], dtype=np.float32)
+    x = np.array(h["x"], dtype=np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    for use_gemm in (False, True):
+        packed, beta = gpu_pack(w)
+        assert beta.cpu().item() == h["beta"]
+        acc = gpu_forward(xb, packed, beta, 4, 4, torch.int32, use_gemm).cpu().numpy()
+        np.testing.assert_array_equal(acc, np.array(h["acc"]))
+        y = gpu_forward(xb, packed, beta, 4, 4, torch.float32, use_gemm).cpu().numpy()
+        np.testing.assert_array_equal(y, np.array(h["y"], dtype=np.float32))
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 15, 16, 17, 31, 32, 33, 48, 64])
+@pytest.mark.parametrize("N,K", [(16, 256), (40, 700), (512, 512), (100, 3000)])
+def test_gemv_parity(M, N, K):
+    w = workloads.gen_weights(N, K, seed=1000 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=2000 + M, outliers=True)
+    check_product(xb, w, use_gemm=False)
+
+
+@pytest.mark.parametrize("M", [1, 16, 65, 100, 128, 129, 300])
+@pytest.mark.parametrize("N,K", [(16, 256), (40, 700), (200, 1000), (512, 512)])
+def test_gemm_parity(M, N, K):
+    w = workloads.gen_weights(N, K, seed=3000 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=4000 + M)
+    check_product(xb, w, use_gemm=True)
+
+
+def test_gemv_split_k_workspace_left_zero():
+    # a long K with few outputs makes the plan split K across workgroups
+    M, N, K = 3, 48, 40000
+    need = bl.gemv_workspace_bytes(M, N, K)
+    w = workloads.gen_weights(N, K, seed=5)
+    xb = workloads.gen_acts_bf16(M, K, seed=6)
+    ref = oracle.bitlinear_forward(xb, w, threads=8)
+    for _ in range(3):  # repeated calls reuse the same workspace
+        check_product(xb, w, use_gemm=False, dtypes=("i32",), ref=ref)
+    if need > 0:
+        ws = bl.workspace(need, DEV)
+        torch.cuda.synchronize()
+        assert not ws[:need].any().item()
+
+
+def test_max_magnitude_accumulators():
+    # q = +-127 everywhere and t = +-1 everywhere at the largest K: |acc| = 127*K
+    K, N, M = bl.MAX_K, 32, 2
+    w = np.full((N, K), 0.02, dtype=np.float32)
+    w[1::2] = -0.02
+    x = np.full((M, K), 3.0, dtype=np.float32)
+    x[1] = -3.0
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    ref = oracle.bitlinear_forward(xb, w, threads=8)
+    assert int(np.abs(ref["acc"]).max()) == 127 * K
+    check_product(xb, w, use_gemm=False, dtypes=("i32", "f32"), ref=ref)
+    check_product(xb, w, use_gemm=True, dtypes=("i32", "f32"), ref=ref)
+
+
+def test_zero_token_and_zero_weights():
+    K, N = 512, 64
+    w = workloads.gen_weights(N, K, seed=8)
+    w[5] = 0.0
+    xb = workloads.gen_acts_bf16(4, K, seed=9)
+    xb[2] = 0
+    for use_gemm in (False, True):
+        check_product(xb, w, use_gemm=use_gemm)
+
+
+def test_empty_batch_is_noop():
+    packed, beta = gpu_pack(workloads.gen_weights(16, 256, seed=1))
+    x_q = torch.empty((0, 256), dtype=torch.int8, device=DEV)
+    x_ds = torch.empty((0,), dtype=torch.float32, device=DEV)
+    y = torch.empty((0, 16), dtype=torch.float32, device=DEV)
+    bl.bitlinear_gemv(x_q, x_ds, 256, packed, beta, 16, y)
+    bl.bitlinear_gemm(x_q, x_ds, 256, packed, beta, 16, y)
+    torch.cuda.synchronize()
+
+
+def test_runs_on_a_side_stream():
+    M, N, K = 8, 256, 1024
+    w = workloads.gen_weights(N, K, seed=12)
+    xb = workloads.gen_acts_bf16(M, K, seed=13)
+    ref = oracle.bitlinear_forward(xb, w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        packed, beta = gpu_pack(w)
+        y = bl.linear(to_dev_bf16(xb), packed, beta, N, torch.int32)
+    s.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), ref["acc"])
