@@ -1,0 +1,344 @@
+"""Benchmark of the BitLinear forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+Headline workload: decode GEMV at batch 1 on the 2B-class shapes, K=2560 ->
+N=6912 and K=6912 -> N=2560, bf16 activations with 1% x20 outliers.  One step
+is the whole inference hot path for one token through both BitLinears:
+per-token int8 quantization then the ternary product with fused dequant
+(weights are packed once, before timing).  Inputs are resident in HBM; the
+packed weights rotate over enough distinct copies (> 2x the 256 MB Infinity
+Cache) that every step streams them from HBM.  The K timed steps are one HIP
+graph replay (no host launch overhead inside the timed region).
+
+value = packed weight bytes of the step x K / elapsed time, in GB/s.
+
+Also printed on the same JSON line:
+  roofline      the GEMV kernel: algorithmic bytes per launch / its average
+                launch duration (HIP events around each launch, on the launch
+                stream), against the 8 TB/s HBM peak;
+  cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) running the same
+                step on the host cores, on a bounded number of repetitions;
+  also          the other workloads: 100B-class decode (M = 1, 8, 32) in GB/s
+                and prefill GEMMs (2B M=2048, 100B M=512) in int8 TOPS.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import bitlinear_matmul_02_amd as bl
+import workloads
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ helpers
+class Linear:
+    """Device buffers of one BitLinear used in a timed step.
+
+    mode "fused": one launch (bitlinear_forward_decode);
+    mode "gemv" / "gemm": bitlinear_quant_act then the product call."""
+
+    def __init__(self, M, K, N, packed_copies, beta, x, y_dtype=torch.float32, mode=None):
+        dev = x.device
+        self.M, self.K, self.N = M, K, N
+        self.packed = packed_copies
+        self.beta = beta
+        self.x = x
+        if mode is None:
+            mode = "fused" if bl.decode_fits(M, K) else ("gemv" if M <= bl.GEMV_MAX_M else "gemm")
+        self.mode = mode
+        self.x_q = torch.empty((M, bl.act_stride(K)), dtype=torch.int8, device=dev)
+        self.x_ds = torch.empty((M,), dtype=torch.float32, device=dev)
+        self.y = torch.empty((M, N), dtype=y_dtype, device=dev)
+        if mode == "gemm":
+            nbytes, self.product = bl.gemm_workspace_bytes(M, N, K), bl.bitlinear_gemm
+        else:
+            nbytes, self.product = bl.gemv_workspace_bytes(M, N, K), bl.bitlinear_gemv
+        self.ws = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=dev) if nbytes > 0 else None
+
+    def weight_bytes(self):
+        return self.N * self.K // 4
+
+    def traffic_bytes(self):
+        """Algorithmic HBM bytes of the timed kernel: packed weights once, its
+        activation input once (bf16 x when fused, int8 rows otherwise), y once."""
+        act = self.M * self.K * self.x.element_size() if self.mode == "fused" else self.M * bl.act_stride(self.K)
+        return self.weight_bytes() + act + self.M * self.N * self.y.element_size()
+
+    def quant(self):
+        if self.mode != "fused":
+            bl.bitlinear_quant_act(self.x, self.x_q, self.x_ds)
+
+    def run_product(self, r):
+        packed = self.packed[r % len(self.packed)]
+        if self.mode == "fused":
+            bl.bitlinear_forward_decode(self.x, packed, self.beta, self.N, self.y)
+        else:
+            self.product(self.x_q, self.x_ds, self.K, packed, self.beta, self.N, self.y, self.ws)
+
+    def step(self, r):
+        self.quant()
+        self.run_product(r)
+
+
+def rotation(per_step_bytes):
+    return int(max(1, min(256, -(-2 * MALL_BYTES // max(per_step_bytes, 1)) + 1)))
+
+
+def pack_from_host(w_np, dev):
+    return bl.pack_weights(torch.from_numpy(w_np).to(dev))
+
+
+def copies_of(packed, n):
+    return [packed] + [packed.clone() for _ in range(n - 1)]
+
+
+def capture(fn, nsteps):
+    """One HIP graph holding fn(0) ... fn(nsteps - 1)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)  # one eager call first (loads code objects)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(nsteps):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def capture_steps(linears, nsteps):
+    def one(i):
+        for lin in linears:
+            lin.step(i)
+    return capture(one, nsteps)
+
+
+def time_graph(g, reps=1):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3, time.perf_counter() - t0
+
+
+def kernel_duration(lin, launches=200):
+    """Average duration of the product kernel: HIP events on the launch stream
+    around a graph of `launches` back-to-back launches (weight copies rotate)."""
+    lin.quant()
+    g = capture(lambda i: lin.run_product(i), launches)
+    time_graph(g)
+    el, _ = time_graph(g)
+    return el / launches
+
+
+# --------------------------------------------------------------- headline
+def headline(args, dev):
+    wl = workloads.DECODE_2B
+    host = []
+    for i, lin in enumerate(wl.linears):
+        w = workloads.gen_weights(lin.N, lin.K, seed=2 * i)
+        xb = workloads.gen_acts_bf16(lin.M, lin.K, seed=2 * i + 1, outliers=lin.outliers)
+        host.append((w, xb))
+    per_step = sum(l.N * l.K // 4 for l in wl.linears)
+    R = rotation(per_step)
+    linears = []
+    for (w, xb), lin in zip(host, wl.linears):
+        packed, beta = pack_from_host(w, dev)
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        linears.append(Linear(lin.M, lin.K, lin.N, copies_of(packed, R), beta, x))
+
+    # sanity: the timed path reproduces the oracle on this input
+    import oracle
+    for (w, xb), L in zip(host, linears):
+        L.quant()
+        L.run_product(0)
+        torch.cuda.synchronize()
+        ref = oracle.bitlinear_forward(xb, w, threads=8)
+        if not np.array_equal(L.y.cpu().numpy(), ref["y"]):
+            raise SystemExit("bench: GPU output differs from the oracle on the headline workload")
+
+    g_warm = capture_steps(linears, max(args.warmup, 1))
+    g_main = capture_steps(linears, args.steps)
+    time_graph(g_warm)
+    elapsed, wall = time_graph(g_main)
+    value = per_step * args.steps / elapsed / 1e9
+
+    durs = [kernel_duration(L) for L in linears]
+    bytes_per = [L.traffic_bytes() for L in linears]
+    # the same step with the standalone quantizer (two launches per BitLinear)
+    split = [Linear(L.M, L.K, L.N, L.packed, L.beta, L.x, mode="gemv") for L in linears]
+    g_split = capture_steps(split, args.steps)
+    time_graph(g_split)
+    el_split, _ = time_graph(g_split)
+    achieved = sum(bytes_per) / sum(durs) / 1e9
+    out = {
+        "value": value, "ms_per_step": elapsed / args.steps * 1e3, "wall_s": wall,
+        "rotation_copies": R,
+        "unfused_us_per_step": round(el_split / args.steps * 1e6, 2),
+        "kernel_us": {"%dx%d->%d" % (L.M, L.K, L.N): round(d * 1e6, 3) for L, d in zip(linears, durs)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_t2_kernel (fused quantization)", "bytes_per_launch": bytes_per},
+    }
+    return out, host, wl
+
+
+def cpu_baseline(host, wl, budget_s=10.0):
+    import oracle
+    threads = min(16, os.cpu_count() or 1)
+    prepared = []
+    for (w, xb), lin in zip(host, wl.linears):
+        beta = oracle.absmean(w)
+        prepared.append((oracle.ternarize(w, beta), beta, xb))
+    per_step = sum(l.N * l.K // 4 for l in wl.linears)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for t, beta, xb in prepared:
+            q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
+            acc = oracle.matmul_i32(q, t, threads=threads)
+            oracle.dequant(acc, ds, beta)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d decode steps (quantize + int32 product + dequant, both 2B shapes, M=1) in %.1f s"
+                      % (reps, el)}
+
+
+# ------------------------------------------------------------------- extras
+def gpu_weights(N, K, seed, dev):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * workloads.W_STD
+    packed, beta = bl.pack_weights(w)
+    del w
+    return packed, beta
+
+
+def gpu_acts(M, K, seed, dev):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    return torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+
+
+def decode_extra(shapes, Ms, dev, steps=100):
+    res = {}
+    packs = [gpu_weights(N, K, 100 + i, dev) for i, (K, N) in enumerate(shapes)]
+    per_step = sum(N * K // 4 for K, N in shapes)
+    R = rotation(per_step)
+    copies = [copies_of(p, R) for p, _ in packs]
+    for M in Ms:
+        lins = [Linear(M, K, N, copies[i], packs[i][1], gpu_acts(M, K, 200 + i, dev))
+                for i, (K, N) in enumerate(shapes)]
+        g = capture_steps(lins, steps)
+        time_graph(g)
+        el, _ = time_graph(g)
+        durs = [kernel_duration(L, 100) for L in lins]
+        res["M%d" % M] = {"mode": lins[0].mode, "GB_s": round(per_step * steps / el / 1e9, 1),
+                          "gemv_GB_s": round(sum(L.traffic_bytes() for L in lins) / sum(durs) / 1e9, 1),
+                          "us_per_step": round(el / steps * 1e6, 2),
+                          "frac_hbm": round(sum(L.traffic_bytes() for L in lins) / sum(durs) / 1e9 / HBM_PEAK_GBS, 4)}
+        del lins, g
+    del copies, packs
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_extra(M, shapes, dev, reps=20):
+    res = {}
+    for i, (K, N) in enumerate(shapes):
+        packed, beta = gpu_weights(N, K, 300 + i, dev)
+        L = Linear(M, K, N, [packed], beta, gpu_acts(M, K, 400 + i, dev))
+        L.quant()
+        L.run_product(0)
+        torch.cuda.synchronize()
+        d = kernel_duration(L, reps)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            L.quant()
+        b.record()
+        torch.cuda.synchronize()
+        tops = 2.0 * M * N * K / d / 1e12
+        res["%dx%d->%d" % (M, K, N)] = {"gemm_us": round(d * 1e6, 1), "TOPS": round(tops, 1),
+                                        "frac_mfma": round(tops / INT8_PEAK_TOPS, 4),
+                                        "quant_us": round(a.elapsed_time(b) / reps * 1e3, 2)}
+        del L, packed
+        torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the path has no sharding or collectives); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bl.lib()
+
+    head, host, wl = headline(args, dev)
+    result = {
+        "metric": "ternary GEMV HBM GB/s + decode tok/s; prefill int8 TOPS; % of roofline",
+        "value": round(head["value"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "shapes": ["1x2560->6912", "1x6912->2560"],
+                   "step": "per BitLinear: absmax int8 quantization + ternary product + dequant (fp32 out), "
+                           "one fused launch",
+                   "rotation_copies": head["rotation_copies"], "parallelism": "none (1 GPU)"},
+        "roofline": head["roofline"],
+        "kernel_us": head["kernel_us"],
+        "unfused_us_per_step": head["unfused_us_per_step"],
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(host, wl)
+    if not args.quick:
+        result["also"] = {
+            "decode_100b": decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
+            "prefill_2b_m2048": prefill_extra(2048, ((2560, 6912), (6912, 2560)), dev),
+            "prefill_100b_m512": prefill_extra(512, workloads.SHAPES_100B, dev),
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

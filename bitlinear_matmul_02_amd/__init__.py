@@ -10,6 +10,7 @@ Functions carry the C names:
     bitlinear_pack_weights(w, packed, w_beta, workspace)
     bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
     bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
+    bitlinear_forward_decode(x, packed, w_beta, N, y)
 plus allocation helpers (``act_stride``, ``packed_bytes`` ...) and two
 conveniences that allocate outputs (``quant_act``, ``pack_weights``,
 ``linear``).
@@ -32,8 +33,9 @@ EXPORTS = (
     "bitlinear_version", "bitlinear_last_error", "bitlinear_act_stride", "bitlinear_packed_bytes",
     "bitlinear_pack_workspace_bytes", "bitlinear_gemv_workspace_bytes",
     "bitlinear_gemm_workspace_bytes", "bitlinear_quant_act", "bitlinear_pack_weights",
-    "bitlinear_gemv", "bitlinear_gemm",
+    "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode",
 )
+DECODE_MAX_ACT_BYTES = 58368
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}
 
@@ -77,6 +79,8 @@ def lib() -> ctypes.CDLL:
     for name in ("bitlinear_gemv", "bitlinear_gemm"):
         getattr(L, name).restype = i32
         getattr(L, name).argtypes = [p, p, i64, i64, p, p, i64, p, i32, p, sz, p]
+    L.bitlinear_forward_decode.restype = i32
+    L.bitlinear_forward_decode.argtypes = [p, i32, i64, i64, p, p, i64, p, i32, p]
     _lib = L
     return L
 
@@ -154,6 +158,17 @@ def bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=No
              stream)
 
 
+def bitlinear_forward_decode(x, packed, w_beta, N, y, stream=None) -> None:
+    """y [M][N] = BitLinear(x) for M <= 64 tokens in one launch (quantization fused)."""
+    M, K = x.shape
+    _check(lib().bitlinear_forward_decode(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(packed), _ptr(w_beta), N,
+                                          _ptr(y), _DTYPE[y.dtype], _stream(stream)))
+
+
+def decode_fits(M: int, K: int) -> bool:
+    return 1 <= M <= GEMV_MAX_M and M * (act_stride(K) + 16) <= DECODE_MAX_ACT_BYTES
+
+
 # ------------------------------------------------------------- conveniences
 _ws_cache: dict = {}
 
@@ -191,8 +206,11 @@ def pack_weights(w, stream=None):
 def linear(x, packed, w_beta, N: int, out_dtype=torch.float32, stream=None):
     """BitLinear forward: quantize x [M][K], then gemv (M <= 64) or gemm."""
     M, K = x.shape
-    x_q, x_ds = quant_act(x, stream=stream)
     y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if decode_fits(M, K):
+        bitlinear_forward_decode(x, packed, w_beta, N, y, stream)
+        return y
+    x_q, x_ds = quant_act(x, stream=stream)
     if M <= GEMV_MAX_M:
         ws = workspace(gemv_workspace_bytes(M, N, K), x.device)
         bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, ws, stream)

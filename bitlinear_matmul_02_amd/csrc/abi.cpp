@@ -35,21 +35,31 @@ bool n_ok(int64_t N) { return N >= 1 && N <= BITLINEAR_MAX_N; }
 
 int64_t act_stride(int64_t K) { return bl::ceil_div(K, bl::kTileK) * bl::kTileK; }
 
-// Checks shared by gemv and gemm.
-int check_product(const char* fn, const int8_t* x_q, const float* x_ds, int64_t M, int64_t max_m,
-                  int64_t K, const void* packed, const float* w_beta, int64_t N, void* y,
-                  int y_dtype, void* ws, size_t ws_bytes, int64_t need_ws) {
+// Shape, dtype and weight/output checks shared by every product call.
+int check_common(const char* fn, int64_t M, int64_t max_m, int64_t K, const void* packed, const float* w_beta,
+                 int64_t N, void* y, int y_dtype) {
   if (M < 0 || M > max_m) return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld outside [0, %lld]", fn, (long long)M, (long long)max_m);
   if (!k_ok(K)) return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld outside [1, %d]", fn, (long long)K, BITLINEAR_MAX_K);
   if (!n_ok(N)) return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld outside [1, %d]", fn, (long long)N, BITLINEAR_MAX_N);
   if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
     return fail(BITLINEAR_ERR_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
   if (M == 0) return BITLINEAR_OK;
-  if (!x_q || !x_ds || !packed || !w_beta || !y) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
-  if (!aligned(x_q, 16) || !aligned(packed, 16))
-    return fail(BITLINEAR_ERR_ALIGN, "%s: x_q and packed must be 16-byte aligned", fn);
-  if (!aligned(x_ds, 4) || !aligned(w_beta, 4) || !aligned(y, y_dtype == BITLINEAR_BF16 ? 2 : 4))
-    return fail(BITLINEAR_ERR_ALIGN, "%s: x_ds, w_beta or y not element aligned", fn);
+  if (!packed || !w_beta || !y) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(packed, 16)) return fail(BITLINEAR_ERR_ALIGN, "%s: packed must be 16-byte aligned", fn);
+  if (!aligned(w_beta, 4) || !aligned(y, y_dtype == BITLINEAR_BF16 ? 2 : 4))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: w_beta or y not element aligned", fn);
+  return BITLINEAR_OK;
+}
+
+// Checks of gemv / gemm: the common ones, the int8 activations, the workspace.
+int check_product(const char* fn, const int8_t* x_q, const float* x_ds, int64_t M, int64_t max_m,
+                  int64_t K, const void* packed, const float* w_beta, int64_t N, void* y,
+                  int y_dtype, void* ws, size_t ws_bytes, int64_t need_ws) {
+  int st = check_common(fn, M, max_m, K, packed, w_beta, N, y, y_dtype);
+  if (st != BITLINEAR_OK || M == 0) return st;
+  if (!x_q || !x_ds) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x_q, 16)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_q must be 16-byte aligned", fn);
+  if (!aligned(x_ds, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_ds not element aligned", fn);
   if (need_ws > 0) {
     if (!ws) return fail(BITLINEAR_ERR_ARG, "%s: this shape needs a %lld-byte workspace", fn, (long long)need_ws);
     if ((int64_t)ws_bytes < need_ws)
@@ -142,6 +152,24 @@ int bitlinear_gemm(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, c
   if (st != BITLINEAR_OK || M == 0) return st == BITLINEAR_OK ? ok() : st;
   return hip_status(bl::launch_gemm_t2(x_q, act_stride(K), x_ds, M, K, static_cast<const uint8_t*>(packed),
                                        w_beta, N, y, y_dtype, workspace, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, const void* packed,
+                             const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
+  const char* fn = "bitlinear_forward_decode";
+  if (x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_F32)
+    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32", fn);
+  int st = check_common(fn, M, BITLINEAR_GEMV_MAX_M, K, packed, w_beta, N, y, y_dtype);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  if (!x) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x, x_dtype == BITLINEAR_BF16 ? 2 : 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x not element aligned", fn);
+  if (!bl::decode_fused_fits(M, K))
+    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (act_stride(K) + 16) = %lld exceeds %d bytes", fn,
+                (long long)(M * (act_stride(K) + 16)), BITLINEAR_DECODE_MAX_ACT_BYTES);
+  return hip_status(bl::launch_decode_t2(x, x_dtype, M, K, static_cast<const uint8_t*>(packed), w_beta, N, y,
+                                         y_dtype, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

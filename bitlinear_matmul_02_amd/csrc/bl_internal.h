@@ -15,6 +15,9 @@ constexpr int kTileN = 16;
 constexpr int kTileK = 256;
 constexpr int kTileBytes = 1024;
 constexpr int kBetaChunk = 4096;
+// LDS a decode workgroup may use for its int8 activation rows (each row is
+// act_stride(K) + 16 bytes); with its 4 KB reduction buffer it stays < 64 KB.
+constexpr int64_t kDecodeLdsBytes = BITLINEAR_DECODE_MAX_ACT_BYTES;
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -34,6 +37,11 @@ int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s);
+
+// Fused decode: per-token quantization of x inside the product kernel.
+bool decode_fused_fits(int64_t M, int64_t K);
+hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
+                            const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s);
 
 // Prefill-shaped product (any M).
 int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);

@@ -1,4 +1,5 @@
-// Decode-shaped ternary product (M <= 64 tokens) with fused dequantization.
+// Decode-shaped ternary product (M <= 64 tokens) with fused dequantization,
+// and its fused variant that also quantizes the activations.
 //
 // The sum acc[m][n] = sum_k q[m][k] * t[n][k] over ternary t is the add /
 // subtract / skip sum of "BitNet / Ternary / Binary - Les LLMs 1-bit" (TL;DR)
@@ -11,80 +12,348 @@
 // (exact, every term is a multiple of 64).
 //
 // Work decomposition.  The weights are a grid of 1 KB tiles (16 rows x 256
-// columns).  A wave owns NB consecutive 16-row blocks of outputs and a
-// contiguous range of k-tiles; per tile it reads 16 bytes per lane (the whole
-// 1 KB tile in one coalesced instruction), expands each of the four 2-bit
-// fields into a 16x64 int8 operand and issues 4 * MB * NB MFMA 16x16x64 steps.
-// Tile loads (and the activation operands of the same tile) are issued kU
-// tiles ahead of use.  The waves of a workgroup split K and add their partial
-// sums with LDS atomics; when several workgroups split K too, their sums meet
-// in an int32 workspace through device-scope atomics and the last workgroup to
-// arrive (a counter) dequantizes, stores y and zeroes the workspace again.
+// columns).  A workgroup owns NB consecutive 16-row output blocks; its waves
+// split the k-tiles into contiguous ranges.  Per k-tile a wave reads 16 bytes
+// per lane of each of its NB weight tiles (one coalesced 1 KB load each, kU
+// k-tiles ahead of use), expands each 2-bit field into an MFMA operand and
+// issues 4 * MB * NB MFMA 16x16x64 steps.  The waves add their partial sums
+// with LDS atomics; wave 0 dequantizes and stores.
+//
+// Activation operands (the int8 token rows) come from one of three places:
+//   ALDS_Q  the workgroup copies the int8 rows into LDS once (16-byte loads,
+//           rows padded by 16 bytes so the 16 token rows fall on different
+//           banks) and reads its operands from there;
+//   ALDS_X  fused quantization: the workgroup reads the bf16/fp32 rows, finds
+//           each row's absmax and writes the int8 rows into LDS itself, with
+//           the same arithmetic as the standalone quantizer ("Key
+//           Technologies Enabling the BitNET Family", Advanced Quantization
+//           Methodologies: per-token absmax 8-bit activations);
+//   ALDS_XS the same for rows that are not whole 16-byte pieces (unaligned x
+//           or K not a multiple of 8 bf16 / 4 fp32), element by element;
+//   AGLOBAL the rows are too large for LDS: operands are 16-byte global loads
+//           carried in the same ring as the weight tiles and reused over the
+//           NB weight tiles of a k-tile.
+// In every mode the first weight tiles are requested before the activations.
+//
+// Tiny outputs with a long K (AGLOBAL only) also split K across workgroups:
+// their sums meet in an int32 workspace through device-scope atomics and the
+// last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
+// workspace again.
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-// Per token-block count MB: output blocks per wave, tiles in flight per wave
-// and the largest workgroup (wider token blocks need more registers).
-template <int MB> struct Shape;
-template <> struct Shape<1> { static constexpr int NB = 1, U = 4, MAXW = 16; };
-template <> struct Shape<2> { static constexpr int NB = 2, U = 2, MAXW = 16; };
-template <> struct Shape<3> { static constexpr int NB = 2, U = 1, MAXW = 8; };
-template <> struct Shape<4> { static constexpr int NB = 2, U = 1, MAXW = 8; };
+constexpr float kEpsX = 1e-5f;
+constexpr int kLdsPad = 16;  // bytes added to each LDS activation row
+enum AMode { AGLOBAL = 0, ALDS_Q = 1, ALDS_X = 2, ALDS_XS = 3 };
 
-inline int shape_nb(int mb) { return mb == 1 ? Shape<1>::NB : Shape<2>::NB; }
-inline int shape_maxw(int mb) { return mb <= 2 ? Shape<1>::MAXW : Shape<3>::MAXW; }
+// k-tiles in flight per wave, chosen to keep the prefetch ring within the
+// register budget (weights: 4 VGPRs per output block; activations in the
+// ring only for AGLOBAL: 16 VGPRs per token block).
+constexpr int ring_depth(int mb, int nb, int amode) {
+  return amode == AGLOBAL ? ((mb * 4 + nb) * 4 <= 24 ? 4 : ((mb * 4 + nb) * 4 <= 40 ? 2 : 1))
+                          : (nb == 1 ? 8 : (nb == 2 ? 4 : 2));
+}
+// Largest workgroup, in waves, for MB token blocks.
+constexpr int max_waves(int mb) { return mb <= 2 ? 16 : 8; }
+
+int64_t lds_row(int64_t K) { return ceil_div(K, kTileK) * kTileK + kLdsPad; }
 
 struct GemvPlan {
-  int MB, NB;      // 16-row token blocks, 16-row output blocks per wave
+  int MB, NB;      // 16-row token blocks, 16-row output blocks per workgroup
   int Nt, Kt, Ng;  // output blocks, k-tiles, output groups (Nt / NB)
   int waves, SB;   // waves per workgroup, workgroups per output group
   int tps;         // k-tiles per wave
+  int amode;       // where activation operands come from
+  int64_t lds_bytes;
   int64_t ws_acc_bytes, ws_bytes;
 };
 
-GemvPlan make_plan(int64_t M, int64_t N, int64_t K) {
+GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse) {
   GemvPlan p{};
   p.MB = (int)ceil_div(M < 1 ? 1 : M, 16);
-  p.NB = shape_nb(p.MB);
   p.Nt = (int)ceil_div(N, kTileN);
   p.Kt = (int)ceil_div(K, kTileK);
+  const int64_t lds = M * lds_row(K);
+  p.amode = fuse ? ALDS_X : (lds <= kDecodeLdsBytes ? ALDS_Q : AGLOBAL);
+  p.lds_bytes = p.amode == AGLOBAL ? 0 : lds;
+  // Output blocks per workgroup: each activation operand is reused over NB
+  // weight tiles; N decides how many workgroups remain.  The LDS modes cap
+  // MB * NB at 4 (4 KB reduction buffer next to the activation rows).
+  // k-tiles per wave: long runs for one token block (the weight stream is the
+  // only work), shorter ones once MFMA work grows with the token count.
+  // Both rules are fitted to measurements on the 2B- and 100B-class shapes.
+  if (p.MB == 1) {
+    p.NB = p.Nt >= 384 ? 2 : 1;
+  } else {
+    p.NB = p.Nt >= 1024 ? 4 : (p.Nt >= 384 ? 2 : 1);
+  }
+  const int nb_cap = p.amode == AGLOBAL ? (p.MB > 2 ? 2 : 4) : (p.MB >= 3 ? 1 : 4 / p.MB);
+  if (p.NB > nb_cap) p.NB = nb_cap;
   p.Ng = (int)ceil_div(p.Nt, p.NB);
-  // aim for about 8192 waves (32 per CU) with at least one tile each
-  const int64_t units = (int64_t)p.Ng * p.Kt;
-  int tpw = (int)ceil_div(units, 8192);
-  if (tpw < 1) tpw = 1;
-  int S = (int)ceil_div(p.Kt, tpw);
-  const int maxw = shape_maxw(p.MB);
-  p.waves = S < maxw ? S : maxw;
-  p.SB = (int)ceil_div(S, p.waves);
-  S = p.waves * p.SB;
-  p.tps = (int)ceil_div(p.Kt, S);
+  const int maxw = max_waves(p.MB);
+  const int target = p.MB == 1 ? (p.Kt >= 32 ? 16 : 8) : 5;
+  int waves = (int)ceil_div(p.Kt, target);
+  if (waves > maxw) waves = maxw;
+  if (waves < 1) waves = 1;
+  p.tps = (int)ceil_div(p.Kt, waves);
+  p.waves = (int)ceil_div(p.Kt, p.tps);
+  p.SB = 1;
+  if (p.amode == AGLOBAL && p.Ng < 64 && p.tps >= 16) {
+    // tiny output, long K: split K across workgroups too
+    int64_t cap = 512 / p.Ng;
+    if (cap < 2) cap = 2;
+    int sb = (int)ceil_div(p.tps, 4);
+    p.SB = (int)(sb > cap ? cap : sb);
+    p.waves = maxw;
+    p.tps = (int)ceil_div(p.Kt, (int64_t)p.waves * p.SB);
+  }
   if (p.SB > 1) {
-    p.ws_acc_bytes = (int64_t)M * p.Ng * p.NB * kTileN * 4;
+    p.ws_acc_bytes = M * p.Ng * p.NB * kTileN * 4;
     p.ws_bytes = p.ws_acc_bytes + (int64_t)p.Ng * 4;
   }
   return p;
 }
 
-template <int MB, int NB = Shape<MB>::NB, int kU = Shape<MB>::U>
-__global__ __launch_bounds__(64 * Shape<MB>::MAXW) void gemv_t2_kernel(
-    const int8_t* __restrict__ q, int64_t ldq, const float* __restrict__ ds, int M,
-    const u4* __restrict__ packed, const float* __restrict__ beta, int N, int Nt, int Kt,
-    int tps, int SB, void* __restrict__ y, int y_dtype, int32_t* __restrict__ ws_acc,
-    uint32_t* __restrict__ ws_cnt) {
+struct GemvArgs {
+  const int8_t* q;  // [M][ldq] int8 (modes AGLOBAL, ALDS_Q)
+  const void* x;    // [M][K] bf16/fp32 activations (mode ALDS_X)
+  int x_dtype;
+  int x_vec;        // ALDS_X: rows can be read in 16-byte pieces
+  const float* ds;  // [M] (modes AGLOBAL, ALDS_Q)
+  int M, K, N, Nt, Kt, tps, SB;
+  int64_t ldq, ldl;
+  const u4* packed;
+  const float* beta;
+  void* y;
+  int y_dtype;
+  int32_t* ws_acc;
+  uint32_t* ws_cnt;
+};
+
+__device__ inline float x_at(const void* x, int dt, int64_t i) {
+  return dt == BITLINEAR_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i])
+                              : static_cast<const float*>(x)[i];
+}
+
+__device__ inline uint32_t quant1(float v, float qs) {
+  return (uint32_t)(int)fminf(fmaxf(rintf(v * qs), -127.0f), 127.0f) & 0xffu;
+}
+
+// 16-byte activation pieces a thread loads before the weight prefetch and
+// holds in registers until the weight loads are in flight.
+constexpr int kXReg = 8;
+
+// Staged prologue, part 1 (issued before the weight loads, so that waiting
+// for these pieces never waits for the weight stream): piece c of the
+// contiguous source rows (int8 rows of act_stride bytes, or 16-byte-aligned
+// bf16/fp32 rows) goes to v[r] for c = tid + r * blockDim.x.  Threads past
+// the last piece load a duplicate of the last piece (never stored, and a
+// duplicate cannot change a maximum).
+__device__ inline void stage_load(const u4* src, int npieces, u4 (&v)[kXReg]) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+#pragma unroll
+  for (int r = 0; r < kXReg; ++r) v[r] = src[min(tid + r * nthr, npieces - 1)];
+}
+
+// Part 2 for int8 rows: write the held pieces (and any beyond kXReg per
+// thread) to the padded LDS rows.
+__device__ void stage_store_q(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int cpr = (int)(a.ldq / 16), npieces = a.M * cpr;
+  const u4* src = reinterpret_cast<const u4*>(a.q);
+#pragma unroll
+  for (int r = 0; r < kXReg; ++r) {
+    const int c = tid + r * nthr;
+    if (c < npieces) {
+      const int m = c / cpr;
+      *reinterpret_cast<u4*>(lds + (int64_t)m * a.ldl + (c - m * cpr) * 16) = v[r];
+    }
+  }
+  for (int c = tid + kXReg * nthr; c < npieces; c += nthr) {
+    const int m = c / cpr;
+    *reinterpret_cast<u4*>(lds + (int64_t)m * a.ldl + (c - m * cpr) * 16) = src[c];
+  }
+  __syncthreads();
+}
+
+__device__ inline float piece_absmax(const u4 v, bool bf16) {
+  float r = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r = bf16 ? fmaxf(r, fmaxf(fabsf(__uint_as_float(v[j] << 16)), fabsf(__uint_as_float(v[j] & 0xffff0000u))))
+             : fmaxf(r, fabsf(__uint_as_float(v[j])));
+  return r;
+}
+
+// Quantize one 16-byte piece (8 bf16 or 4 fp32 values) into LDS at dst.
+__device__ inline void piece_quant_store(const u4 v, bool bf16, float qs, int8_t* dst) {
+  if (bf16) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lo |= quant1(__uint_as_float(v[j] << 16), qs) << (16 * j);
+      lo |= quant1(__uint_as_float(v[j] & 0xffff0000u), qs) << (16 * j + 8);
+      hi |= quant1(__uint_as_float(v[2 + j] << 16), qs) << (16 * j);
+      hi |= quant1(__uint_as_float(v[2 + j] & 0xffff0000u), qs) << (16 * j + 8);
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w |= quant1(__uint_as_float(v[j]), qs) << (8 * j);
+    *reinterpret_cast<uint32_t*>(dst) = w;
+  }
+}
+
+// Part 2 for bf16/fp32 rows (16-byte aligned, K a multiple of the piece):
+// row_g[m] = max |x[m][:]| from the held pieces, then each piece quantized
+// with q = clamp(rint(x * (127 / max(gamma, 1e-5))), -127, 127) into LDS.
+__device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds, float* row_g,
+                              float* row_qs) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+  const bool bf16 = a.x_dtype == BITLINEAR_BF16;
+  const int per16 = bf16 ? 8 : 4;
+  const int cpr = a.K / per16, npieces = a.M * cpr;
+  const u4* src = static_cast<const u4*>(a.x);
+  const int64_t Kp = (int64_t)a.Kt * kTileK;
+  // zero the padding columns [K, Kp) of every row (4-byte stores)
+  const int padw = (int)((Kp - a.K) / 4);
+  for (int i = tid; i < a.M * padw; i += nthr) {
+    const int m = i / padw;
+    *reinterpret_cast<uint32_t*>(lds + (int64_t)m * a.ldl + a.K + 4 * (i - m * padw)) = 0u;
+  }
+  for (int m = 0; m < a.M; ++m) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kXReg; ++r) {
+      const int c = tid + r * nthr;
+      if (c < npieces && c / cpr == m) amax = fmaxf(amax, piece_absmax(v[r], bf16));
+    }
+    for (int c = tid + kXReg * nthr; c < npieces; c += nthr)  // pieces beyond the held ones
+      if (c / cpr == m) amax = fmaxf(amax, piece_absmax(src[c], bf16));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    // |x| >= 0, so the fp32 bit patterns order like the values
+    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&row_g[m]), __float_as_uint(amax));
+  }
+  __syncthreads();
+  if (tid < a.M) row_qs[tid] = 127.0f / fmaxf(row_g[tid], 1e-5f);  // IEEE division
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kXReg; ++r) {
+    const int c = tid + r * nthr;
+    if (c < npieces) {
+      const int m = c / cpr;
+      piece_quant_store(v[r], bf16, row_qs[m], lds + (int64_t)m * a.ldl + (c - m * cpr) * per16);
+    }
+  }
+  for (int c = tid + kXReg * nthr; c < npieces; c += nthr) {
+    const int m = c / cpr;
+    piece_quant_store(src[c], bf16, row_qs[m], lds + (int64_t)m * a.ldl + (c - m * cpr) * per16);
+  }
+  __syncthreads();
+}
+
+// ALDS_X prologue for rows that are not 16-byte pieces (unaligned x or K not
+// a multiple of the piece): row_g[m] = max_k |x[m][k]|, then the int8 rows
+// into LDS, element by element.
+__device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, float* row_g) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+  const int M = a.M;
+  const int64_t Kp = (int64_t)a.Kt * kTileK;
+  const int per16 = a.x_dtype == BITLINEAR_BF16 ? 8 : 4;  // elements per 16 bytes
+  if (tid < 64) row_g[tid] = 0.0f;
+  __syncthreads();
+  for (int m = 0; m < M; ++m) {
+    float amax = 0.0f;
+    if (a.x_vec) {
+      const u4* row = reinterpret_cast<const u4*>(static_cast<const char*>(a.x) + (int64_t)m * a.K * (16 / per16));
+      for (int c = tid; c * per16 < a.K; c += nthr) {
+        const u4 v = row[c];
+        if (per16 == 8) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[j] << 16)), fabsf(__uint_as_float(v[j] & 0xffff0000u))));
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(__uint_as_float(v[j])));
+        }
+      }
+    } else {
+      for (int k = tid; k < a.K; k += nthr) amax = fmaxf(amax, fabsf(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k)));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    // |x| >= 0, so the fp32 bit patterns order like the values
+    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&row_g[m]), __float_as_uint(amax));
+  }
+  __syncthreads();
+  for (int m = 0; m < M; ++m) {
+    const float g = fmaxf(row_g[m], kEpsX);
+    const float qs = 127.0f / g;  // IEEE division, as the standalone quantizer
+    int8_t* lrow = lds + (int64_t)m * a.ldl;
+    if (a.x_vec) {
+      const u4* row = reinterpret_cast<const u4*>(static_cast<const char*>(a.x) + (int64_t)m * a.K * (16 / per16));
+      for (int c = tid; c * per16 < Kp; c += nthr) {
+        const int k = c * per16;
+        if (k < a.K) {
+          const u4 v = row[c];
+          if (per16 == 8) {
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              lo |= quant1(__uint_as_float(v[j] << 16), qs) << (16 * j);
+              lo |= quant1(__uint_as_float(v[j] & 0xffff0000u), qs) << (16 * j + 8);
+              hi |= quant1(__uint_as_float(v[2 + j] << 16), qs) << (16 * j);
+              hi |= quant1(__uint_as_float(v[2 + j] & 0xffff0000u), qs) << (16 * j + 8);
+            }
+            *reinterpret_cast<uint2*>(lrow + k) = make_uint2(lo, hi);
+          } else {
+            uint32_t w = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w |= quant1(__uint_as_float(v[j]), qs) << (8 * j);
+            *reinterpret_cast<uint32_t*>(lrow + k) = w;
+          }
+        } else if (per16 == 8) {
+          *reinterpret_cast<uint2*>(lrow + k) = make_uint2(0u, 0u);
+        } else {
+          *reinterpret_cast<uint32_t*>(lrow + k) = 0u;
+        }
+      }
+    } else {
+      for (int k = 4 * tid; k < Kp; k += 4 * nthr) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (k + j < a.K) w |= quant1(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k + j), qs) << (8 * j);
+        *reinterpret_cast<uint32_t*>(lrow + k) = w;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int MB, int NB, int AM, int kU = ring_depth(MB, NB, AM)>
+__global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int E = MB * NB * 4;  // accumulator values per lane
+  constexpr int UA = AM == AGLOBAL ? kU : 1;
   __shared__ int red[E][64];
+  constexpr bool FUSED = AM == ALDS_X || AM == ALDS_XS;
+  __shared__ float row_g[FUSED ? 64 : 1];   // fused: per-row gamma = max |x|
+  __shared__ float row_qs[FUSED ? 64 : 1];  // fused: per-row 127 / max(gamma, eps)
+  extern __shared__ __attribute__((aligned(16))) int8_t act_lds[];  // [M][ldl]
 
   const int lane = threadIdx.x & 63, waves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int grp = blockIdx.x / SB, sb = blockIdx.x - grp * SB;
+  const int grp = blockIdx.x / a.SB, sb = blockIdx.x - grp * a.SB;
   const int split = sb * waves + wave;
-  const int k0 = split * tps;
-  const int k1 = min(k0 + tps, Kt);
+  const int k0 = split * a.tps;
+  const int k1 = min(k0 + a.tps, a.Kt);
   const int nb0 = grp * NB;
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int M = a.M;
 
   v4i acc[MB][NB];
 #pragma unroll
@@ -92,58 +361,90 @@ __global__ __launch_bounds__(64 * Shape<MB>::MAXW) void gemv_t2_kernel(
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[mb][j] = v4i{0, 0, 0, 0};
 
-  // Per-lane activation rows.  Lanes of token rows >= M read row M-1 instead:
-  // their accumulators are never stored, so the loads need no branch.
-  const int8_t* arow[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    arow[mb] = q + (int64_t)min(mb * 16 + r16, M - 1) * ldq + 16 * g4;
   const u4* bptr[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int nb = min(nb0 + j, Nt - 1);  // blocks past Nt are masked at the store
-    bptr[j] = packed + (int64_t)nb * Kt * 64 + lane;
+    const int nb = min(nb0 + j, a.Nt - 1);  // blocks past Nt are masked at the store
+    bptr[j] = a.packed + (int64_t)nb * a.Kt * 64 + lane;
   }
+  // Activation operand rows.  Lanes of token rows >= M read row M-1 instead:
+  // their accumulators are never stored, so the loads need no branch.
+  int64_t aoff[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    aoff[mb] = (int64_t)min(mb * 16 + r16, M - 1) * (AM == AGLOBAL ? a.ldq : a.ldl) + 16 * g4;
 
   u4 wbuf[kU][NB];
-  v4i abuf[kU][MB][4];
-  auto load_tile = [&](int slot, int kt) {
+  v4i abuf[UA][MB][4];
+  auto load_w = [&](int slot, int kt) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) wbuf[slot][j] = __builtin_nontemporal_load(bptr[j] + (int64_t)kt * 64);
+  };
+  auto load_a = [&](int slot, int kt) {
+    const int8_t* base = AM == AGLOBAL ? a.q : act_lds;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        abuf[slot][mb][i] = *reinterpret_cast<const v4i*>(arow[mb] + (int64_t)kt * kTileK + 64 * i);
+        abuf[slot][mb][i] = *reinterpret_cast<const v4i*>(base + aoff[mb] + (int64_t)kt * kTileK + 64 * i);
   };
-  auto mma_tile = [&](int slot) {
+  auto mma_tile = [&](int slot, int kt) {
+    const int as = AM == AGLOBAL ? slot : 0;
+    if (AM != AGLOBAL) load_a(0, kt);  // LDS operands: read at use
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const v4i b = t2_field(wbuf[slot][j], i);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma16(abuf[slot][mb][i], b, acc[mb][j]);
+        for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma16(abuf[as][mb][i], b, acc[mb][j]);
       }
   };
 
-  if (k0 < k1) {
-    // ring of kU tiles in flight; the re-loads past the end read tile k1-1
-    // again (in bounds) and are never used
+  const bool has_work = k0 < k1;
+  // activation pieces first (few, cache-resident), then the weight stream
+  u4 stage[kXReg];
+  if constexpr (AM == ALDS_X) {
+    if (threadIdx.x < 64) row_g[threadIdx.x] = 0.0f;
+    stage_load(static_cast<const u4*>(a.x), a.M * (a.K / (a.x_dtype == BITLINEAR_BF16 ? 8 : 4)), stage);
+  }
+  if constexpr (AM == ALDS_Q) stage_load(reinterpret_cast<const u4*>(a.q), a.M * (int)(a.ldq / 16), stage);
+  // Unconditional, so the wait for the staged pieces never has to assume a
+  // path without weight loads (a wave without k-tiles reads tile 0 of its
+  // first block, in bounds, and never uses it).
+  const int kfirst = has_work ? k0 : 0, klast = has_work ? k1 - 1 : 0;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) load_tile(u, min(k0 + u, k1 - 1));
+  for (int u = 0; u < kU; ++u) load_w(u, min(kfirst + u, klast));
+  // keep the compiler from hoisting work on the staged pieces above the
+  // weight loads (that would wait for the pieces before the stream starts)
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (AM == ALDS_Q) stage_store_q(a, stage, act_lds);
+  if constexpr (AM == ALDS_X) {
+    __syncthreads();  // row_g cleared
+    stage_store_x(a, stage, act_lds, row_g, row_qs);
+  }
+  if constexpr (AM == ALDS_XS) quantize_rows_scalar(a, act_lds, row_g);
+
+  if (has_work) {
+    // ring of kU k-tiles in flight; re-loads past the end read tile k1-1
+    // again (in bounds) and are never used
+    if constexpr (AM == AGLOBAL) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) load_a(u, min(k0 + u, k1 - 1));
+    }
     int kt = k0;
     for (; kt + kU <= k1; kt += kU) {
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
-        mma_tile(u);
-        load_tile(u, min(kt + u + kU, k1 - 1));
+        mma_tile(u, kt + u);
+        load_w(u, min(kt + u + kU, k1 - 1));
+        if constexpr (AM == AGLOBAL) load_a(u, min(kt + u + kU, k1 - 1));
       }
     }
     const int rem = k1 - kt;
 #pragma unroll
     for (int u = 0; u < kU - 1; ++u)
-      if (u < rem) mma_tile(u);
+      if (u < rem) mma_tile(u, kt + u);
   }
 
   // ---- reduce the waves of this workgroup
@@ -166,9 +467,9 @@ __global__ __launch_bounds__(64 * Shape<MB>::MAXW) void gemv_t2_kernel(
         for (int r = 0; r < 4; ++r) acc[mb][j][r] = red[(mb * NB + j) * 4 + r][lane];
   }
 
-  // ---- combine workgroups (split K across the grid)
-  const int ldw = gridDim.x / SB * NB * kTileN;  // workspace row length
-  if (SB > 1) {
+  // ---- combine workgroups (K split across the grid; AGLOBAL plans only)
+  if (AM == AGLOBAL && a.SB > 1) {
+    const int ldw = gridDim.x / a.SB * NB * kTileN;  // workspace row length
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -178,14 +479,14 @@ __global__ __launch_bounds__(64 * Shape<MB>::MAXW) void gemv_t2_kernel(
           const int m = mb * 16 + 4 * g4 + r;
           const int n = (nb0 + j) * kTileN + r16;
           if (m < M)
-            __hip_atomic_fetch_add(ws_acc + (int64_t)m * ldw + n, acc[mb][j][r], __ATOMIC_RELAXED,
+            __hip_atomic_fetch_add(a.ws_acc + (int64_t)m * ldw + n, acc[mb][j][r], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     __threadfence();
     int last = 0;
     if (lane == 0)
-      last = __hip_atomic_fetch_add(ws_cnt + grp, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(SB - 1);
+      last = __hip_atomic_fetch_add(a.ws_cnt + grp, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(a.SB - 1);
     last = __shfl(last, 0, 64);
     if (!last) return;
     __threadfence();
@@ -197,61 +498,118 @@ __global__ __launch_bounds__(64 * Shape<MB>::MAXW) void gemv_t2_kernel(
         for (int r = 0; r < 4; ++r) {
           const int m = mb * 16 + 4 * g4 + r;
           const int n = (nb0 + j) * kTileN + r16;
-          acc[mb][j][r] = m < M ? __hip_atomic_exchange(ws_acc + (int64_t)m * ldw + n, 0, __ATOMIC_RELAXED,
+          acc[mb][j][r] = m < M ? __hip_atomic_exchange(a.ws_acc + (int64_t)m * ldw + n, 0, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT)
                                 : 0;
         }
-    if (lane == 0) __hip_atomic_store(ws_cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(a.ws_cnt + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- dequantize and store: lane holds rows 4*g4 + r of each token block,
   //      column r16 of each output block
-  const float bt = *beta;
+  const float bt = *a.beta;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int m = mb * 16 + 4 * g4 + r;
       if (m >= M) continue;
-      const float scale = ds[m] * bt;
+      const float dsm = FUSED ? fmaxf(row_g[m], kEpsX) / 127.0f : a.ds[m];
+      const float scale = dsm * bt;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int n = (nb0 + j) * kTileN + r16;
-        if (n < N) store_out(y, y_dtype, (int64_t)m * N + n, acc[mb][j][r], scale);
+        if (n < a.N) store_out(a.y, a.y_dtype, (int64_t)m * a.N + n, acc[mb][j][r], scale);
       }
     }
 }
 
-template <int MB>
-hipError_t launch_t(const GemvPlan& p, const int8_t* q, int64_t ldq, const float* ds, int64_t M,
-                    const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype,
-                    void* ws, hipStream_t s) {
-  int32_t* ws_acc = nullptr;
-  uint32_t* ws_cnt = nullptr;
-  if (p.SB > 1) {
-    ws_acc = static_cast<int32_t*>(ws);
-    ws_cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.ws_acc_bytes);
-  }
-  hipLaunchKernelGGL((gemv_t2_kernel<MB>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves), 0, s,
-                     q, ldq, ds, (int)M, reinterpret_cast<const u4*>(packed), beta, (int)N, p.Nt,
-                     p.Kt, p.tps, p.SB, y, y_dtype, ws_acc, ws_cnt);
+template <int MB, int NB, int AM>
+hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),
+                     (size_t)p.lds_bytes, s, a);
   return hipGetLastError();
+}
+
+template <int AM>
+hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+#define BL_GEMV_CASE(mb, nb) \
+  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM>(p, a, s)
+  BL_GEMV_CASE(1, 1);
+  BL_GEMV_CASE(1, 2);
+  BL_GEMV_CASE(1, 4);
+  BL_GEMV_CASE(2, 1);
+  BL_GEMV_CASE(2, 2);
+  BL_GEMV_CASE(3, 1);
+  BL_GEMV_CASE(4, 1);
+  if constexpr (AM == AGLOBAL) {
+    BL_GEMV_CASE(3, 2);
+    BL_GEMV_CASE(4, 2);
+    BL_GEMV_CASE(2, 4);
+  }
+#undef BL_GEMV_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  switch (p.amode) {
+    case ALDS_Q: return dispatch_mb_nb<ALDS_Q>(p, a, s);
+    case ALDS_X: return a.x_vec ? dispatch_mb_nb<ALDS_X>(p, a, s) : dispatch_mb_nb<ALDS_XS>(p, a, s);
+    default: return dispatch_mb_nb<AGLOBAL>(p, a, s);
+  }
+}
+
+GemvArgs make_args(const GemvPlan& p, int64_t M, int64_t K, int64_t N, const uint8_t* packed, const float* beta,
+                   void* y, int y_dtype, void* ws) {
+  GemvArgs a{};
+  a.M = (int)M;
+  a.K = (int)K;
+  a.N = (int)N;
+  a.Nt = p.Nt;
+  a.Kt = p.Kt;
+  a.tps = p.tps;
+  a.SB = p.SB;
+  a.ldq = (int64_t)p.Kt * kTileK;
+  a.ldl = lds_row(K);
+  a.packed = reinterpret_cast<const u4*>(packed);
+  a.beta = beta;
+  a.y = y;
+  a.y_dtype = y_dtype;
+  if (p.SB > 1) {
+    a.ws_acc = static_cast<int32_t*>(ws);
+    a.ws_cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.ws_acc_bytes);
+  }
+  return a;
 }
 
 }  // namespace
 
-int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K).ws_bytes; }
+int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, false).ws_bytes; }
+
+bool decode_fused_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= BITLINEAR_GEMV_MAX_M && M * lds_row(K) <= kDecodeLdsBytes;
+}
 
 hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s) {
-  const GemvPlan p = make_plan(M, N, K);
-  switch (p.MB) {
-    case 1: return launch_t<1>(p, q, ldq, ds, M, packed, beta, N, y, y_dtype, ws, s);
-    case 2: return launch_t<2>(p, q, ldq, ds, M, packed, beta, N, y, y_dtype, ws, s);
-    case 3: return launch_t<3>(p, q, ldq, ds, M, packed, beta, N, y, y_dtype, ws, s);
-    default: return launch_t<4>(p, q, ldq, ds, M, packed, beta, N, y, y_dtype, ws, s);
-  }
+  const GemvPlan p = make_plan(M, N, K, false);
+  GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, ws);
+  a.q = q;
+  a.ldq = ldq;
+  a.ds = ds;
+  return dispatch(p, a, s);
+}
+
+hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
+                            const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+  const GemvPlan p = make_plan(M, N, K, true);
+  GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr);
+  a.x = x;
+  a.x_dtype = x_dtype;
+  const int per16 = x_dtype == BITLINEAR_BF16 ? 8 : 4;
+  a.x_vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  return dispatch(p, a, s);
 }
 
 }  // namespace bl

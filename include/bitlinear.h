@@ -153,6 +153,25 @@ int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
                    const float *w_beta, int64_t N, void *y, int y_dtype, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/* LDS budget of the decode kernels for int8 activation rows (see below). */
+#define BITLINEAR_DECODE_MAX_ACT_BYTES 58368
+
+/*
+ * Whole BitLinear forward for decode, in one launch: per-token absmax int8
+ * quantization of x (as bitlinear_quant_act) fused into the ternary product
+ * with dequantization (as bitlinear_gemv).  Each workgroup quantizes the
+ * token rows into its own LDS, so no int8 buffer is written.  Results are
+ * identical to bitlinear_quant_act followed by bitlinear_gemv.
+ *   x       [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32
+ *           (element alignment).
+ *   packed, w_beta, y, y_dtype  as bitlinear_gemv.
+ * Needs M * (bitlinear_act_stride(K) + 16) <= BITLINEAR_DECODE_MAX_ACT_BYTES,
+ * else BITLINEAR_ERR_UNSUPPORTED (use bitlinear_quant_act + bitlinear_gemv).
+ * Other errors as bitlinear_gemv.  Uses no workspace.
+ */
+int bitlinear_forward_decode(const void *x, int x_dtype, int64_t M, int64_t K, const void *packed,
+                             const float *w_beta, int64_t N, void *y, int y_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,6 +40,7 @@ def test_header_constants_match_binding():
     assert int(consts["BITLINEAR_I32"]) == bl.I32
     assert int(consts["BITLINEAR_MAX_K"]) == bl.MAX_K
     assert int(consts["BITLINEAR_GEMV_MAX_M"]) == bl.GEMV_MAX_M
+    assert int(consts["BITLINEAR_DECODE_MAX_ACT_BYTES"]) == bl.DECODE_MAX_ACT_BYTES
 
 
 def test_size_helpers():
@@ -136,3 +137,25 @@ def test_error_string_is_thread_local():
     th.join()
     assert seen["msg"] == ""
     assert "K=0" in bl.last_error()
+
+
+def test_forward_decode_validation():
+    fn = bl.lib().bitlinear_forward_decode
+    ok_args = dict(x=FAKE, xdt=bl.BF16, M=1, K=256, packed=FAKE, beta=FAKE, N=16, y=FAKE, ydt=bl.F32)
+
+    def call(**kw):
+        a = dict(ok_args, **kw)
+        return fn(a["x"], a["xdt"], a["M"], a["K"], a["packed"], a["beta"], a["N"], a["y"], a["ydt"], None)
+    assert call(x=None) == bl.ERR_ARG
+    assert call(xdt=bl.I32) == bl.ERR_ARG
+    assert call(ydt=9) == bl.ERR_ARG
+    assert call(M=65) == bl.ERR_SHAPE
+    assert call(K=0) == bl.ERR_SHAPE
+    assert call(x=FAKE + 1) == bl.ERR_ALIGN
+    assert call(packed=FAKE + 8) == bl.ERR_ALIGN
+    # activations that do not fit the workgroup's LDS: use quant_act + gemv instead
+    assert call(M=8, K=8192) == bl.ERR_UNSUPPORTED
+    assert "exceeds" in bl.last_error()
+    assert call(M=0) == bl.OK
+    assert bl.decode_fits(1, 28672) and bl.decode_fits(2, 28672) and bl.decode_fits(8, 6912)
+    assert not bl.decode_fits(8, 8192)

@@ -44,8 +44,12 @@ def gpu_pack(w: np.ndarray):
 def gpu_forward(xb, packed, beta, N, K, out_dtype, use_gemm):
     x = to_dev_bf16(xb)
     M = x.shape[0]
-    x_q, x_ds = bl.quant_act(x)
     y = torch.empty((M, N), dtype=out_dtype, device=DEV)
+    if use_gemm == "fused":
+        bl.bitlinear_forward_decode(x, packed, beta, N, y)
+        torch.cuda.synchronize()
+        return y
+    x_q, x_ds = bl.quant_act(x)
     if use_gemm:
         ws = bl.workspace(bl.gemm_workspace_bytes(M, N, K), DEV)
         bl.bitlinear_gemm(x_q, x_ds, K, packed, beta, N, y, ws)
@@ -144,7 +148,7 @@ def test_pack_zero_and_tie_weights():
 
 
 # --------------------------------------------------------------- products
-def test_hand_example_on_gpu(golden_dir):
+def test_hand_example_on_gpu(golden_dir):  # noqa: C901
     import json
     import os
     with open(os.path.join(golden_dir, "hand_4x4.json")) as f:
@@ -152,7 +156,7 @@ def test_hand_example_on_gpu(golden_dir):
     w = np.array(h["w"], dtype=np.float32)
     x = np.array(h["x"], dtype=np.float32)
     xb = (x.view(np.uint32) >> 16).astype(np.uint16)
-    for use_gemm in (False, True):
+    for use_gemm in (False, True, "fused"):
         packed, beta = gpu_pack(w)
         assert beta.cpu().item() == h["beta"]
         acc = gpu_forward(xb, packed, beta, 4, 4, torch.int32, use_gemm).cpu().numpy()
@@ -167,6 +171,32 @@ def test_gemv_parity(M, N, K):
     w = workloads.gen_weights(N, K, seed=1000 + N)
     xb = workloads.gen_acts_bf16(M, K, seed=2000 + M, outliers=True)
     check_product(xb, w, use_gemm=False)
+
+
+@pytest.mark.parametrize("M", [1, 2, 8, 16, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(16, 256), (40, 700), (512, 512), (100, 3000), (2000, 300)])
+def test_forward_decode_parity(M, N, K):
+    if not bl.decode_fits(M, K):
+        pytest.skip("activations exceed the fused kernel's LDS budget")
+    w = workloads.gen_weights(N, K, seed=5000 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=6000 + M, outliers=True)
+    check_product(xb, w, use_gemm="fused")
+
+
+def test_forward_decode_f32_input_and_zero_row():
+    M, N, K = 3, 80, 1000
+    w = workloads.gen_weights(N, K, seed=70)
+    x = workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, K, seed=71)) * np.float32(1.37)
+    x[1] = 0
+    q, ds, _ = oracle.quant_act(x)
+    beta = oracle.absmean(w)
+    acc = oracle.matmul_i32(q, oracle.ternarize(w, beta))
+    y_ref = oracle.dequant(acc, ds, beta)
+    packed, b = gpu_pack(w)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    bl.bitlinear_forward_decode(torch.from_numpy(x).to(DEV), packed, b, N, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y.cpu().numpy(), y_ref)
 
 
 @pytest.mark.parametrize("M", [1, 16, 65, 100, 128, 129, 300])
