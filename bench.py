@@ -14,9 +14,9 @@ graph replay (no host launch overhead inside the timed region).
 value = packed weight bytes of the step x K / elapsed time, in GB/s.
 
 Also printed on the same JSON line:
-  roofline      the GEMV kernel: algorithmic bytes per launch / its average
-                launch duration (HIP events around each launch, on the launch
-                stream), against the 8 TB/s HBM peak;
+  roofline      the decode kernel: algorithmic bytes per launch / its average
+                launch duration (HIP events on the launch stream around a
+                graph of back-to-back launches), against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) running the same
                 step on the host cores, on a bounded number of repetitions;
   also          the other workloads: 100B-class decode (M = 1, 8, 32) in GB/s
@@ -65,7 +65,9 @@ class Linear:
         self.beta = beta
         self.x = x
         if mode is None:
-            mode = "fused" if bl.decode_fits(M, K) else ("gemv" if M <= bl.GEMV_MAX_M else "gemm")
+            # the fused decode kernel wins while the quantization it repeats per
+            # workgroup is small (measured: M <= 4); the GEMV otherwise
+            mode = "fused" if (M <= 4 and bl.decode_fits(M, K)) else ("gemv" if M <= bl.GEMV_MAX_M else "gemm")
         self.mode = mode
         self.x_q = torch.empty((M, bl.act_stride(K)), dtype=torch.int8, device=dev)
         self.x_ds = torch.empty((M,), dtype=torch.float32, device=dev)

@@ -207,7 +207,7 @@ def linear(x, packed, w_beta, N: int, out_dtype=torch.float32, stream=None):
     """BitLinear forward: quantize x [M][K], then gemv (M <= 64) or gemm."""
     M, K = x.shape
     y = torch.empty((M, N), dtype=out_dtype, device=x.device)
-    if decode_fits(M, K):
+    if M <= 4 and decode_fits(M, K):
         bitlinear_forward_decode(x, packed, w_beta, N, y, stream)
         return y
     x_q, x_ds = quant_act(x, stream=stream)

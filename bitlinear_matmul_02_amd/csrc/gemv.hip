@@ -137,9 +137,6 @@ __device__ inline float x_at(const void* x, int dt, int64_t i) {
                               : static_cast<const float*>(x)[i];
 }
 
-__device__ inline uint32_t quant1(float v, float qs) {
-  return (uint32_t)(int)fminf(fmaxf(rintf(v * qs), -127.0f), 127.0f) & 0xffu;
-}
 
 // 16-byte activation pieces a thread loads before the weight prefetch and
 // holds in registers until the weight loads are in flight.
@@ -178,112 +175,124 @@ __device__ void stage_store_q(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
   __syncthreads();
 }
 
-__device__ inline float piece_absmax(const u4 v, bool bf16) {
-  float r = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    r = bf16 ? fmaxf(r, fmaxf(fabsf(__uint_as_float(v[j] << 16)), fabsf(__uint_as_float(v[j] & 0xffff0000u))))
-             : fmaxf(r, fabsf(__uint_as_float(v[j])));
-  return r;
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+// max |x| over a 16-byte piece (8 bf16 or 4 fp32 values) as fp32 bits: with
+// the sign bits cleared the bit patterns order like the magnitudes, so the
+// maximum is taken on integers (packed 16-bit for bf16).
+__device__ inline uint32_t piece_absmax_bits(const u4 v, bool bf16) {
+  if (bf16) {
+    us2 m = __builtin_bit_cast(us2, v[0] & 0x7fff7fffu);
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[1] & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[2] & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[3] & 0x7fff7fffu));
+    return (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+  }
+  return max(max(v[0] & 0x7fffffffu, v[1] & 0x7fffffffu), max(v[2] & 0x7fffffffu, v[3] & 0x7fffffffu));
+}
+
+// One int8 code q = rint(x * qs) as a byte.  |x * qs| <= 127 * (1 + 2^-23)
+// because |x| <= g and qs = fl(127 / g), so adding 1.5 * 2^23 rounds the
+// product to the nearest integer, ties to even (the sum lies in [2^23, 2^24)
+// where the float spacing is 1), the integer sits in the low mantissa bits,
+// and the clamp to [-127, 127] can never act.  Multiply and add are separate
+// roundings (no contraction), exactly as rint(fl(x * qs)).
+__device__ inline uint32_t qbyte(float x, float qs) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(x, qs), 12582912.0f)) & 0xffu;
 }
 
 // Quantize one 16-byte piece (8 bf16 or 4 fp32 values) into LDS at dst.
 __device__ inline void piece_quant_store(const u4 v, bool bf16, float qs, int8_t* dst) {
   if (bf16) {
-    uint32_t lo = 0, hi = 0;
+    uint32_t w[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lo |= quant1(__uint_as_float(v[j] << 16), qs) << (16 * j);
-      lo |= quant1(__uint_as_float(v[j] & 0xffff0000u), qs) << (16 * j + 8);
-      hi |= quant1(__uint_as_float(v[2 + j] << 16), qs) << (16 * j);
-      hi |= quant1(__uint_as_float(v[2 + j] & 0xffff0000u), qs) << (16 * j + 8);
-    }
-    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    for (int h = 0; h < 2; ++h)
+      w[h] = qbyte(__uint_as_float(v[2 * h] << 16), qs) | (qbyte(__uint_as_float(v[2 * h] & 0xffff0000u), qs) << 8) |
+             (qbyte(__uint_as_float(v[2 * h + 1] << 16), qs) << 16) |
+             (qbyte(__uint_as_float(v[2 * h + 1] & 0xffff0000u), qs) << 24);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
   } else {
-    uint32_t w = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w |= quant1(__uint_as_float(v[j]), qs) << (8 * j);
-    *reinterpret_cast<uint32_t*>(dst) = w;
+    *reinterpret_cast<uint32_t*>(dst) = qbyte(__uint_as_float(v[0]), qs) | (qbyte(__uint_as_float(v[1]), qs) << 8) |
+                                        (qbyte(__uint_as_float(v[2]), qs) << 16) |
+                                        (qbyte(__uint_as_float(v[3]), qs) << 24);
   }
 }
 
+// Row of piece c (cpr pieces per row); exact for c < 2^24 (the float error of
+// (c + 0.5) / cpr is far below the 0.5 / cpr margin to a row boundary).
+__device__ inline int piece_row(int c, int M, float inv_cpr) {
+  return M == 1 ? 0 : (int)(((float)c + 0.5f) * inv_cpr);
+}
+
 // Part 2 for bf16/fp32 rows (16-byte aligned, K a multiple of the piece):
-// row_g[m] = max |x[m][:]| from the held pieces, then each piece quantized
-// with q = clamp(rint(x * (127 / max(gamma, 1e-5))), -127, 127) into LDS.
-__device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds, float* row_g,
-                              float* row_qs) {
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+// gamma_m = max |x[m][:]| from the held pieces (per-wave maxima in LDS slots,
+// combined by thread m), then each piece quantized with
+// q = rint(x * (127 / max(gamma, 1e-5))) into LDS.  `slots` holds at least
+// waves * M words.
+__device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds, uint32_t* slots,
+                              float* row_g, float* row_qs) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, waves = nthr >> 6;
   const bool bf16 = a.x_dtype == BITLINEAR_BF16;
   const int per16 = bf16 ? 8 : 4;
-  const int cpr = a.K / per16, npieces = a.M * cpr;
+  const int M = a.M, cpr = a.K / per16, npieces = M * cpr;
+  const float inv_cpr = 1.0f / (float)cpr;
   const u4* src = static_cast<const u4*>(a.x);
   const int64_t Kp = (int64_t)a.Kt * kTileK;
   // zero the padding columns [K, Kp) of every row (4-byte stores)
   const int padw = (int)((Kp - a.K) / 4);
-  for (int i = tid; i < a.M * padw; i += nthr) {
+  for (int i = tid; i < M * padw; i += nthr) {
     const int m = i / padw;
     *reinterpret_cast<uint32_t*>(lds + (int64_t)m * a.ldl + a.K + 4 * (i - m * padw)) = 0u;
   }
-  for (int m = 0; m < a.M; ++m) {
-    float amax = 0.0f;
+  for (int m = 0; m < M; ++m) {
+    uint32_t amax = 0;
 #pragma unroll
     for (int r = 0; r < kXReg; ++r) {
       const int c = tid + r * nthr;
-      if (c < npieces && c / cpr == m) amax = fmaxf(amax, piece_absmax(v[r], bf16));
+      if (c < npieces && piece_row(c, M, inv_cpr) == m) amax = max(amax, piece_absmax_bits(v[r], bf16));
     }
     for (int c = tid + kXReg * nthr; c < npieces; c += nthr)  // pieces beyond the held ones
-      if (c / cpr == m) amax = fmaxf(amax, piece_absmax(src[c], bf16));
+      if (piece_row(c, M, inv_cpr) == m) amax = max(amax, piece_absmax_bits(src[c], bf16));
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    // |x| >= 0, so the fp32 bit patterns order like the values
-    if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&row_g[m]), __float_as_uint(amax));
+    for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+    if (lane == 0) slots[wave * M + m] = amax;
   }
   __syncthreads();
-  if (tid < a.M) row_qs[tid] = 127.0f / fmaxf(row_g[tid], 1e-5f);  // IEEE division
+  if (tid < M) {
+    uint32_t g = 0;
+    for (int w = 0; w < waves; ++w) g = max(g, slots[w * M + tid]);
+    const float gm = fmaxf(__uint_as_float(g), 1e-5f);
+    row_g[tid] = gm;
+    row_qs[tid] = 127.0f / gm;  // IEEE division, as the standalone quantizer
+  }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kXReg; ++r) {
     const int c = tid + r * nthr;
     if (c < npieces) {
-      const int m = c / cpr;
+      const int m = piece_row(c, M, inv_cpr);
       piece_quant_store(v[r], bf16, row_qs[m], lds + (int64_t)m * a.ldl + (c - m * cpr) * per16);
     }
   }
   for (int c = tid + kXReg * nthr; c < npieces; c += nthr) {
-    const int m = c / cpr;
+    const int m = piece_row(c, M, inv_cpr);
     piece_quant_store(src[c], bf16, row_qs[m], lds + (int64_t)m * a.ldl + (c - m * cpr) * per16);
   }
   __syncthreads();
 }
 
-// ALDS_X prologue for rows that are not 16-byte pieces (unaligned x or K not
-// a multiple of the piece): row_g[m] = max_k |x[m][k]|, then the int8 rows
-// into LDS, element by element.
+// ALDS_XS prologue, for rows that are not whole 16-byte pieces (unaligned x
+// or K not a multiple of the piece): row_g[m] = max(max_k |x[m][k]|, 1e-5),
+// then the int8 rows into LDS, element by element.
 __device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, float* row_g) {
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
   const int M = a.M;
   const int64_t Kp = (int64_t)a.Kt * kTileK;
-  const int per16 = a.x_dtype == BITLINEAR_BF16 ? 8 : 4;  // elements per 16 bytes
   if (tid < 64) row_g[tid] = 0.0f;
   __syncthreads();
   for (int m = 0; m < M; ++m) {
     float amax = 0.0f;
-    if (a.x_vec) {
-      const u4* row = reinterpret_cast<const u4*>(static_cast<const char*>(a.x) + (int64_t)m * a.K * (16 / per16));
-      for (int c = tid; c * per16 < a.K; c += nthr) {
-        const u4 v = row[c];
-        if (per16 == 8) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(v[j] << 16)), fabsf(__uint_as_float(v[j] & 0xffff0000u))));
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(__uint_as_float(v[j])));
-        }
-      }
-    } else {
-      for (int k = tid; k < a.K; k += nthr) amax = fmaxf(amax, fabsf(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k)));
-    }
+    for (int k = tid; k < a.K; k += nthr) amax = fmaxf(amax, fabsf(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k)));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     // |x| >= 0, so the fp32 bit patterns order like the values
@@ -294,44 +303,16 @@ __device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, float* row_
     const float g = fmaxf(row_g[m], kEpsX);
     const float qs = 127.0f / g;  // IEEE division, as the standalone quantizer
     int8_t* lrow = lds + (int64_t)m * a.ldl;
-    if (a.x_vec) {
-      const u4* row = reinterpret_cast<const u4*>(static_cast<const char*>(a.x) + (int64_t)m * a.K * (16 / per16));
-      for (int c = tid; c * per16 < Kp; c += nthr) {
-        const int k = c * per16;
-        if (k < a.K) {
-          const u4 v = row[c];
-          if (per16 == 8) {
-            uint32_t lo = 0, hi = 0;
+    for (int k = 4 * tid; k < Kp; k += 4 * nthr) {
+      uint32_t w = 0;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              lo |= quant1(__uint_as_float(v[j] << 16), qs) << (16 * j);
-              lo |= quant1(__uint_as_float(v[j] & 0xffff0000u), qs) << (16 * j + 8);
-              hi |= quant1(__uint_as_float(v[2 + j] << 16), qs) << (16 * j);
-              hi |= quant1(__uint_as_float(v[2 + j] & 0xffff0000u), qs) << (16 * j + 8);
-            }
-            *reinterpret_cast<uint2*>(lrow + k) = make_uint2(lo, hi);
-          } else {
-            uint32_t w = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w |= quant1(__uint_as_float(v[j]), qs) << (8 * j);
-            *reinterpret_cast<uint32_t*>(lrow + k) = w;
-          }
-        } else if (per16 == 8) {
-          *reinterpret_cast<uint2*>(lrow + k) = make_uint2(0u, 0u);
-        } else {
-          *reinterpret_cast<uint32_t*>(lrow + k) = 0u;
-        }
-      }
-    } else {
-      for (int k = 4 * tid; k < Kp; k += 4 * nthr) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (k + j < a.K) w |= quant1(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k + j), qs) << (8 * j);
-        *reinterpret_cast<uint32_t*>(lrow + k) = w;
-      }
+      for (int j = 0; j < 4; ++j)
+        if (k + j < a.K) w |= qbyte(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k + j), qs) << (8 * j);
+      *reinterpret_cast<uint32_t*>(lrow + k) = w;
     }
   }
+  __syncthreads();
+  if (tid < M) row_g[tid] = fmaxf(row_g[tid], kEpsX);
   __syncthreads();
 }
 
@@ -341,7 +322,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   constexpr int UA = AM == AGLOBAL ? kU : 1;
   __shared__ int red[E][64];
   constexpr bool FUSED = AM == ALDS_X || AM == ALDS_XS;
-  __shared__ float row_g[FUSED ? 64 : 1];   // fused: per-row gamma = max |x|
+  __shared__ float row_g[FUSED ? 64 : 1];   // fused: per-row g = max(max |x|, 1e-5)
   __shared__ float row_qs[FUSED ? 64 : 1];  // fused: per-row 127 / max(gamma, eps)
   extern __shared__ __attribute__((aligned(16))) int8_t act_lds[];  // [M][ldl]
 
@@ -405,7 +386,6 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // activation pieces first (few, cache-resident), then the weight stream
   u4 stage[kXReg];
   if constexpr (AM == ALDS_X) {
-    if (threadIdx.x < 64) row_g[threadIdx.x] = 0.0f;
     stage_load(static_cast<const u4*>(a.x), a.M * (a.K / (a.x_dtype == BITLINEAR_BF16 ? 8 : 4)), stage);
   }
   if constexpr (AM == ALDS_Q) stage_load(reinterpret_cast<const u4*>(a.q), a.M * (int)(a.ldq / 16), stage);
@@ -419,10 +399,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // weight loads (that would wait for the pieces before the stream starts)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AM == ALDS_Q) stage_store_q(a, stage, act_lds);
-  if constexpr (AM == ALDS_X) {
-    __syncthreads();  // row_g cleared
-    stage_store_x(a, stage, act_lds, row_g, row_qs);
-  }
+  if constexpr (AM == ALDS_X) stage_store_x(a, stage, act_lds, reinterpret_cast<uint32_t*>(&red[0][0]), row_g, row_qs);
   if constexpr (AM == ALDS_XS) quantize_rows_scalar(a, act_lds, row_g);
 
   if (has_work) {
@@ -514,7 +491,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     for (int r = 0; r < 4; ++r) {
       const int m = mb * 16 + 4 * g4 + r;
       if (m >= M) continue;
-      const float dsm = FUSED ? fmaxf(row_g[m], kEpsX) / 127.0f : a.ds[m];
+      const float dsm = FUSED ? row_g[m] / 127.0f : a.ds[m];
       const float scale = dsm * bt;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -535,9 +512,9 @@ template <int AM>
 hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 #define BL_GEMV_CASE(mb, nb) \
   if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM>(p, a, s)
+  // the (MB, NB) pairs make_plan can produce for this mode
   BL_GEMV_CASE(1, 1);
   BL_GEMV_CASE(1, 2);
-  BL_GEMV_CASE(1, 4);
   BL_GEMV_CASE(2, 1);
   BL_GEMV_CASE(2, 2);
   BL_GEMV_CASE(3, 1);

@@ -2,153 +2,174 @@
 // ("Key Technologies Enabling the BitNET Family", Advanced Quantization
 // Methodologies: 8-bit activations by absmax, per token).
 //
-// One workgroup of 256 threads per token row.  Pass 1 finds gamma = max|x|
-// with a wavefront butterfly (DPP/ds_swizzle via __shfl_xor) and one LDS
-// exchange between the four waves; pass 2 re-reads the row (an L2 hit) and
-// writes q = clamp(rint(x * (127/g)), -127, 127), g = max(gamma, 1e-5), eight
-// elements per thread per step, plus zero padding up to the row stride.
+// One workgroup per token row.  Each thread loads its 16-byte pieces of the
+// row (8 bf16 or 4 fp32 values) once and keeps up to kHold of them in
+// registers: the row maximum of |x| is taken on the sign-cleared bit patterns
+// (packed 16-bit integer max for bf16), reduced across the wave with
+// butterfly shuffles and across waves through LDS; then every held piece is
+// quantized, q = rint(x * (127 / g)), g = max(gamma, 1e-5), and stored as
+// int8 (zero padding up to the row stride).  Rows that are not whole 16-byte
+// pieces (unaligned x, or K not a multiple of the piece) take an element
+// path.  Long rows get 1024 threads, short ones 256.
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr float kEpsX = 1e-5f;
+constexpr int kHold = 4;  // pieces per thread kept in registers
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t piece_absmax_bits(const u4 v, bool bf16) {
+  if (bf16) {
+    us2 m = __builtin_bit_cast(us2, v[0] & 0x7fff7fffu);
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[1] & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[2] & 0x7fff7fffu));
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(us2, v[3] & 0x7fff7fffu));
+    return (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+  }
+  return max(max(v[0] & 0x7fffffffu, v[1] & 0x7fffffffu), max(v[2] & 0x7fffffffu, v[3] & 0x7fffffffu));
 }
 
-__device__ inline int wave_sum(int v) {
+// q = rint(x * qs) as a byte.  |x * qs| <= 127 * (1 + 2^-23) since |x| <= g
+// and qs = fl(127 / g): adding 1.5 * 2^23 rounds the product to the nearest
+// integer, ties to even, into the low mantissa bits, and the clamp to
+// [-127, 127] never acts.  Separate multiply and add roundings.
+__device__ inline uint32_t qbyte(float x, float qs) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(x, qs), 12582912.0f)) & 0xffu;
+}
+
+// Quantize one piece; returns the codes' sum and writes 8 (bf16) or 4 bytes.
+__device__ inline int piece_quant_store(const u4 v, bool bf16, float qs, int8_t* dst) {
+  int sum = 0;
+  if (bf16) {
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t b0 = qbyte(__uint_as_float(v[2 * h] << 16), qs);
+      const uint32_t b1 = qbyte(__uint_as_float(v[2 * h] & 0xffff0000u), qs);
+      const uint32_t b2 = qbyte(__uint_as_float(v[2 * h + 1] << 16), qs);
+      const uint32_t b3 = qbyte(__uint_as_float(v[2 * h + 1] & 0xffff0000u), qs);
+      w[h] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      sum += (int)(int8_t)b0 + (int)(int8_t)b1 + (int)(int8_t)b2 + (int)(int8_t)b3;
+    }
+    *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+  } else {
+    const uint32_t b0 = qbyte(__uint_as_float(v[0]), qs), b1 = qbyte(__uint_as_float(v[1]), qs);
+    const uint32_t b2 = qbyte(__uint_as_float(v[2]), qs), b3 = qbyte(__uint_as_float(v[3]), qs);
+    *reinterpret_cast<uint32_t*>(dst) = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    sum = (int)(int8_t)b0 + (int)(int8_t)b1 + (int)(int8_t)b2 + (int)(int8_t)b3;
+  }
+  return sum;
+}
+
+__device__ inline float load_x(const void* x, bool bf16, int64_t i) {
+  return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
+}
+
+// Block-wide max of non-negative float bit patterns / sum of ints via LDS.
+template <int NT>
+__device__ inline uint32_t block_max(uint32_t v, uint32_t* slots) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = slots[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) r = max(r, slots[w]);
+  return r;
+}
+
+template <int NT>
+__device__ inline int block_sum(int v, int* slots) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
-template <int XDT>
-__device__ inline float load_x(const void* x, int64_t i) {
-  if constexpr (XDT == BITLINEAR_BF16)
-    return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
-  else
-    return static_cast<const float*>(x)[i];
-}
-
-// Eight consecutive elements starting at i (caller guarantees 16-byte
-// alignment for bf16 / 16-byte alignment of each half for fp32).
-template <int XDT>
-__device__ inline void load_x8(const void* x, int64_t i, float (&v)[8]) {
-  if constexpr (XDT == BITLINEAR_BF16) {
-    const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + i);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int r = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = __uint_as_float(w[j] << 16);
-      v[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-    }
-  } else {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + i);
-    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + i + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
+  for (int w = 0; w < NT / 64; ++w) r += slots[w];
+  return r;
 }
 
-__device__ inline int quant1(float x, float qs) {
-  const float r = rintf(x * qs);
-  return (int)fminf(fmaxf(r, -127.0f), 127.0f);
-}
-
-template <int XDT, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_act_kernel(const void* __restrict__ x,
-                                                              int64_t K, int64_t ldq,
-                                                              int8_t* __restrict__ q,
-                                                              float* __restrict__ ds,
-                                                              int32_t* __restrict__ rowsum) {
-  __shared__ float red_f[kThreads / 64];
-  __shared__ int red_i[kThreads / 64];
+template <int NT, bool VEC>
+__global__ __launch_bounds__(NT) void quant_act_kernel(const void* __restrict__ x, int bf16i, int64_t K,
+                                                       int64_t ldq, int8_t* __restrict__ q,
+                                                       float* __restrict__ ds, int32_t* __restrict__ rowsum) {
+  __shared__ uint32_t slots_max[NT / 64];
+  __shared__ int slots_sum[NT / 64];
+  const bool bf16 = bf16i != 0;
   const int64_t m = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t base = m * K;
-
-  // pass 1: gamma = max |x|
-  float amax = 0.0f;
-  if constexpr (VEC) {
-    for (int64_t k = 8 * (int64_t)tid; k < K; k += 8 * kThreads) {
-      float v[8];
-      load_x8<XDT>(x, base + k, v);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    }
-  } else {
-    for (int64_t k = tid; k < K; k += kThreads) amax = fmaxf(amax, fabsf(load_x<XDT>(x, base + k)));
-  }
-  amax = wave_max(amax);
-  if (lane == 0) red_f[wave] = amax;
-  __syncthreads();
-  float gamma = red_f[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) gamma = fmaxf(gamma, red_f[w]);
-
-  const float g = fmaxf(gamma, kEpsX);
-  const float qs = 127.0f / g;  // IEEE division (correctly rounded build)
-
-  // pass 2: quantize, 8 elements -> one 8-byte store
+  const int tid = threadIdx.x;
   int8_t* qrow = q + m * ldq;
+  float g;
   int sum = 0;
-  for (int64_t k = 8 * (int64_t)tid; k < ldq; k += 8 * kThreads) {
-    int c[8];
-    if (VEC && k + 8 <= K) {
-      float v[8];
-      load_x8<XDT>(x, base + k, v);
+  if constexpr (VEC) {
+    const int per16 = bf16 ? 8 : 4;
+    const int np = (int)(K / per16);  // pieces in the row
+    const u4* src = reinterpret_cast<const u4*>(static_cast<const char*>(x) + m * K * (bf16 ? 2 : 4));
+    u4 v[kHold];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = quant1(v[j], qs);
-    } else {
+    for (int r = 0; r < kHold; ++r) v[r] = src[min(tid + r * NT, np - 1)];  // duplicates never stored
+    uint32_t amax = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = (k + j < K) ? quant1(load_x<XDT>(x, base + k + j), qs) : 0;
+    for (int r = 0; r < kHold; ++r) amax = max(amax, piece_absmax_bits(v[r], bf16));
+    for (int c = tid + kHold * NT; c < np; c += NT) amax = max(amax, piece_absmax_bits(src[c], bf16));
+    g = fmaxf(__uint_as_float(block_max<NT>(amax, slots_max)), kEpsX);
+    const float qs = 127.0f / g;  // IEEE division
+#pragma unroll
+    for (int r = 0; r < kHold; ++r) {
+      const int c = tid + r * NT;
+      if (c < np) sum += piece_quant_store(v[r], bf16, qs, qrow + (int64_t)c * per16);
     }
-    uint32_t lo = 0, hi = 0;
+    for (int c = tid + kHold * NT; c < np; c += NT) sum += piece_quant_store(src[c], bf16, qs, qrow + (int64_t)c * per16);
+    for (int64_t k = K + 4 * (int64_t)tid; k < ldq; k += 4 * NT) *reinterpret_cast<uint32_t*>(qrow + k) = 0u;
+  } else {
+    float amax = 0.0f;
+    for (int64_t k = tid; k < K; k += NT) amax = fmaxf(amax, fabsf(load_x(x, bf16, m * K + k)));
+    g = fmaxf(__uint_as_float(block_max<NT>(__float_as_uint(amax), slots_max)), kEpsX);
+    const float qs = 127.0f / g;
+    for (int64_t k = 4 * (int64_t)tid; k < ldq; k += 4 * NT) {
+      uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= (uint32_t)(c[j] & 0xff) << (8 * j);
-      hi |= (uint32_t)(c[4 + j] & 0xff) << (8 * j);
-      sum += c[j] + c[4 + j];
+      for (int j = 0; j < 4; ++j)
+        if (k + j < K) {
+          const uint32_t b = qbyte(load_x(x, bf16, m * K + k + j), qs);
+          w |= b << (8 * j);
+          sum += (int)(int8_t)b;
+        }
+      *reinterpret_cast<uint32_t*>(qrow + k) = w;
     }
-    *reinterpret_cast<uint2*>(qrow + k) = make_uint2(lo, hi);
   }
-  if (rowsum != nullptr) {
-    sum = wave_sum(sum);
-    if (lane == 0) red_i[wave] = sum;
-  }
-  __syncthreads();
+  if (rowsum != nullptr) sum = block_sum<NT>(sum, slots_sum);
   if (tid == 0) {
     ds[m] = g / 127.0f;
-    if (rowsum != nullptr) {
-      int s = 0;
-      for (int w = 0; w < kThreads / 64; ++w) s += red_i[w];
-      rowsum[m] = s;
-    }
+    if (rowsum != nullptr) rowsum[m] = sum;
   }
+}
+
+template <int NT>
+void launch_nt(const void* x, int bf16, int64_t M, int64_t K, int64_t ldq, int8_t* q, float* ds, int32_t* rowsum,
+               bool vec, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((quant_act_kernel<NT, true>), dim3((unsigned)M), dim3(NT), 0, s, x, bf16, K, ldq, q, ds, rowsum);
+  else
+    hipLaunchKernelGGL((quant_act_kernel<NT, false>), dim3((unsigned)M), dim3(NT), 0, s, x, bf16, K, ldq, q, ds, rowsum);
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldq,
                             int8_t* q, float* ds, int32_t* rowsum, hipStream_t s) {
-  const bool vec = (K % 8 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-  dim3 grid((unsigned)M), block(kThreads);
-  if (x_dtype == BITLINEAR_BF16) {
-    if (vec)
-      hipLaunchKernelGGL((quant_act_kernel<BITLINEAR_BF16, true>), grid, block, 0, s, x, K, ldq, q, ds, rowsum);
-    else
-      hipLaunchKernelGGL((quant_act_kernel<BITLINEAR_BF16, false>), grid, block, 0, s, x, K, ldq, q, ds, rowsum);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((quant_act_kernel<BITLINEAR_F32, true>), grid, block, 0, s, x, K, ldq, q, ds, rowsum);
-    else
-      hipLaunchKernelGGL((quant_act_kernel<BITLINEAR_F32, false>), grid, block, 0, s, x, K, ldq, q, ds, rowsum);
-  }
+  const bool bf16 = x_dtype == BITLINEAR_BF16;
+  const int per16 = bf16 ? 8 : 4;
+  const bool vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  // 1024 threads once the row has more pieces than 256 threads hold
+  if (K / per16 > 256 * kHold)
+    launch_nt<1024>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
+  else
+    launch_nt<256>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
   return hipGetLastError();
 }
 
