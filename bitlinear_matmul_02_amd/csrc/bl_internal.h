@@ -22,6 +22,7 @@ constexpr int64_t kDecodeLdsBytes = BITLINEAR_DECODE_MAX_ACT_BYTES;
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned int u4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- launches
@@ -76,6 +77,13 @@ __device__ inline v4i t2_field(const u4 w, int i) {
 // One 16x16x64 int8 matrix-core step: acc += A(16x64) * B(64x16).
 __device__ inline v4i mfma16(v4i a, v4i b, v4i acc) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+}
+
+// One 32x32x32 int8 matrix-core step: acc += A(32x32) * B(32x32).  Lane l
+// holds row l % 32 of A / column l % 32 of B, bytes j of k = 16 * (l / 32) + j;
+// output element e of lane l is D[8 * (e / 4) + 4 * (l / 32) + e % 4][l % 32].
+__device__ inline v16i mfma32(v4i a, v4i b, v16i acc) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
 }
 
 // Dequantize one accumulator (scaled by 64 by t2_field) and store it.

@@ -3,86 +3,248 @@
 //
 // At many tokens the ternary product is a dense contraction, so the 2-bit
 // tiles are expanded to int8 operands ({-64, 0, 64} = 64*t, see t2_field) and
-// fed to MFMA 16x16x64; each matrix-core step performs the add / subtract /
+// fed to MFMA 32x32x32; each matrix-core step performs the add / subtract /
 // skip sum ("BitNet / Ternary / Binary - Les LLMs 1-bit", TL;DR) of 1024
-// weights for 16 tokens.  The int32 total is shifted right by 6 (exact) and
+// weights for 32 tokens.  The int32 total is shifted right by 6 (exact) and
 // dequantized as y = acc * (ds * beta) in the epilogue.
 //
-// Tiling: a workgroup of 4 waves computes a 128 x 128 block of outputs; each
-// wave a 64 x 64 sub-block (4 x 4 MFMA accumulators).  The k loop walks the
-// 256-column weight tiles; the 16-byte tile slice of each lane is read once
-// per tile and expanded in registers into four B operands (one per 2-bit
-// field), the matching A operands are 16-byte loads from the int8 rows.
+// Why 32x32x32: on gfx950 one wave per SIMD issuing 32x32x32 int8 steps
+// sustains ~4.1 POPS, the 16x16x64 form only ~1.6-2.7 POPS at that occupancy.
+//
+// Operands from the 2-bit tile format (16 rows x 256 columns per 1 KB tile,
+// lane L = 16*g4 + r of a tile holds row r, columns 64*i + 16*g4 + 0..15 of
+// field i): for the 32x32x32 step s (columns 32*s .. 32*s + 31 of the tile),
+// lane (n = l % 32, g = l / 32) needs row n of the two 16-row tiles at
+// columns 32*s + 16*g + 0..15, which is field s/2 of tile lane
+// 16*(2*(s%2) + g) + n%16.  So each lane reads two 16-byte chunks per
+// 256-column step (chunk h = s % 2) and expands field f for steps 2f and 2f+1.
+//
+// Tiling.  A workgroup of 8 waves (2 x 4) computes a BM x BN block of outputs
+// (tokens x weight rows), each wave (BM/2) x (BN/4); two waves per SIMD let
+// one wave's loads, LDS traffic and operand expansion overlap the other's
+// matrix-core work.  Per 256-column k-step the workgroup needs the BM x 256
+// int8 activation slab and the BN/16 weight tiles (BN x 64 bytes):
+//   * both are requested D k-steps ahead into a register ring (activation
+//     slab first: vmcnt retires in order) and written, one k-step ahead of
+//     use and interleaved with the MFMAs, into the free half of
+//     double-buffered LDS slabs; weight tiles are loaded once per workgroup
+//     and shared by the waves in LDS;
+//   * 16-byte piece c of activation row r sits in slot r*16 + (c ^ (r & 15)),
+//     so the 32 rows a matrix-core operand reads fall on different banks;
+//     weight tiles keep their 1 KB lane-major layout (conflict-free reads);
+//   * each MFMA step's next operands (LDS reads, 2-bit expansion) are issued
+//     while the current step's MFMAs run.
+// Workgroups are numbered so that each of the 8 XCDs (blocks are dealt to
+// them round-robin) works on a contiguous run of output tiles, walked in
+// groups of 4 token blocks along N, which share both operands in its L2.
+#include <mutex>
+
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-constexpr int kBM = 128, kBN = 128;
+template <int BM, int BN>
+struct GemmTile {
+  static constexpr int WGM = 2, WGN = 4;              // waves along M x along N
+  static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave block
+  static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA tiles per wave
+  static constexpr int SLAB_A = BM * kTileK;          // activation slab bytes
+  static constexpr int SLAB_B = BN / kTileN * kTileBytes;  // weight slab bytes
+  static constexpr int PA = SLAB_A / 16 / NT;         // 16-byte pieces per thread
+  static constexpr int PB = SLAB_B / 16 / NT;
+  static constexpr int LDS = 2 * (SLAB_A + SLAB_B);   // double-buffered
+};
 
-__global__ __launch_bounds__(256) void gemm_t2_kernel(const int8_t* __restrict__ q, int64_t ldq,
+// Tile index of workgroup b when T tiles are dealt round-robin to 8 XCDs:
+// XCD x receives blocks x, x+8, ...; give it the contiguous tiles
+// [start(x), start(x) + count(x)).
+__device__ inline int xcd_tile(int b, int T) {
+  const int x = b & 7, i = b >> 3;
+  int start = 0;
+  for (int j = 0; j < x; ++j) start += (T - j + 7) >> 3;
+  return start + i;
+}
+
+template <int BM, int BN, int D>
+__global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__ q, int64_t ldq,
                                                       const float* __restrict__ ds, int M,
                                                       const u4* __restrict__ packed,
-                                                      const float* __restrict__ beta, int N,
-                                                      int Nt, int Kt, void* __restrict__ y,
-                                                      int y_dtype) {
-  constexpr int MB = 4, NB = 4;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kBM + wm * 64;
-  const int nb0 = (blockIdx.x * kBN + wn * 64) / kTileN;
-  const int r16 = lane & 15, g4 = lane >> 4;
+                                                      const float* __restrict__ beta, int N, int Nt,
+                                                      int Kt, int tiles_n, void* __restrict__ y, int y_dtype) {
+  using G = GemmTile<BM, BN>;
+  constexpr int MB = G::MB, NB = G::NB;
+  extern __shared__ __attribute__((aligned(16))) int8_t lds[];
+  // LDS: activation halves [0, 2 SLAB_A), then weight halves
+  auto slabA = [&](int buf) { return lds + buf * G::SLAB_A; };
+  auto slabB = [&](int buf) { return lds + 2 * G::SLAB_A + buf * G::SLAB_B; };
 
-  v4i acc[MB][NB];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+  const int wm = wave / G::WGN, wn = wave % G::WGN;
+  // within an XCD's run of tiles, walk groups of GM token blocks along N
+  constexpr int GM = 4;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tiles_m = (int)(gridDim.x / tiles_n);
+  const int group = tile / (GM * tiles_n), within = tile - group * GM * tiles_n;
+  const int gm = min(GM, tiles_m - group * GM);  // token blocks in this group
+  const int tm = group * GM + within % gm, tn = within / gm;
+  const int m0 = tm * BM, nt0 = tn * (BN / kTileN);  // first token, first 16-row weight tile
+  const int r32 = lane & 31, g2 = lane >> 5;
+
+  v16i acc[MB][NB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NB; ++j) acc[mb][j] = v4i{0, 0, 0, 0};
-
-  const int8_t* arow[MB];
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int row = min(m0 + mb * 16 + r16, M - 1);  // rows past M are masked at the store
-    arow[mb] = q + (int64_t)row * ldq + 16 * g4;
+      for (int e = 0; e < 16; ++e) acc[mb][j][e] = 0;
+
+  // activation pieces this thread moves: slot s = p*NT + tid holds piece
+  // (s & 15) ^ (row & 15) of slab row s >> 4; rows past M read row M-1
+  const int8_t* asrc[G::PA];
+#pragma unroll
+  for (int p = 0; p < G::PA; ++p) {
+    const int s = p * G::NT + tid, row = s >> 4;
+    asrc[p] = q + (int64_t)min(m0 + row, M - 1) * ldq + (((s & 15) ^ (row & 15)) * 16);
   }
-  const u4* bptr[NB];
+  // weight pieces this thread moves: piece c = p*NT + tid is 16-byte piece
+  // c % 64 of local tile c / 64; tiles past Nt read the last tile
+  const u4* bsrc[G::PB];
 #pragma unroll
-  for (int j = 0; j < NB; ++j) bptr[j] = packed + (int64_t)min(nb0 + j, Nt - 1) * Kt * 64 + lane;
+  for (int p = 0; p < G::PB; ++p) {
+    const int c = p * G::NT + tid;
+    bsrc[p] = packed + (int64_t)min(nt0 + (c >> 6), Nt - 1) * Kt * 64 + (c & 63);
+  }
+  // this lane's weight chunks in the LDS slab: block j, chunk h
+  int boff[NB][2];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int lt = (wn * G::WN + 32 * j + r32) >> 4;  // local 16-row tile
+      boff[j][h] = lt * kTileBytes + (16 * (2 * h + g2) + (r32 & 15)) * 16;
+    }
+  // LDS rows of this lane's activation operands; the swizzle term only
+  // depends on r32 because every block starts on a multiple of 16 rows
+  const int arow0 = wm * G::WM + r32;
 
-  for (int kt = 0; kt < Kt; ++kt) {
-    u4 w[NB];
+  u4 aring[D][G::PA];
+  u4 bring[D][G::PB];
+  auto load = [&](int u, int kt) {
 #pragma unroll
-    for (int j = 0; j < NB; ++j) w[j] = bptr[j][(int64_t)kt * 64];
+    for (int p = 0; p < G::PA; ++p) aring[u][p] = *reinterpret_cast<const u4*>(asrc[p] + (int64_t)kt * kTileK);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v4i a[MB];
+    for (int p = 0; p < G::PB; ++p) bring[u][p] = bsrc[p][(int64_t)kt * 64];
+  };
+  auto stage_piece = [&](int u, int buf, int i) {  // i in [0, PA + PB)
+    if (i < G::PA)
+      *reinterpret_cast<u4*>(slabA(buf) + (i * G::NT + tid) * 16) = aring[u][i];
+    else
+      *reinterpret_cast<u4*>(slabB(buf) + ((i - G::PA) * G::NT + tid) * 16) = bring[u][i - G::PA];
+  };
+  auto read_a = [&](v4i (&a)[MB], int buf, int s_) {
+    const int c = 2 * s_ + g2;  // 16-byte piece: columns 32s + 16g
+    const int off = (arow0 * 16 + (c ^ (r32 & 15))) * 16;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        a[mb] = *reinterpret_cast<const v4i*>(arow[mb] + (int64_t)kt * kTileK + 64 * i);
+    for (int mb = 0; mb < MB; ++mb) a[mb] = *reinterpret_cast<const v4i*>(slabA(buf) + off + mb * 32 * kTileK);
+  };
+
+  // One k-step: 8 MFMA steps s = 2f + h, software-pipelined; the next
+  // k-step's pieces are written to the other LDS half along the way.
+  auto compute = [&](int buf, bool stage_next, int unext) {
+    u4 wch[NB][2];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const v4i b = t2_field(w[j], i);
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma16(a[mb], b, acc[mb][j]);
+      for (int h = 0; h < 2; ++h) wch[j][h] = *reinterpret_cast<const u4*>(slabB(buf) + boff[j][h]);
+    v4i a[2][MB];
+    v4i b[2][NB];
+    read_a(a[0], buf, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[0][j] = t2_field(wch[j][0], 0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const int cur = st & 1, nx = cur ^ 1;
+      if (st + 1 < 8) {
+        read_a(a[nx], buf, st + 1);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) b[nx][j] = t2_field(wch[j][(st + 1) & 1], (st + 1) >> 1);
       }
+      if (stage_next) {
+#pragma unroll
+        for (int i = st * (G::PA + G::PB) / 8; i < (st + 1) * (G::PA + G::PB) / 8; ++i) stage_piece(unext, buf ^ 1, i);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma32(a[cur][mb], b[cur][j], acc[mb][j]);
+    }
+  };
+
+  // prologue: k-steps 0 .. D-1 requested (indices past the end re-read the
+  // last k-step, in bounds, never used); k-step 0 into LDS half 0
+#pragma unroll
+  for (int u = 0; u < D; ++u) load(u, min(u, Kt - 1));
+#pragma unroll
+  for (int i = 0; i < G::PA + G::PB; ++i) stage_piece(0, 0, i);
+  __syncthreads();
+
+  // full rounds of the ring, free of branches so the waits stay partial
+  int k0 = 0;
+  for (; k0 + D < Kt; k0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int kt = k0 + u;
+      load(u, min(kt + D, Kt - 1));  // slot u (k-step kt) went to LDS during the previous k-step
+      compute(kt & 1, true, (u + 1) % D);
+      __syncthreads();
+    }
+  }
+  // the last 1..D k-steps (already requested)
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    const int kt = k0 + u;
+    if (kt < Kt) {  // uniform
+      compute(kt & 1, kt + 1 < Kt, (u + 1) % D);
+      __syncthreads();
     }
   }
 
   const float bt = *beta;
+  const int n_wave = nt0 * kTileN + wn * G::WN;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + mb * 16 + 4 * g4 + r;
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + wm * G::WM + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
       if (m >= M) continue;
       const float scale = ds[m] * bt;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int n = (nb0 + j) * kTileN + r16;
-        if (n < N) store_out(y, y_dtype, (int64_t)m * N + n, acc[mb][j][r], scale);
+        const int n = n_wave + 32 * j + r32;
+        if (n < N) store_out(y, y_dtype, (int64_t)m * N + n, acc[mb][j][e], scale);
       }
     }
+}
+
+template <int BM, int BN, int D>
+hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, const uint8_t* packed,
+                       const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+  using G = GemmTile<BM, BN>;
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+  });
+  if (attr != hipSuccess) return attr;
+  const int Nt = (int)ceil_div(N, kTileN), Kt = (int)ceil_div(K, kTileK);
+  const int tiles_n = (int)ceil_div(N, BN), tiles_m = (int)ceil_div(M, BM);
+  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D>), dim3((unsigned)(tiles_m * tiles_n)), dim3(G::NT), G::LDS, s, q,
+                     ldq, ds, (int)M, reinterpret_cast<const u4*>(packed), beta, (int)N, Nt, Kt, tiles_n, y, y_dtype);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -92,11 +254,11 @@ int64_t gemm_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 hipError_t launch_gemm_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void*, hipStream_t s) {
-  const int Nt = (int)ceil_div(N, kTileN), Kt = (int)ceil_div(K, kTileK);
-  dim3 grid((unsigned)ceil_div(N, kBN), (unsigned)ceil_div(M, kBM));
-  hipLaunchKernelGGL(gemm_t2_kernel, grid, dim3(256), 0, s, q, ldq, ds, (int)M,
-                     reinterpret_cast<const u4*>(packed), beta, (int)N, Nt, Kt, y, y_dtype);
-  return hipGetLastError();
+  // 128 x 256 blocks when that still gives a few hundred workgroups,
+  // 128 x 128 otherwise
+  const int64_t big = ceil_div(M, 128) * ceil_div(N, 256);
+  if (big >= 384) return launch_tile<128, 256, 2>(q, ldq, ds, M, K, packed, beta, N, y, y_dtype, s);
+  return launch_tile<128, 128, 2>(q, ldq, ds, M, K, packed, beta, N, y, y_dtype, s);
 }
 
 }  // namespace bl
