@@ -64,6 +64,10 @@ def _load():
     lib.oracle_pack_t2.argtypes = [p, i64, i64, p]
     lib.oracle_unpack_t2.restype = i64
     lib.oracle_unpack_t2.argtypes = [p, i64, i64, p]
+    lib.oracle_relu2_mul.restype = None
+    lib.oracle_relu2_mul.argtypes = [p, p, i64, p]
+    lib.oracle_add_f32.restype = None
+    lib.oracle_add_f32.argtypes = [p, p, i64]
     _lib = lib
     return lib
 
@@ -178,6 +182,26 @@ def unpack_t2(packed: np.ndarray, N: int, K: int):
     t = np.empty((N, K), dtype=np.int8)
     bad = _load().oracle_unpack_t2(_ptr(packed), N, K, _ptr(t))
     return t, int(bad)
+
+
+# ------------------------------------------------------------ decoder glue
+def relu2_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """h = ReLU(g)^2 * u elementwise, fp32 (r = g if g > 0 else 0; (r*r)*u)."""
+    g = _c(g, np.float32)
+    u = _c(u, np.float32)
+    assert g.shape == u.shape
+    h = np.empty_like(g)
+    _load().oracle_relu2_mul(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def add_f32(x: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """Residual sum x + r, fp32 (returns a new array)."""
+    out = _c(x, np.float32).copy()
+    r = _c(r, np.float32)
+    assert out.shape == r.shape
+    _load().oracle_add_f32(_ptr(out), _ptr(r), out.size)
+    return out
 
 
 # ------------------------------------------------------------ whole forward

@@ -29,6 +29,10 @@
  *      wording (sum of activations with weight +1 minus those with weight -1).
  *  - oracle_dequant_f32, oracle_f32_to_bf16: rescaling by the two quantizer
  *      scales; implied by the quantizer pair above, not printed on the pages.
+ *  - oracle_relu2_mul, oracle_add_f32: the decoder glue around the
+ *      BitLinears of one layer ("Key Technologies Enabling the BitNET
+ *      Family", Architectural Innovations and Optimizations: squared ReLU in
+ *      the feed-forward layers); the residual sums of a decoder layer.
  *  - oracle_pack_t2 / oracle_unpack_t2: 2 bits per ternary weight
  *      ("BitNet Technical Notes", Appendix glossary: bit-packing at 2 bits per
  *      ternary weight; "BitNet: Inference framework for 1-bit LLMs", post #139:
@@ -43,6 +47,9 @@
  *  - activations: gamma = max |x|; g = max(gamma, 1e-5); q = clamp(rint(x *
  *    (127 / g)), -127, 127); ds = g / 127.
  *  - dequant: y = (float)acc * (ds * beta).
+ *  - feed-forward glue: h = (r * r) * u with r = g if g > 0 else 0, fp32 in
+ *    this order; the gate / up / down form is the plainest reading of an FFN
+ *    with ReLU^2 between its projections.
  *
  * Parity status: every function here is pinned by the CPU test suite
  * (hand-worked example, brute force, closed forms, invariants, the pages'
@@ -283,4 +290,24 @@ void oracle_bitlinear_forward(const uint16_t *xb, int64_t M, int64_t K, const fl
     oracle_quant_act_bf16(xb, M, K, q, ds, rowsum);
     oracle_matmul_i32(q, t, M, N, K, acc, threads);
     oracle_dequant_f32(acc, ds, *beta, M, N, y);
+}
+
+/* ------------------------------------------------------- decoder glue */
+
+/* h = ReLU(g)^2 * u elementwise: r = g if g > 0 else +0, then (r * r) * u,
+ * two fp32 roundings in this order. */
+void oracle_relu2_mul(const float *g, const float *u, int64_t count, float *h)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        float r = g[i] > 0.0f ? g[i] : 0.0f;
+        float r2 = r * r;
+        h[i] = r2 * u[i];
+    }
+}
+
+/* Residual sum x += r, one fp32 rounding per element. */
+void oracle_add_f32(float *x, const float *r, int64_t count)
+{
+    for (int64_t i = 0; i < count; ++i)
+        x[i] = x[i] + r[i];
 }

@@ -434,3 +434,42 @@ def test_forward_single_4x512():
     assert np.all(err <= bound * (1 + 1e-6) + 1e-6)
     np.testing.assert_array_equal(out["y_bf16"],
                                   torch.from_numpy(out["y"]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# ------------------------------------------------------------- decoder glue
+def test_relu2_mul_special_values():
+    # exact small integers and dyadic values: every product is representable
+    g = np.array([-3.0, -0.0, 0.0, 0.5, 1.0, 2.0, 3.0, -1e30, 1e-20], dtype=np.float32)
+    u = np.array([5.0, 7.0, -2.0, 4.0, -1.0, 3.0, -2.5, 9.0, 1.0], dtype=np.float32)
+    h = oracle.relu2_mul(g, u)
+    tiny = np.float32(1e-20) * np.float32(1e-20)  # underflows to a subnormal, one rounding
+    np.testing.assert_array_equal(h, np.array([0, 0, 0, 1.0, -1.0, 12.0, -22.5, 0, tiny], dtype=np.float32))
+    # the ReLU side never lets a negative gate through, whatever u is
+    assert not np.any(h[g <= 0])
+
+
+def test_relu2_mul_reduces_to_library_square():
+    rng = np.random.default_rng(11)
+    g = rng.standard_normal(4096).astype(np.float32) * 3
+    # u = 1: h is the library's single-rounding square of max(g, 0)
+    h = oracle.relu2_mul(g, np.ones_like(g))
+    np.testing.assert_array_equal(h, np.square(np.maximum(g, np.float32(0))))
+    # scaling u by a power of two scales h exactly; a sign flip of u flips h
+    u = rng.standard_normal(4096).astype(np.float32)
+    base = oracle.relu2_mul(g, u)
+    np.testing.assert_array_equal(oracle.relu2_mul(g, u * np.float32(8)), base * np.float32(8))
+    np.testing.assert_array_equal(oracle.relu2_mul(g, -u), -base)
+    # within one rounding of the fp64 value (two fp32 roundings: <= 2^-23 relative)
+    ref = np.square(np.maximum(g, 0).astype(np.float64)) * u.astype(np.float64)
+    assert np.all(np.abs(base - ref) <= np.abs(ref) * 2.0 ** -22.9 + 1e-45)
+
+
+def test_add_f32_matches_library_add():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal(5000).astype(np.float32)
+    r = rng.standard_normal(5000).astype(np.float32) * 1e3
+    np.testing.assert_array_equal(oracle.add_f32(x, r), np.add(x, r))
+    # exact on integers; the input is left untouched
+    xi = np.arange(-50, 50, dtype=np.float32)
+    np.testing.assert_array_equal(oracle.add_f32(xi, xi), 2 * xi)
+    assert xi[0] == -50
