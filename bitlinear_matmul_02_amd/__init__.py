@@ -11,6 +11,9 @@ Functions carry the C names:
     bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
     bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
     bitlinear_forward_decode(x, packed, w_beta, N, y)
+    bitlinear_relu2_mul(g, u, h)
+An fp32 output tensor can be passed with ``accumulate=True`` to the product
+calls, which then add their result into it (``BITLINEAR_F32_ADD``).
 plus allocation helpers (``act_stride``, ``packed_bytes`` ...) and two
 conveniences that allocate outputs (``quant_act``, ``pack_weights``,
 ``linear``).
@@ -26,14 +29,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libbitlinear.so")
 
 OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
-F32, BF16, I32 = 0, 1, 2
+F32, BF16, I32, F32_ADD = 0, 1, 2, 3
 MAX_K, MAX_N, MAX_M, GEMV_MAX_M = 131072, 1 << 20, 1 << 20, 64
 
 EXPORTS = (
     "bitlinear_version", "bitlinear_last_error", "bitlinear_act_stride", "bitlinear_packed_bytes",
     "bitlinear_pack_workspace_bytes", "bitlinear_gemv_workspace_bytes",
     "bitlinear_gemm_workspace_bytes", "bitlinear_quant_act", "bitlinear_pack_weights",
-    "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode",
+    "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode", "bitlinear_relu2_mul",
 )
 DECODE_MAX_ACT_BYTES = 58368
 
@@ -81,6 +84,8 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).argtypes = [p, p, i64, i64, p, p, i64, p, i32, p, sz, p]
     L.bitlinear_forward_decode.restype = i32
     L.bitlinear_forward_decode.argtypes = [p, i32, i64, i64, p, p, i64, p, i32, p]
+    L.bitlinear_relu2_mul.restype = i32
+    L.bitlinear_relu2_mul.argtypes = [p, p, i64, p, p]
     _lib = L
     return L
 
@@ -140,29 +145,47 @@ def bitlinear_pack_weights(w, packed, w_beta, workspace, stream=None) -> None:
                                         _stream(stream)))
 
 
-def _product(fn, x_q, x_ds, M, K, packed, w_beta, N, y, workspace, stream):
+def _ydtype(y, accumulate: bool) -> int:
+    if accumulate:
+        if y.dtype != torch.float32:
+            raise BitLinearError(ERR_ARG, "accumulate needs an fp32 output")
+        return F32_ADD
+    return _DTYPE[y.dtype]
+
+
+def _product(fn, x_q, x_ds, M, K, packed, w_beta, N, y, workspace, stream, accumulate):
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(fn(_ptr(x_q), _ptr(x_ds), M, K, _ptr(packed), _ptr(w_beta), N, _ptr(y), _DTYPE[y.dtype],
+    _check(fn(_ptr(x_q), _ptr(x_ds), M, K, _ptr(packed), _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate),
               _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None) -> None:
-    """y [M][N] = dequant(x_q . T^T) for M <= 64 tokens (y dtype fp32, bf16 or int32)."""
+def bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None,
+                   accumulate: bool = False) -> None:
+    """y [M][N] = dequant(x_q . T^T) for M <= 64 tokens (y dtype fp32, bf16 or int32;
+    with ``accumulate`` y += the fp32 result)."""
     _product(lib().bitlinear_gemv, x_q, x_ds, x_ds.shape[0], K, packed, w_beta, N, y, workspace,
-             stream)
+             stream, accumulate)
 
 
-def bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None) -> None:
+def bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None,
+                   accumulate: bool = False) -> None:
     """The same product for any number of tokens, on the int8 matrix cores."""
     _product(lib().bitlinear_gemm, x_q, x_ds, x_ds.shape[0], K, packed, w_beta, N, y, workspace,
-             stream)
+             stream, accumulate)
 
 
-def bitlinear_forward_decode(x, packed, w_beta, N, y, stream=None) -> None:
+def bitlinear_forward_decode(x, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
     """y [M][N] = BitLinear(x) for M <= 64 tokens in one launch (quantization fused)."""
     M, K = x.shape
     _check(lib().bitlinear_forward_decode(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(packed), _ptr(w_beta), N,
-                                          _ptr(y), _DTYPE[y.dtype], _stream(stream)))
+                                          _ptr(y), _ydtype(y, accumulate), _stream(stream)))
+
+
+def bitlinear_relu2_mul(g, u, h, stream=None) -> None:
+    """h = ReLU(g)^2 * u elementwise (fp32 tensors of one shape)."""
+    if not (g.dtype == u.dtype == h.dtype == torch.float32) or not (g.shape == u.shape == h.shape):
+        raise BitLinearError(ERR_ARG, "relu2_mul needs fp32 tensors of one shape")
+    _check(lib().bitlinear_relu2_mul(_ptr(g), _ptr(u), g.numel(), _ptr(h), _stream(stream)))
 
 
 def decode_fits(M: int, K: int) -> bool:

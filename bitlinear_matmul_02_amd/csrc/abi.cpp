@@ -41,7 +41,8 @@ int check_common(const char* fn, int64_t M, int64_t max_m, int64_t K, const void
   if (M < 0 || M > max_m) return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld outside [0, %lld]", fn, (long long)M, (long long)max_m);
   if (!k_ok(K)) return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld outside [1, %d]", fn, (long long)K, BITLINEAR_MAX_K);
   if (!n_ok(N)) return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld outside [1, %d]", fn, (long long)N, BITLINEAR_MAX_N);
-  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32)
+  if (y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_BF16 && y_dtype != BITLINEAR_I32 &&
+      y_dtype != BITLINEAR_F32_ADD)
     return fail(BITLINEAR_ERR_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
   if (M == 0) return BITLINEAR_OK;
   if (!packed || !w_beta || !y) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
@@ -73,7 +74,7 @@ int check_product(const char* fn, const int8_t* x_q, const float* x_ds, int64_t 
 
 extern "C" {
 
-int bitlinear_version(void) { return (1 << 16) | 0; }
+int bitlinear_version(void) { return (1 << 16) | 1; }
 
 const char* bitlinear_last_error(void) { return g_err; }
 
@@ -171,6 +172,15 @@ int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, c
   return hip_status(bl::launch_decode_t2(x, x_dtype, M, K, static_cast<const uint8_t*>(packed), w_beta, N, y,
                                          y_dtype, static_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int bitlinear_relu2_mul(const float* g, const float* u, int64_t count, float* h, void* stream) {
+  const char* fn = "bitlinear_relu2_mul";
+  if (count < 0) return fail(BITLINEAR_ERR_SHAPE, "%s: count %lld < 0", fn, (long long)count);
+  if (count == 0) return ok();
+  if (!g || !u || !h) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(g, 4) || !aligned(u, 4) || !aligned(h, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: pointers must be 4-byte aligned", fn);
+  return hip_status(bl::launch_relu2_mul(g, u, count, h, static_cast<hipStream_t>(stream)), fn);
 }
 
 }  // extern "C"

@@ -50,6 +50,8 @@ hipError_t launch_gemm_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s);
 
+hipError_t launch_relu2_mul(const float* g, const float* u, int64_t count, float* h, hipStream_t s);
+
 // ------------------------------------------------------- device helpers
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
@@ -95,6 +97,8 @@ __device__ inline void store_out(void* y, int y_dtype, int64_t idx, int acc64, f
     const float v = (float)acc * scale;
     if (y_dtype == BITLINEAR_F32)
       static_cast<float*>(y)[idx] = v;
+    else if (y_dtype == BITLINEAR_F32_ADD)
+      static_cast<float*>(y)[idx] = __fadd_rn(static_cast<const float*>(y)[idx], v);
     else
       static_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
   }

@@ -1,0 +1,96 @@
+"""Decode step over a stack of BitLinear decoder layers.
+
+Each layer holds seven BitLinears (q, k, v, o, gate, up, down) and the glue
+between them: the squared-ReLU gated feed-forward activation ("Key
+Technologies Enabling the BitNET Family", Architectural Innovations and
+Optimizations) and two residual sums.  Attention itself is not part of this
+path: the o projection takes the q projection's output in its place, and k / v
+are computed and kept (as a KV cache would receive them).  RMSNorm is not
+modelled.  Per layer, with x the fp32 residual stream [M][d]:
+
+    q, k, v = BL_q(x), BL_k(x), BL_v(x)
+    x = x + BL_o(q)
+    h = ReLU(BL_gate(x))^2 * BL_up(x)
+    x = x + BL_down(h)
+
+Everything is enqueued on one stream by the library's kernels and allocates
+nothing after construction, so a step can be captured in a HIP graph.  For at
+most ``FUSED_MAX_M`` tokens each BitLinear is one fused launch (quantization
+in the product's prologue); beyond that the input is quantized once and
+shared by the BitLinears that read it.  The residual sums are fused into the
+o / down products' epilogues (``accumulate``).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (GEMV_MAX_M, act_stride, bitlinear_forward_decode, bitlinear_gemm, bitlinear_gemv,
+               bitlinear_quant_act, bitlinear_relu2_mul, decode_fits, gemm_workspace_bytes,
+               gemv_workspace_bytes)
+
+NAMES = ("q", "k", "v", "o", "gate", "up", "down")
+FUSED_MAX_M = 4
+
+
+class PackedLinear:
+    """One packed BitLinear: 2-bit tiles and the fp32 weight scale on the device."""
+
+    def __init__(self, packed: torch.Tensor, beta: torch.Tensor, N: int, K: int):
+        self.packed, self.beta, self.N, self.K = packed, beta, N, K
+
+
+class DecoderStack:
+    def __init__(self, layers: list[dict], M: int, device):
+        """layers: one dict per layer mapping each of NAMES to a PackedLinear."""
+        self.layers = layers
+        self.M = M
+        dev = torch.device(device)
+        first = layers[0]
+        d, qn, kn, vn = first["q"].K, first["q"].N, first["k"].N, first["v"].N
+        f = first["gate"].N
+        for L in layers:
+            assert set(L) == set(NAMES)
+            assert (L["o"].K, L["o"].N, L["gate"].K, L["up"].K, L["up"].N, L["down"].K, L["down"].N) == \
+                (qn, d, d, d, f, f, d)
+        self.d, self.f = d, f
+        z = lambda n: torch.zeros((M, n), dtype=torch.float32, device=dev)
+        self.q, self.k, self.v, self.g, self.u, self.h = z(qn), z(kn), z(vn), z(f), z(f), z(f)
+        self.fused = M <= FUSED_MAX_M and all(decode_fits(M, K) for K in (d, qn, f))
+        self.gemv = M <= GEMV_MAX_M
+        if not self.fused:
+            self.xq = {K: torch.zeros((M, act_stride(K)), dtype=torch.int8, device=dev) for K in {d, qn, f}}
+            self.xds = {K: torch.zeros((M,), dtype=torch.float32, device=dev) for K in {d, qn, f}}
+            wsf = gemv_workspace_bytes if self.gemv else gemm_workspace_bytes
+            ws = max(wsf(M, L[n].N, L[n].K) for L in layers for n in NAMES)
+            self.ws = torch.zeros((max(ws, 1),), dtype=torch.uint8, device=dev)
+
+    # one BitLinear on an input already quantized into self.xq / self.xds
+    def _product(self, lin: PackedLinear, y, accumulate, stream):
+        fn = bitlinear_gemv if self.gemv else bitlinear_gemm
+        fn(self.xq[lin.K], self.xds[lin.K], lin.K, lin.packed, lin.beta, lin.N, y, self.ws, stream,
+           accumulate=accumulate)
+
+    def _linears(self, x, lins, outs, accumulate, stream):
+        """outs[i] (+)= BL_i(x) for BitLinears that share the input x."""
+        if self.fused:
+            for lin, y in zip(lins, outs):
+                bitlinear_forward_decode(x, lin.packed, lin.beta, lin.N, y, stream, accumulate=accumulate)
+            return
+        K = lins[0].K
+        bitlinear_quant_act(x, self.xq[K], self.xds[K], None, stream)
+        for lin, y in zip(lins, outs):
+            self._product(lin, y, accumulate, stream)
+
+    def layer(self, i: int, x: torch.Tensor, stream=None) -> None:
+        L = self.layers[i]
+        self._linears(x, (L["q"], L["k"], L["v"]), (self.q, self.k, self.v), False, stream)
+        self._linears(self.q, (L["o"],), (x,), True, stream)
+        self._linears(x, (L["gate"], L["up"]), (self.g, self.u), False, stream)
+        bitlinear_relu2_mul(self.g, self.u, self.h, stream)
+        self._linears(self.h, (L["down"],), (x,), True, stream)
+
+    def step(self, x: torch.Tensor, stream=None) -> None:
+        """One decode step: x [M][d] fp32 (the residual stream) is updated in place."""
+        assert x.dtype == torch.float32 and tuple(x.shape) == (self.M, self.d) and x.is_contiguous()
+        for i in range(len(self.layers)):
+            self.layer(i, x, stream)

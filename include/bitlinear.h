@@ -55,6 +55,7 @@ extern "C" {
 #define BITLINEAR_F32 0  /* IEEE fp32 */
 #define BITLINEAR_BF16 1 /* bfloat16, round-to-nearest-even when written */
 #define BITLINEAR_I32 2  /* raw int32 accumulators (output only) */
+#define BITLINEAR_F32_ADD 3 /* fp32, added to what y holds: y += value (output only) */
 
 /* Supported sizes. */
 #define BITLINEAR_MAX_K 131072       /* keeps 64 * 127 * K below 2^31 */
@@ -135,7 +136,10 @@ int bitlinear_pack_weights(const float *w, int64_t N, int64_t K, void *packed, f
  *   packed, w_beta  output of bitlinear_pack_weights for N x K weights.
  *   y          [M][N] out, y_dtype BITLINEAR_F32 (y = acc * (ds * beta) in
  *              fp32), BITLINEAR_BF16 (the same value rounded to nearest even)
- *              or BITLINEAR_I32 (the raw accumulator acc = sum_k q * t).
+ *              or BITLINEAR_I32 (the raw accumulator acc = sum_k q * t),
+ *              or BITLINEAR_F32_ADD (y = y + acc * (ds * beta), two fp32
+ *              roundings: the residual sum of a decoder layer fused into
+ *              the product; y must not overlap x_q or x_ds).
  *              Needs element alignment only.
  *   workspace  bitlinear_gemv_workspace_bytes(M, N, K) bytes (NULL if 0).
  * M must be in [0, BITLINEAR_GEMV_MAX_M].
@@ -173,6 +177,19 @@ int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
  */
 int bitlinear_forward_decode(const void *x, int x_dtype, int64_t M, int64_t K, const void *packed,
                              const float *w_beta, int64_t N, void *y, int y_dtype, void *stream);
+
+/*
+ * Feed-forward activation between the gate / up and down BitLinears of a
+ * decoder layer ("Key Technologies Enabling the BitNET Family", Architectural
+ * Innovations and Optimizations: squared ReLU in the feed-forward layers):
+ *   h[i] = (r * r) * u[i],  r = g[i] if g[i] > 0 else +0,
+ * fp32, two roundings in this order.
+ *   g, u     [count] fp32 device inputs (gate and up projections).
+ *   h        [count] fp32 device output; may be g or u (elementwise).
+ * All pointers 4-byte aligned; count == 0 enqueues nothing.
+ * Errors: ERR_ARG (null pointer), ERR_SHAPE (count < 0), ERR_ALIGN.
+ */
+int bitlinear_relu2_mul(const float *g, const float *u, int64_t count, float *h, void *stream);
 
 #ifdef __cplusplus
 }

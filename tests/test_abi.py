@@ -38,6 +38,7 @@ def test_header_constants_match_binding():
     assert int(consts["BITLINEAR_F32"]) == bl.F32
     assert int(consts["BITLINEAR_BF16"]) == bl.BF16
     assert int(consts["BITLINEAR_I32"]) == bl.I32
+    assert int(consts["BITLINEAR_F32_ADD"]) == bl.F32_ADD
     assert int(consts["BITLINEAR_MAX_K"]) == bl.MAX_K
     assert int(consts["BITLINEAR_GEMV_MAX_M"]) == bl.GEMV_MAX_M
     assert int(consts["BITLINEAR_DECODE_MAX_ACT_BYTES"]) == bl.DECODE_MAX_ACT_BYTES
@@ -159,3 +160,21 @@ def test_forward_decode_validation():
     assert call(M=0) == bl.OK
     assert bl.decode_fits(1, 28672) and bl.decode_fits(2, 28672) and bl.decode_fits(8, 6912)
     assert not bl.decode_fits(8, 8192)
+
+
+def test_relu2_mul_validation():
+    fn = bl.lib().bitlinear_relu2_mul
+    assert fn(None, FAKE, 16, FAKE, None) == bl.ERR_ARG
+    assert "null" in bl.last_error()
+    assert fn(FAKE, FAKE, -1, FAKE, None) == bl.ERR_SHAPE
+    assert fn(FAKE + 2, FAKE, 16, FAKE, None) == bl.ERR_ALIGN
+    assert fn(FAKE, FAKE, 16, FAKE + 1, None) == bl.ERR_ALIGN
+    assert fn(None, None, 0, None, None) == bl.OK  # empty: nothing enqueued
+
+
+def test_accumulate_dtype_accepted_by_validation():
+    # F32_ADD passes the dtype check (the call then fails on the null workspace-free shape check)
+    fn = bl.lib().bitlinear_gemv
+    assert call_product(fn, ydt=bl.F32_ADD, y=FAKE + 2) == bl.ERR_ALIGN
+    assert call_product(fn, ydt=4) == bl.ERR_ARG
+    assert "y_dtype" in bl.last_error()

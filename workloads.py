@@ -82,6 +82,18 @@ LAYER_SHAPES = (
     ("down", D_FFN, D_MODEL),
 )
 
+# One decode step over every BitLinear of the 30-layer stack, batch 1 and 8.
+DECODE_STEP_BATCHES = (1, 8)
+
+
+def decoder_weight_seed(layer: int, j: int) -> int:
+    """Seed of the j-th matrix (LAYER_SHAPES order) of decoder layer ``layer``."""
+    return 100 + 7 * layer + j
+
+
+DECODER_X0_SEED = 1  # seed of the bf16 input tokens of the decode step
+
+
 # Prefill GEMM: 2048 tokens on the 2B-class FFN shapes.
 PREFILL_2B = Workload("prefill_gemm_2b_m2048", (Linear(2048, 2560, 6912), Linear(2048, 6912, 2560)))
 
