@@ -68,6 +68,8 @@ def _load():
     lib.oracle_relu2_mul.argtypes = [p, p, i64, p]
     lib.oracle_add_f32.restype = None
     lib.oracle_add_f32.argtypes = [p, p, i64]
+    lib.oracle_rmsnorm_f32.restype = None
+    lib.oracle_rmsnorm_f32.argtypes = [p, i64, i64, p]
     _lib = lib
     return lib
 
@@ -185,6 +187,18 @@ def unpack_t2(packed: np.ndarray, N: int, K: int):
 
 
 # ------------------------------------------------------------ decoder glue
+EPS_NORM = np.float32(1e-5)
+
+
+def rmsnorm(x: np.ndarray) -> np.ndarray:
+    """Row-wise RMS normalization (gain 1) of fp32 x [M][K]."""
+    x = _c(x, np.float32)
+    M, K = x.shape
+    out = np.empty_like(x)
+    _load().oracle_rmsnorm_f32(_ptr(x), M, K, _ptr(out))
+    return out
+
+
 def relu2_mul(g: np.ndarray, u: np.ndarray) -> np.ndarray:
     """h = ReLU(g)^2 * u elementwise, fp32 (r = g if g > 0 else 0; (r*r)*u)."""
     g = _c(g, np.float32)

@@ -29,6 +29,9 @@
  *      wording (sum of activations with weight +1 minus those with weight -1).
  *  - oracle_dequant_f32, oracle_f32_to_bf16: rescaling by the two quantizer
  *      scales; implied by the quantizer pair above, not printed on the pages.
+ *  - oracle_rmsnorm_f32: RMS normalization of each token row before it is
+ *      quantized (same page and section as the squared ReLU below: RMSNorm
+ *      is the normalization, without bias terms).
  *  - oracle_relu2_mul, oracle_add_f32: the decoder glue around the
  *      BitLinears of one layer ("Key Technologies Enabling the BitNET
  *      Family", Architectural Innovations and Optimizations: squared ReLU in
@@ -47,6 +50,9 @@
  *  - activations: gamma = max |x|; g = max(gamma, 1e-5); q = clamp(rint(x *
  *    (127 / g)), -127, 127); ds = g / 127.
  *  - dequant: y = (float)acc * (ds * beta).
+ *  - RMS normalization (gain 1, no bias; placement and epsilon not given on
+ *    the pages): S = sum_k x_k^2 in fp64 (each square exact), ms = (float)(S /
+ *    K), r = 1 / sqrt(ms + 1e-5) in fp32, xn_k = x_k * r.
  *  - feed-forward glue: h = (r * r) * u with r = g if g > 0 else 0, fp32 in
  *    this order; the gate / up / down form is the plainest reading of an FFN
  *    with ReLU^2 between its projections.
@@ -63,6 +69,7 @@
 #define ORACLE_BETA_CHUNK 4096
 #define ORACLE_EPS_W 1e-8f
 #define ORACLE_EPS_X 1e-5f
+#define ORACLE_EPS_NORM 1e-5f
 
 /* ---------------------------------------------------------------- weights */
 
@@ -310,4 +317,21 @@ void oracle_add_f32(float *x, const float *r, int64_t count)
 {
     for (int64_t i = 0; i < count; ++i)
         x[i] = x[i] + r[i];
+}
+
+/* RMS normalization of each row of x[M][K] (gain 1): xn = x * r with
+ * r = 1 / sqrt(mean(x^2) + eps); the mean of squares is summed in fp64 in
+ * index order and rounded once to fp32. */
+void oracle_rmsnorm_f32(const float *x, int64_t M, int64_t K, float *xn)
+{
+    for (int64_t m = 0; m < M; ++m) {
+        const float *row = x + m * K;
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += (double)row[k] * (double)row[k];
+        float ms = (float)(s / (double)K);
+        float r = 1.0f / sqrtf(ms + ORACLE_EPS_NORM);
+        for (int64_t k = 0; k < K; ++k)
+            xn[m * K + k] = row[k] * r;
+    }
 }

@@ -473,3 +473,43 @@ def test_add_f32_matches_library_add():
     xi = np.arange(-50, 50, dtype=np.float32)
     np.testing.assert_array_equal(oracle.add_f32(xi, xi), 2 * xi)
     assert xi[0] == -50
+
+
+# ------------------------------------------------------------- RMS normalization
+def test_rmsnorm_constant_and_zero_rows():
+    x = np.zeros((3, 64), dtype=np.float32)
+    x[0] = 2.0          # mean square 4: r = 1 / sqrt(4 + 1e-5)
+    x[1, ::2] = -0.5    # mean square 0.125
+    out = oracle.rmsnorm(x)
+    r0 = np.float32(1) / np.sqrt(np.float32(4) + oracle.EPS_NORM)
+    np.testing.assert_array_equal(out[0], np.full(64, np.float32(2) * r0, dtype=np.float32))
+    r1 = np.float32(1) / np.sqrt(np.float32(0.125) + oracle.EPS_NORM)
+    np.testing.assert_array_equal(out[1, ::2], np.float32(-0.5) * r1)
+    assert not out[1, 1::2].any()
+    assert not out[2].any()  # zero row stays zero (r = 1 / sqrt(eps) finite)
+    # without the epsilon the constant row would map to exactly 1
+    assert abs(float(out[0, 0]) - 1.0) < 2e-6
+
+
+def test_rmsnorm_unit_rms_and_fp64_bound():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((5, 2560)) * np.array([[1e-2], [1.0], [3.0], [40.0], [1e3]])).astype(np.float32)
+    out = oracle.rmsnorm(x)
+    x64 = x.astype(np.float64)
+    ref = x64 / np.sqrt((x64 ** 2).mean(1, keepdims=True) + 1e-5)
+    # three fp32 roundings of r and one of the product: a few ulp
+    assert np.all(np.abs(out - ref) <= np.abs(ref) * 4 * 2.0 ** -23 + 1e-30)
+    rms = np.sqrt((out.astype(np.float64) ** 2).mean(1))
+    np.testing.assert_allclose(rms[1:], 1.0, rtol=1e-5)
+    # the small row is pulled below 1 by the epsilon: rms = s / sqrt(s^2 + eps)
+    s = np.sqrt((x64[0] ** 2).mean())
+    assert abs(rms[0] - s / np.sqrt(s * s + 1e-5)) < 1e-5
+
+
+def test_rmsnorm_sign_symmetry_and_row_independence():
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((4, 300)).astype(np.float32)
+    out = oracle.rmsnorm(x)
+    np.testing.assert_array_equal(oracle.rmsnorm(-x), -out)
+    np.testing.assert_array_equal(oracle.rmsnorm(x[2:3]), out[2:3])
+    np.testing.assert_array_equal(oracle.rmsnorm(x[:, ::-1].copy())[:, ::-1] != 0, out != 0)
