@@ -19,8 +19,11 @@ Also printed on the same JSON line:
                 graph of back-to-back launches), against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) running the same
                 step on the host cores, on a bounded number of repetitions;
-  also          the other workloads: 100B-class decode (M = 1, 8, 32) in GB/s
-                and prefill GEMMs (2B M=2048, 100B M=512) in int8 TOPS.
+  also          the other workloads: one decode step over the 30-layer 2B-class
+                stack (210 BitLinears + glue, batch 1 and 8) in tokens/s,
+                checked bit for bit against the oracle's chain; 100B-class
+                decode (M = 1, 8, 32) in GB/s; prefill GEMMs (2B M=2048,
+                100B M=512) in int8 TOPS.
 """
 from __future__ import annotations
 
@@ -272,6 +275,82 @@ def decode_extra(shapes, Ms, dev, steps=100):
     return res
 
 
+def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
+    """One decode step over all BitLinears of the 30-layer stack, for each batch in Ms.
+
+    Latent weights are drawn on the device (torch generator, one seed per
+    matrix), packed, and copied to the host where the oracle advances its own
+    chain layer by layer from the same bf16 input tokens; after one eager step
+    the GPU's residual stream must equal the oracle's bit for bit.  A timed
+    step restarts from the input tokens (a 10 KB device copy) and runs the
+    210 BitLinears with their glue; `steps` of them form one HIP graph."""
+    import oracle
+    from bitlinear_matmul_02_amd.decoder import DecoderStack, PackedLinear
+    threads = min(16, os.cpu_count() or 1)
+    x0 = {M: workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, workloads.D_MODEL, workloads.DECODER_X0_SEED))
+          for M in Ms}
+    xr = dict(x0)
+    layers, wbytes = [], 0
+    for l in range(n_layers):
+        L, lat = {}, {}
+        for j, (name, K, N) in enumerate(workloads.LAYER_SHAPES):
+            g = torch.Generator(device=dev).manual_seed(workloads.decoder_weight_seed(l, j))
+            w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * workloads.W_STD
+            packed, beta = bl.pack_weights(w)
+            L[name] = PackedLinear(packed, beta, N, K)
+            lat[name] = w.cpu().numpy()
+            wbytes += packed.numel()
+            del w
+        tern = {}
+        for name, w in lat.items():
+            b = oracle.absmean(w)
+            tern[name] = (b, oracle.ternarize(w, b))
+        del lat
+
+        def lin(inp, name):
+            b, t = tern[name]
+            q, ds, _ = oracle.quant_act(inp)
+            return oracle.dequant(oracle.matmul_i32(q, t, threads=threads), ds, b)
+        for M in Ms:
+            x = xr[M]
+            q = lin(oracle.rmsnorm(x), "q")  # k and v do not feed the residual stream
+            x = oracle.add_f32(x, lin(q, "o"))
+            xn = oracle.rmsnorm(x)
+            x = oracle.add_f32(x, lin(oracle.relu2_mul(lin(xn, "gate"), lin(xn, "up")), "down"))
+            xr[M] = x
+        layers.append(L)
+        del tern
+    res = {"layers": n_layers, "bitlinears": 7 * n_layers, "weight_bytes": wbytes}
+    for M in Ms:
+        stack = DecoderStack(layers, M, dev)
+        src = torch.from_numpy(x0[M]).to(dev)
+        x = src.clone()
+        stack.step(x)
+        torch.cuda.synchronize()
+        got = x.cpu().numpy()
+        exact = bool(np.array_equal(got, xr[M]))
+        rel = float(np.max(np.abs(got.astype(np.float64) - xr[M]) / np.maximum(np.abs(xr[M]), 1e-30)))
+        if not np.all(np.isfinite(xr[M])) or not (exact or rel <= 1e-3):
+            raise RuntimeError("decode step M=%d differs from the oracle (max rel %.3g)" % (M, rel))
+
+        def one(i):
+            x.copy_(src)
+            stack.step(x)
+        g = capture(one, steps)
+        time_graph(g)
+        el, _ = time_graph(g)
+        t = el / steps
+        res["M%d" % M] = {"tok_s": round(M / t, 1), "us_per_step": round(t * 1e6, 1),
+                          "weight_GB_s": round(wbytes / t / 1e9, 1),
+                          "frac_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                          "path": "fused" if stack.fused else "quant_act + gemv",
+                          "oracle_match": "bit-exact" if exact else "rel %.2g" % rel}
+        del g, stack, x, src
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
 def prefill_extra(M, shapes, dev, reps=20):
     res = {}
     for i, (K, N) in enumerate(shapes):
@@ -335,6 +414,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(host, wl)
     if not args.quick:
         result["also"] = {
+            "decode_step_2b_30l": decode_step(workloads.DECODE_STEP_BATCHES, dev),
             "decode_100b": decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
             "prefill_2b_m2048": prefill_extra(2048, ((2560, 6912), (6912, 2560)), dev),
             "prefill_100b_m512": prefill_extra(512, workloads.SHAPES_100B, dev),

@@ -13,7 +13,9 @@ Functions carry the C names:
     bitlinear_forward_decode(x, packed, w_beta, N, y)
     bitlinear_relu2_mul(g, u, h)
 An fp32 output tensor can be passed with ``accumulate=True`` to the product
-calls, which then add their result into it (``BITLINEAR_F32_ADD``).
+calls, which then add their result into it (``BITLINEAR_F32_ADD``); the calls
+that quantize activations take ``rmsnorm=True`` to RMS-normalize each row
+first (``BITLINEAR_X_RMSNORM``).
 plus allocation helpers (``act_stride``, ``packed_bytes`` ...) and two
 conveniences that allocate outputs (``quant_act``, ``pack_weights``,
 ``linear``).
@@ -30,6 +32,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libbitlinear.so")
 
 OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16, I32, F32_ADD = 0, 1, 2, 3
+X_RMSNORM = 16  # flag OR-ed into an activation dtype: RMS-normalize rows before quantizing
 MAX_K, MAX_N, MAX_M, GEMV_MAX_M = 131072, 1 << 20, 1 << 20, 64
 
 EXPORTS = (
@@ -131,10 +134,14 @@ def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
 
 
 # --------------------------------------------------------------- the C calls
-def bitlinear_quant_act(x, x_q, x_ds, x_rowsum=None, stream=None) -> None:
+def _xdtype(x, rmsnorm: bool) -> int:
+    return _DTYPE[x.dtype] | (X_RMSNORM if rmsnorm else 0)
+
+
+def bitlinear_quant_act(x, x_q, x_ds, x_rowsum=None, stream=None, rmsnorm: bool = False) -> None:
     """x [M][K] bf16/fp32 -> x_q [M][act_stride(K)] int8, x_ds [M] fp32, x_rowsum [M] int32."""
     M, K = x.shape
-    _check(lib().bitlinear_quant_act(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(x_q), _ptr(x_ds),
+    _check(lib().bitlinear_quant_act(_ptr(x), _xdtype(x, rmsnorm), M, K, _ptr(x_q), _ptr(x_ds),
                                      _ptr(x_rowsum), _stream(stream)))
 
 
@@ -174,10 +181,11 @@ def bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=No
              stream, accumulate)
 
 
-def bitlinear_forward_decode(x, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
+def bitlinear_forward_decode(x, packed, w_beta, N, y, stream=None, accumulate: bool = False,
+                             rmsnorm: bool = False) -> None:
     """y [M][N] = BitLinear(x) for M <= 64 tokens in one launch (quantization fused)."""
     M, K = x.shape
-    _check(lib().bitlinear_forward_decode(_ptr(x), _DTYPE[x.dtype], M, K, _ptr(packed), _ptr(w_beta), N,
+    _check(lib().bitlinear_forward_decode(_ptr(x), _xdtype(x, rmsnorm), M, K, _ptr(packed), _ptr(w_beta), N,
                                           _ptr(y), _ydtype(y, accumulate), _stream(stream)))
 
 
@@ -208,12 +216,12 @@ def workspace(nbytes: int, device) -> torch.Tensor | None:
     return buf
 
 
-def quant_act(x, with_rowsum: bool = False, stream=None):
+def quant_act(x, with_rowsum: bool = False, stream=None, rmsnorm: bool = False):
     M, K = x.shape
     x_q = torch.empty((M, act_stride(K)), dtype=torch.int8, device=x.device)
     x_ds = torch.empty((M,), dtype=torch.float32, device=x.device)
     rs = torch.empty((M,), dtype=torch.int32, device=x.device) if with_rowsum else None
-    bitlinear_quant_act(x, x_q, x_ds, rs, stream)
+    bitlinear_quant_act(x, x_q, x_ds, rs, stream, rmsnorm=rmsnorm)
     return (x_q, x_ds, rs) if with_rowsum else (x_q, x_ds)
 
 

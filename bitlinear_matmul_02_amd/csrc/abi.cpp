@@ -103,13 +103,14 @@ int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 int bitlinear_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* x_q, float* x_ds,
                         int32_t* x_rowsum, void* stream) {
   const char* fn = "bitlinear_quant_act";
-  if (x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_F32)
-    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32", fn);
+  const int x_base = x_dtype & ~BITLINEAR_X_RMSNORM;
+  if (x_base != BITLINEAR_BF16 && x_base != BITLINEAR_F32)
+    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32 (| BITLINEAR_X_RMSNORM)", fn);
   if (M < 0 || M > BITLINEAR_MAX_M) return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
   if (!k_ok(K)) return fail(BITLINEAR_ERR_SHAPE, "%s: K=%lld outside [1, %d]", fn, (long long)K, BITLINEAR_MAX_K);
   if (M == 0) return ok();
   if (!x || !x_q || !x_ds) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
-  if (!aligned(x, x_dtype == BITLINEAR_BF16 ? 2 : 4) || !aligned(x_q, 16) || !aligned(x_ds, 4) ||
+  if (!aligned(x, x_base == BITLINEAR_BF16 ? 2 : 4) || !aligned(x_q, 16) || !aligned(x_ds, 4) ||
       (x_rowsum && !aligned(x_rowsum, 4)))
     return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned pointer (x_q needs 16 bytes)", fn);
   return hip_status(bl::launch_quant_act(x, x_dtype, M, K, act_stride(K), x_q, x_ds, x_rowsum,
@@ -159,13 +160,14 @@ int bitlinear_gemm(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, c
 int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, const void* packed,
                              const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
   const char* fn = "bitlinear_forward_decode";
-  if (x_dtype != BITLINEAR_BF16 && x_dtype != BITLINEAR_F32)
-    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32", fn);
+  const int x_base = x_dtype & ~BITLINEAR_X_RMSNORM;
+  if (x_base != BITLINEAR_BF16 && x_base != BITLINEAR_F32)
+    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32 (| BITLINEAR_X_RMSNORM)", fn);
   int st = check_common(fn, M, BITLINEAR_GEMV_MAX_M, K, packed, w_beta, N, y, y_dtype);
   if (st != BITLINEAR_OK) return st;
   if (M == 0) return ok();
   if (!x) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
-  if (!aligned(x, x_dtype == BITLINEAR_BF16 ? 2 : 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x not element aligned", fn);
+  if (!aligned(x, x_base == BITLINEAR_BF16 ? 2 : 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x not element aligned", fn);
   if (!bl::decode_fused_fits(M, K))
     return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (act_stride(K) + 16) = %lld exceeds %d bytes", fn,
                 (long long)(M * (act_stride(K) + 16)), BITLINEAR_DECODE_MAX_ACT_BYTES);

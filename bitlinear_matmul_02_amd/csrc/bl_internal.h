@@ -18,6 +18,7 @@ constexpr int kBetaChunk = 4096;
 // LDS a decode workgroup may use for its int8 activation rows (each row is
 // act_stride(K) + 16 bytes); with its 4 KB reduction buffer it stays < 64 KB.
 constexpr int64_t kDecodeLdsBytes = BITLINEAR_DECODE_MAX_ACT_BYTES;
+constexpr int kXDtypeMask = BITLINEAR_X_RMSNORM - 1;  // x_dtype without its flags
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

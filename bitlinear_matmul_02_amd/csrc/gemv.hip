@@ -39,6 +39,8 @@
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
 // workspace again.
+#include <mutex>
+
 #include "bl_internal.h"
 
 namespace bl {
@@ -119,8 +121,9 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse) {
 struct GemvArgs {
   const int8_t* q;  // [M][ldq] int8 (modes AGLOBAL, ALDS_Q)
   const void* x;    // [M][K] bf16/fp32 activations (mode ALDS_X)
-  int x_dtype;
+  int x_dtype;       // BITLINEAR_BF16 or BITLINEAR_F32
   int x_vec;        // ALDS_X: rows can be read in 16-byte pieces
+  int norm;         // fused modes: RMS-normalize each row before quantizing
   const float* ds;  // [M] (modes AGLOBAL, ALDS_Q)
   int M, K, N, Nt, Kt, tps, SB;
   int64_t ldq, ldl;
@@ -218,6 +221,42 @@ __device__ inline void piece_quant_store(const u4 v, bool bf16, float qs, int8_t
   }
 }
 
+// Sum of squares of a piece's values in fp64 (each square exact).
+__device__ inline double piece_sumsq(const u4 v, bool bf16) {
+  double s = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (bf16) {
+      const double lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xffff0000u);
+      s += lo * lo;
+      s += hi * hi;
+    } else {
+      const double e = __uint_as_float(v[j]);
+      s += e * e;
+    }
+  }
+  return s;
+}
+
+// RMS normalization scale r = 1 / sqrt((float)(S / K) + 1e-5) (fp32, correctly
+// rounded division and root), as the standalone quantizer applies it.
+__device__ inline float rms_scale(double sumsq, int K) {
+  const float ms = (float)(sumsq / (double)K);
+  return 1.0f / sqrtf(ms + 1e-5f);
+}
+
+// Quantize a piece after scaling its values by r (bf16 widens exactly to fp32).
+__device__ inline void piece_quant_store_norm(const u4 v, bool bf16, float r, float qs, int8_t* dst) {
+  auto sc = [&](uint32_t bits) { return __float_as_uint(__fmul_rn(__uint_as_float(bits), r)); };
+  if (bf16) {
+    piece_quant_store(u4{sc(v[0] << 16), sc(v[0] & 0xffff0000u), sc(v[1] << 16), sc(v[1] & 0xffff0000u)}, false, qs, dst);
+    piece_quant_store(u4{sc(v[2] << 16), sc(v[2] & 0xffff0000u), sc(v[3] << 16), sc(v[3] & 0xffff0000u)}, false, qs,
+                      dst + 4);
+  } else {
+    piece_quant_store(u4{sc(v[0]), sc(v[1]), sc(v[2]), sc(v[3])}, false, qs, dst);
+  }
+}
+
 // Row of piece c (cpr pieces per row); exact for c < 2^24 (the float error of
 // (c + 0.5) / cpr is far below the 0.5 / cpr margin to a row boundary).
 __device__ inline int piece_row(int c, int M, float inv_cpr) {
@@ -228,9 +267,12 @@ __device__ inline int piece_row(int c, int M, float inv_cpr) {
 // gamma_m = max |x[m][:]| from the held pieces (per-wave maxima in LDS slots,
 // combined by thread m), then each piece quantized with
 // q = rint(x * (127 / max(gamma, 1e-5))) into LDS.  `slots` holds at least
-// waves * M words.
-__device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds, uint32_t* slots,
-                              float* row_g, float* row_qs) {
+// waves * M words, `sq` waves * M doubles.  With a.norm the row is first
+// RMS-normalized (per-wave fp64 sums of squares in `sq`, added in wave order):
+// the quantizer sees fl(x * r), whose maximum is fl(gamma * r).
+template <bool NORM>
+__device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds, uint32_t* slots, double* sq,
+                              float* row_g, float* row_qs, float* row_r) {
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, waves = nthr >> 6;
   const bool bf16 = a.x_dtype == BITLINEAR_BF16;
   const int per16 = bf16 ? 8 : 4;
@@ -244,79 +286,130 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
     const int m = i / padw;
     *reinterpret_cast<uint32_t*>(lds + (int64_t)m * a.ldl + a.K + 4 * (i - m * padw)) = 0u;
   }
+  constexpr bool norm = NORM;
   for (int m = 0; m < M; ++m) {
     uint32_t amax = 0;
+    double s2 = 0.0;
 #pragma unroll
     for (int r = 0; r < kXReg; ++r) {
       const int c = tid + r * nthr;
-      if (c < npieces && piece_row(c, M, inv_cpr) == m) amax = max(amax, piece_absmax_bits(v[r], bf16));
+      if (c < npieces && piece_row(c, M, inv_cpr) == m) {
+        amax = max(amax, piece_absmax_bits(v[r], bf16));
+        if (norm) s2 += piece_sumsq(v[r], bf16);
+      }
     }
     for (int c = tid + kXReg * nthr; c < npieces; c += nthr)  // pieces beyond the held ones
-      if (piece_row(c, M, inv_cpr) == m) amax = max(amax, piece_absmax_bits(src[c], bf16));
+      if (piece_row(c, M, inv_cpr) == m) {
+        amax = max(amax, piece_absmax_bits(src[c], bf16));
+        if (norm) s2 += piece_sumsq(src[c], bf16);
+      }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
     if (lane == 0) slots[wave * M + m] = amax;
+    if (norm) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+      if (lane == 0) sq[wave * M + m] = s2;
+    }
   }
   __syncthreads();
   if (tid < M) {
     uint32_t g = 0;
     for (int w = 0; w < waves; ++w) g = max(g, slots[w * M + tid]);
-    const float gm = fmaxf(__uint_as_float(g), 1e-5f);
+    float gamma = __uint_as_float(g);
+    if (norm) {
+      double s2 = 0.0;
+      for (int w = 0; w < waves; ++w) s2 += sq[w * M + tid];
+      const float rn = rms_scale(s2, a.K);
+      row_r[tid] = rn;
+      gamma = __fmul_rn(gamma, rn);
+    }
+    const float gm = fmaxf(gamma, 1e-5f);
     row_g[tid] = gm;
     row_qs[tid] = 127.0f / gm;  // IEEE division, as the standalone quantizer
   }
   __syncthreads();
+  auto quant = [&](const u4 p, int c) {
+    const int m = piece_row(c, M, inv_cpr);
+    int8_t* dst = lds + (int64_t)m * a.ldl + (c - m * cpr) * per16;
+    if (norm)
+      piece_quant_store_norm(p, bf16, row_r[m], row_qs[m], dst);
+    else
+      piece_quant_store(p, bf16, row_qs[m], dst);
+  };
 #pragma unroll
   for (int r = 0; r < kXReg; ++r) {
     const int c = tid + r * nthr;
-    if (c < npieces) {
-      const int m = piece_row(c, M, inv_cpr);
-      piece_quant_store(v[r], bf16, row_qs[m], lds + (int64_t)m * a.ldl + (c - m * cpr) * per16);
-    }
+    if (c < npieces) quant(v[r], c);
   }
-  for (int c = tid + kXReg * nthr; c < npieces; c += nthr) {
-    const int m = piece_row(c, M, inv_cpr);
-    piece_quant_store(src[c], bf16, row_qs[m], lds + (int64_t)m * a.ldl + (c - m * cpr) * per16);
-  }
+  for (int c = tid + kXReg * nthr; c < npieces; c += nthr) quant(src[c], c);
   __syncthreads();
 }
 
 // ALDS_XS prologue, for rows that are not whole 16-byte pieces (unaligned x
-// or K not a multiple of the piece): row_g[m] = max(max_k |x[m][k]|, 1e-5),
-// then the int8 rows into LDS, element by element.
-__device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, float* row_g) {
-  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63;
+// or K not a multiple of the piece): row_g[m] = max(max_k |x[m][k]|, 1e-5)
+// (of the normalized row with a.norm, as stage_store_x), then the int8 rows
+// into LDS, element by element.
+template <bool NORM>
+__device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, double* sq, float* row_g, float* row_qs,
+                                     float* row_r) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, waves = nthr >> 6;
   const int M = a.M;
+  constexpr bool norm = NORM;
   const int64_t Kp = (int64_t)a.Kt * kTileK;
   if (tid < 64) row_g[tid] = 0.0f;
   __syncthreads();
   for (int m = 0; m < M; ++m) {
     float amax = 0.0f;
-    for (int k = tid; k < a.K; k += nthr) amax = fmaxf(amax, fabsf(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k)));
+    double s2 = 0.0;
+    for (int k = tid; k < a.K; k += nthr) {
+      const float xv = x_at(a.x, a.x_dtype, (int64_t)m * a.K + k);
+      amax = fmaxf(amax, fabsf(xv));
+      if (norm) s2 += (double)xv * (double)xv;
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     // |x| >= 0, so the fp32 bit patterns order like the values
     if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&row_g[m]), __float_as_uint(amax));
+    if (norm) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+      if (lane == 0) sq[wave * M + m] = s2;
+    }
+  }
+  __syncthreads();
+  if (tid < M) {
+    float gamma = row_g[tid];
+    if (norm) {
+      double s2 = 0.0;
+      for (int w = 0; w < waves; ++w) s2 += sq[w * M + tid];
+      const float rn = rms_scale(s2, a.K);
+      row_r[tid] = rn;
+      gamma = __fmul_rn(gamma, rn);
+    }
+    const float gm = fmaxf(gamma, kEpsX);
+    row_g[tid] = gm;
+    row_qs[tid] = 127.0f / gm;  // IEEE division, as the standalone quantizer
   }
   __syncthreads();
   for (int m = 0; m < M; ++m) {
-    const float g = fmaxf(row_g[m], kEpsX);
-    const float qs = 127.0f / g;  // IEEE division, as the standalone quantizer
+    const float qs = row_qs[m], rn = norm ? row_r[m] : 1.0f;
     int8_t* lrow = lds + (int64_t)m * a.ldl;
     for (int k = 4 * tid; k < Kp; k += 4 * nthr) {
       uint32_t w = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (k + j < a.K) w |= qbyte(x_at(a.x, a.x_dtype, (int64_t)m * a.K + k + j), qs) << (8 * j);
+        if (k + j < a.K) {
+          const float xv = x_at(a.x, a.x_dtype, (int64_t)m * a.K + k + j);
+          w |= qbyte(norm ? __fmul_rn(xv, rn) : xv, qs) << (8 * j);
+        }
       *reinterpret_cast<uint32_t*>(lrow + k) = w;
     }
   }
   __syncthreads();
-  if (tid < M) row_g[tid] = fmaxf(row_g[tid], kEpsX);
-  __syncthreads();
 }
 
-template <int MB, int NB, int AM, int kU = ring_depth(MB, NB, AM)>
+template <int MB, int NB, int AM, bool NORM, int kU = ring_depth(MB, NB, AM)>
 __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int E = MB * NB * 4;  // accumulator values per lane
   constexpr int UA = AM == AGLOBAL ? kU : 1;
@@ -324,6 +417,8 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   constexpr bool FUSED = AM == ALDS_X || AM == ALDS_XS;
   __shared__ float row_g[FUSED ? 64 : 1];   // fused: per-row g = max(max |x|, 1e-5)
   __shared__ float row_qs[FUSED ? 64 : 1];  // fused: per-row 127 / max(gamma, eps)
+  __shared__ float row_r[NORM ? 64 : 1];   // fused with normalization: per-row RMS scale
+  __shared__ double sq_slots[NORM ? max_waves(MB) * 16 * MB : 1];  // per-wave, per-row sums of squares
   extern __shared__ __attribute__((aligned(16))) int8_t act_lds[];  // [M][ldl]
 
   const int lane = threadIdx.x & 63, waves = blockDim.x >> 6;
@@ -399,8 +494,9 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // weight loads (that would wait for the pieces before the stream starts)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AM == ALDS_Q) stage_store_q(a, stage, act_lds);
-  if constexpr (AM == ALDS_X) stage_store_x(a, stage, act_lds, reinterpret_cast<uint32_t*>(&red[0][0]), row_g, row_qs);
-  if constexpr (AM == ALDS_XS) quantize_rows_scalar(a, act_lds, row_g);
+  if constexpr (AM == ALDS_X)
+    stage_store_x<NORM>(a, stage, act_lds, reinterpret_cast<uint32_t*>(&red[0][0]), sq_slots, row_g, row_qs, row_r);
+  if constexpr (AM == ALDS_XS) quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
 
   if (has_work) {
     // ring of kU k-tiles in flight; re-loads past the end read tile k1-1
@@ -491,7 +587,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     for (int r = 0; r < 4; ++r) {
       const int m = mb * 16 + 4 * g4 + r;
       if (m >= M) continue;
-      const float dsm = FUSED ? row_g[m] / 127.0f : a.ds[m];
+      const float dsm = FUSED ? row_g[m] / 127.0f : a.ds[m];  // g of the normalized row with a.norm
       const float scale = dsm * bt;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
@@ -501,17 +597,28 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     }
 }
 
-template <int MB, int NB, int AM>
+template <int MB, int NB, int AM, bool NORM>
 hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),
+  if constexpr (AM == ALDS_X || AM == ALDS_XS) {
+    // static LDS of the fused modes plus the largest activation rows can pass
+    // the default 64 KB per workgroup: raise the limit once
+    static std::once_flag once;
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM>),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLdsBytes);
+    });
+    if (attr != hipSuccess) return attr;
+  }
+  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),
                      (size_t)p.lds_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int AM>
+template <int AM, bool NORM = false>
 hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 #define BL_GEMV_CASE(mb, nb) \
-  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM>(p, a, s)
+  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM, NORM>(p, a, s)
   // the (MB, NB) pairs make_plan can produce for this mode
   BL_GEMV_CASE(1, 1);
   BL_GEMV_CASE(1, 2);
@@ -531,7 +638,9 @@ hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 hipError_t dispatch(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   switch (p.amode) {
     case ALDS_Q: return dispatch_mb_nb<ALDS_Q>(p, a, s);
-    case ALDS_X: return a.x_vec ? dispatch_mb_nb<ALDS_X>(p, a, s) : dispatch_mb_nb<ALDS_XS>(p, a, s);
+    case ALDS_X:
+      if (a.norm) return a.x_vec ? dispatch_mb_nb<ALDS_X, true>(p, a, s) : dispatch_mb_nb<ALDS_XS, true>(p, a, s);
+      return a.x_vec ? dispatch_mb_nb<ALDS_X>(p, a, s) : dispatch_mb_nb<ALDS_XS>(p, a, s);
     default: return dispatch_mb_nb<AGLOBAL>(p, a, s);
   }
 }
@@ -583,8 +692,9 @@ hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, co
   const GemvPlan p = make_plan(M, N, K, true);
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr);
   a.x = x;
-  a.x_dtype = x_dtype;
-  const int per16 = x_dtype == BITLINEAR_BF16 ? 8 : 4;
+  a.x_dtype = x_dtype & kXDtypeMask;
+  a.norm = (x_dtype & BITLINEAR_X_RMSNORM) != 0;
+  const int per16 = a.x_dtype == BITLINEAR_BF16 ? 8 : 4;
   a.x_vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
   return dispatch(p, a, s);
 }

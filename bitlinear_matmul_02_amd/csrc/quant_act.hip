@@ -11,12 +11,20 @@
 // int8 (zero padding up to the row stride).  Rows that are not whole 16-byte
 // pieces (unaligned x, or K not a multiple of the piece) take an element
 // path.  Long rows get 1024 threads, short ones 256.
+//
+// Optionally the row is RMS-normalized first (gain 1; "Key Technologies
+// Enabling the BitNET Family", Architectural Innovations and Optimizations:
+// RMSNorm is the normalization): S = sum x^2 in fp64 (squares exact),
+// r = 1 / sqrt((float)(S / K) + 1e-5) in fp32, and the quantizer sees
+// fl(x * r).  Its maximum is fl(gamma * r) exactly, because rounding is
+// monotone, so gamma is still taken on the raw row.
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
 constexpr float kEpsX = 1e-5f;
+constexpr float kEpsNorm = 1e-5f;
 constexpr int kHold = 4;  // pieces per thread kept in registers
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
@@ -68,6 +76,39 @@ __device__ inline float load_x(const void* x, bool bf16, int64_t i) {
   return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i]) : static_cast<const float*>(x)[i];
 }
 
+// Sum of squares of one piece's values, in fp64 (each square is exact).
+__device__ inline double piece_sumsq(const u4 v, bool bf16) {
+  double s = 0.0;
+  if (bf16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = __uint_as_float(v[j] << 16), hi = __uint_as_float(v[j] & 0xffff0000u);
+      s += lo * lo;
+      s += hi * hi;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = __uint_as_float(v[j]);
+      s += a * a;
+    }
+  }
+  return s;
+}
+
+// r = 1 / sqrt(mean square + eps), fp32 (correctly rounded division and root).
+__device__ inline float rms_scale(double sumsq, int64_t K) {
+  const float ms = (float)(sumsq / (double)K);
+  return 1.0f / sqrtf(ms + kEpsNorm);
+}
+
+// Apply the normalization to a piece (fp32 multiply per value); the result
+// is an fp32 piece (bf16 input widens to two fp32 pieces: lo, hi).
+__device__ inline u4 scale_f32_piece(const u4 v, float r) {
+  return u4{__float_as_uint(__fmul_rn(__uint_as_float(v[0]), r)), __float_as_uint(__fmul_rn(__uint_as_float(v[1]), r)),
+            __float_as_uint(__fmul_rn(__uint_as_float(v[2]), r)), __float_as_uint(__fmul_rn(__uint_as_float(v[3]), r))};
+}
+
 // Block-wide max of non-negative float bit patterns / sum of ints via LDS.
 template <int NT>
 __device__ inline uint32_t block_max(uint32_t v, uint32_t* slots) {
@@ -93,12 +134,36 @@ __device__ inline int block_sum(int v, int* slots) {
   return r;
 }
 
-template <int NT, bool VEC>
+template <int NT>
+__device__ inline double block_sum_f64(double v, double* slots) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double r = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) r += slots[w];
+  return r;
+}
+
+// Quantize one piece after normalization: bf16 values widen exactly to fp32
+// and are scaled there; writes 8 (bf16) or 4 bytes.
+__device__ inline int piece_quant_store_norm(const u4 v, bool bf16, float r, float qs, int8_t* dst) {
+  if (bf16) {
+    const u4 lo = scale_f32_piece(u4{v[0] << 16, v[0] & 0xffff0000u, v[1] << 16, v[1] & 0xffff0000u}, r);
+    const u4 hi = scale_f32_piece(u4{v[2] << 16, v[2] & 0xffff0000u, v[3] << 16, v[3] & 0xffff0000u}, r);
+    return piece_quant_store(lo, false, qs, dst) + piece_quant_store(hi, false, qs, dst + 4);
+  }
+  return piece_quant_store(scale_f32_piece(v, r), false, qs, dst);
+}
+
+template <int NT, bool VEC, bool NORM>
 __global__ __launch_bounds__(NT) void quant_act_kernel(const void* __restrict__ x, int bf16i, int64_t K,
                                                        int64_t ldq, int8_t* __restrict__ q,
                                                        float* __restrict__ ds, int32_t* __restrict__ rowsum) {
   __shared__ uint32_t slots_max[NT / 64];
   __shared__ int slots_sum[NT / 64];
+  __shared__ double slots_sq[NORM ? NT / 64 : 1];
   const bool bf16 = bf16i != 0;
   const int64_t m = blockIdx.x;
   const int tid = threadIdx.x;
@@ -113,29 +178,58 @@ __global__ __launch_bounds__(NT) void quant_act_kernel(const void* __restrict__ 
 #pragma unroll
     for (int r = 0; r < kHold; ++r) v[r] = src[min(tid + r * NT, np - 1)];  // duplicates never stored
     uint32_t amax = 0;
+    double sq = 0.0;
 #pragma unroll
-    for (int r = 0; r < kHold; ++r) amax = max(amax, piece_absmax_bits(v[r], bf16));
-    for (int c = tid + kHold * NT; c < np; c += NT) amax = max(amax, piece_absmax_bits(src[c], bf16));
-    g = fmaxf(__uint_as_float(block_max<NT>(amax, slots_max)), kEpsX);
+    for (int r = 0; r < kHold; ++r) {
+      amax = max(amax, piece_absmax_bits(v[r], bf16));
+      if (NORM && tid + r * NT < np) sq += piece_sumsq(v[r], bf16);  // duplicates excluded
+    }
+    for (int c = tid + kHold * NT; c < np; c += NT) {
+      amax = max(amax, piece_absmax_bits(src[c], bf16));
+      if (NORM) sq += piece_sumsq(src[c], bf16);
+    }
+    float gamma = __uint_as_float(block_max<NT>(amax, slots_max));
+    float rn = 1.0f;
+    if constexpr (NORM) {
+      rn = rms_scale(block_sum_f64<NT>(sq, slots_sq), K);
+      gamma = __fmul_rn(gamma, rn);  // = max |fl(x * r)|
+    }
+    g = fmaxf(gamma, kEpsX);
     const float qs = 127.0f / g;  // IEEE division
+    auto quant = [&](const u4 p, int c) {
+      int8_t* dst = qrow + (int64_t)c * per16;
+      return NORM ? piece_quant_store_norm(p, bf16, rn, qs, dst) : piece_quant_store(p, bf16, qs, dst);
+    };
 #pragma unroll
     for (int r = 0; r < kHold; ++r) {
       const int c = tid + r * NT;
-      if (c < np) sum += piece_quant_store(v[r], bf16, qs, qrow + (int64_t)c * per16);
+      if (c < np) sum += quant(v[r], c);
     }
-    for (int c = tid + kHold * NT; c < np; c += NT) sum += piece_quant_store(src[c], bf16, qs, qrow + (int64_t)c * per16);
+    for (int c = tid + kHold * NT; c < np; c += NT) sum += quant(src[c], c);
     for (int64_t k = K + 4 * (int64_t)tid; k < ldq; k += 4 * NT) *reinterpret_cast<uint32_t*>(qrow + k) = 0u;
   } else {
     float amax = 0.0f;
-    for (int64_t k = tid; k < K; k += NT) amax = fmaxf(amax, fabsf(load_x(x, bf16, m * K + k)));
-    g = fmaxf(__uint_as_float(block_max<NT>(__float_as_uint(amax), slots_max)), kEpsX);
+    double sq = 0.0;
+    for (int64_t k = tid; k < K; k += NT) {
+      const float xv = load_x(x, bf16, m * K + k);
+      amax = fmaxf(amax, fabsf(xv));
+      if (NORM) sq += (double)xv * (double)xv;
+    }
+    float gamma = __uint_as_float(block_max<NT>(__float_as_uint(amax), slots_max));
+    float rn = 1.0f;
+    if constexpr (NORM) {
+      rn = rms_scale(block_sum_f64<NT>(sq, slots_sq), K);
+      gamma = __fmul_rn(gamma, rn);
+    }
+    g = fmaxf(gamma, kEpsX);
     const float qs = 127.0f / g;
     for (int64_t k = 4 * (int64_t)tid; k < ldq; k += 4 * NT) {
       uint32_t w = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (k + j < K) {
-          const uint32_t b = qbyte(load_x(x, bf16, m * K + k + j), qs);
+          const float xv = load_x(x, bf16, m * K + k + j);
+          const uint32_t b = qbyte(NORM ? __fmul_rn(xv, rn) : xv, qs);
           w |= b << (8 * j);
           sum += (int)(int8_t)b;
         }
@@ -149,27 +243,40 @@ __global__ __launch_bounds__(NT) void quant_act_kernel(const void* __restrict__ 
   }
 }
 
-template <int NT>
+template <int NT, bool NORM>
 void launch_nt(const void* x, int bf16, int64_t M, int64_t K, int64_t ldq, int8_t* q, float* ds, int32_t* rowsum,
                bool vec, hipStream_t s) {
   if (vec)
-    hipLaunchKernelGGL((quant_act_kernel<NT, true>), dim3((unsigned)M), dim3(NT), 0, s, x, bf16, K, ldq, q, ds, rowsum);
+    hipLaunchKernelGGL((quant_act_kernel<NT, true, NORM>), dim3((unsigned)M), dim3(NT), 0, s, x, bf16, K, ldq, q, ds,
+                       rowsum);
   else
-    hipLaunchKernelGGL((quant_act_kernel<NT, false>), dim3((unsigned)M), dim3(NT), 0, s, x, bf16, K, ldq, q, ds, rowsum);
+    hipLaunchKernelGGL((quant_act_kernel<NT, false, NORM>), dim3((unsigned)M), dim3(NT), 0, s, x, bf16, K, ldq, q, ds,
+                       rowsum);
+}
+
+template <bool NORM>
+void launch_norm(const void* x, int bf16, int64_t M, int64_t K, int64_t ldq, int8_t* q, float* ds, int32_t* rowsum,
+                 bool vec, hipStream_t s) {
+  const int per16 = bf16 ? 8 : 4;
+  // 1024 threads once the row has more pieces than 256 threads hold
+  if (K / per16 > 256 * kHold)
+    launch_nt<1024, NORM>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
+  else
+    launch_nt<256, NORM>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
 }
 
 }  // namespace
 
 hipError_t launch_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldq,
                             int8_t* q, float* ds, int32_t* rowsum, hipStream_t s) {
-  const bool bf16 = x_dtype == BITLINEAR_BF16;
+  const bool bf16 = (x_dtype & kXDtypeMask) == BITLINEAR_BF16;
+  const bool norm = (x_dtype & BITLINEAR_X_RMSNORM) != 0;
   const int per16 = bf16 ? 8 : 4;
   const bool vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
-  // 1024 threads once the row has more pieces than 256 threads hold
-  if (K / per16 > 256 * kHold)
-    launch_nt<1024>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
+  if (norm)
+    launch_norm<true>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
   else
-    launch_nt<256>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
+    launch_norm<false>(x, bf16, M, K, ldq, q, ds, rowsum, vec, s);
   return hipGetLastError();
 }
 

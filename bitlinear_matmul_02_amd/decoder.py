@@ -1,17 +1,21 @@
 """Decode step over a stack of BitLinear decoder layers.
 
 Each layer holds seven BitLinears (q, k, v, o, gate, up, down) and the glue
-between them: the squared-ReLU gated feed-forward activation ("Key
-Technologies Enabling the BitNET Family", Architectural Innovations and
-Optimizations) and two residual sums.  Attention itself is not part of this
-path: the o projection takes the q projection's output in its place, and k / v
-are computed and kept (as a KV cache would receive them).  RMSNorm is not
-modelled.  Per layer, with x the fp32 residual stream [M][d]:
+between them ("Key Technologies Enabling the BitNET Family", Architectural
+Innovations and Optimizations: RMSNorm, squared ReLU in the feed-forward
+layers, no biases): two RMS normalizations (gain 1), the squared-ReLU gated
+feed-forward activation and two residual sums.  Attention itself is not part
+of this path: the o projection takes the q projection's output in its place,
+and k / v are computed and kept (as a KV cache would receive them).  Per
+layer, with x the fp32 residual stream [M][d] and N(.) the RMS normalization:
 
-    q, k, v = BL_q(x), BL_k(x), BL_v(x)
+    q, k, v = BL_q(N(x)), BL_k(N(x)), BL_v(N(x))
     x = x + BL_o(q)
-    h = ReLU(BL_gate(x))^2 * BL_up(x)
+    h = ReLU(BL_gate(N(x)))^2 * BL_up(N(x))
     x = x + BL_down(h)
+
+The normalization is fused into the BitLinears' activation quantization
+(``rmsnorm``), so N(x) is never written out.
 
 Everything is enqueued on one stream by the library's kernels and allocates
 nothing after construction, so a step can be captured in a HIP graph.  For at
@@ -70,22 +74,23 @@ class DecoderStack:
         fn(self.xq[lin.K], self.xds[lin.K], lin.K, lin.packed, lin.beta, lin.N, y, self.ws, stream,
            accumulate=accumulate)
 
-    def _linears(self, x, lins, outs, accumulate, stream):
-        """outs[i] (+)= BL_i(x) for BitLinears that share the input x."""
+    def _linears(self, x, lins, outs, accumulate, stream, rmsnorm=False):
+        """outs[i] (+)= BL_i(x) (of N(x) with rmsnorm) for BitLinears sharing the input x."""
         if self.fused:
             for lin, y in zip(lins, outs):
-                bitlinear_forward_decode(x, lin.packed, lin.beta, lin.N, y, stream, accumulate=accumulate)
+                bitlinear_forward_decode(x, lin.packed, lin.beta, lin.N, y, stream, accumulate=accumulate,
+                                         rmsnorm=rmsnorm)
             return
         K = lins[0].K
-        bitlinear_quant_act(x, self.xq[K], self.xds[K], None, stream)
+        bitlinear_quant_act(x, self.xq[K], self.xds[K], None, stream, rmsnorm=rmsnorm)
         for lin, y in zip(lins, outs):
             self._product(lin, y, accumulate, stream)
 
     def layer(self, i: int, x: torch.Tensor, stream=None) -> None:
         L = self.layers[i]
-        self._linears(x, (L["q"], L["k"], L["v"]), (self.q, self.k, self.v), False, stream)
+        self._linears(x, (L["q"], L["k"], L["v"]), (self.q, self.k, self.v), False, stream, rmsnorm=True)
         self._linears(self.q, (L["o"],), (x,), True, stream)
-        self._linears(x, (L["gate"], L["up"]), (self.g, self.u), False, stream)
+        self._linears(x, (L["gate"], L["up"]), (self.g, self.u), False, stream, rmsnorm=True)
         bitlinear_relu2_mul(self.g, self.u, self.h, stream)
         self._linears(self.h, (L["down"],), (x,), True, stream)
 

@@ -57,6 +57,14 @@ extern "C" {
 #define BITLINEAR_I32 2  /* raw int32 accumulators (output only) */
 #define BITLINEAR_F32_ADD 3 /* fp32, added to what y holds: y += value (output only) */
 
+/* Flag OR-ed into an activation x_dtype: RMS-normalize each token row (gain
+ * 1, no bias) before it is quantized ("Key Technologies Enabling the BitNET
+ * Family", Architectural Innovations and Optimizations: RMSNorm is the
+ * normalization).  S = sum_k x_k^2 in fp64, r = 1 / sqrt((float)(S / K) +
+ * 1e-5) in fp32, and the quantizer sees fl(x_k * r); x_ds then refers to the
+ * normalized row.  The fp64 sum is taken in a fixed but unspecified order. */
+#define BITLINEAR_X_RMSNORM 16
+
 /* Supported sizes. */
 #define BITLINEAR_MAX_K 131072       /* keeps 64 * 127 * K below 2^31 */
 #define BITLINEAR_MAX_N 1048576
@@ -96,7 +104,8 @@ int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * Per-token absmax activation quantization.
- *   x        [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32;
+ *   x        [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32,
+ *            optionally | BITLINEAR_X_RMSNORM;
  *            needs only element alignment (2 or 4 bytes).
  *   x_q      [M][bitlinear_act_stride(K)] int8 out:
  *            q = clamp(rint(x * (127 / g)), -127, 127), g = max(max_k |x|, 1e-5),
@@ -168,8 +177,8 @@ int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
  * identical to bitlinear_quant_act followed by bitlinear_gemv.  Every
  * workgroup quantizes the whole rows again, so this pays off for few tokens
  * (measured on MI355X: M <= 4); beyond that the two calls are faster.
- *   x       [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32
- *           (element alignment).
+ *   x       [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32,
+ *           optionally | BITLINEAR_X_RMSNORM (element alignment).
  *   packed, w_beta, y, y_dtype  as bitlinear_gemv.
  * Needs M * (bitlinear_act_stride(K) + 16) <= BITLINEAR_DECODE_MAX_ACT_BYTES,
  * else BITLINEAR_ERR_UNSUPPORTED (use bitlinear_quant_act + bitlinear_gemv).

@@ -39,6 +39,7 @@ def test_header_constants_match_binding():
     assert int(consts["BITLINEAR_BF16"]) == bl.BF16
     assert int(consts["BITLINEAR_I32"]) == bl.I32
     assert int(consts["BITLINEAR_F32_ADD"]) == bl.F32_ADD
+    assert int(consts["BITLINEAR_X_RMSNORM"]) == bl.X_RMSNORM
     assert int(consts["BITLINEAR_MAX_K"]) == bl.MAX_K
     assert int(consts["BITLINEAR_GEMV_MAX_M"]) == bl.GEMV_MAX_M
     assert int(consts["BITLINEAR_DECODE_MAX_ACT_BYTES"]) == bl.DECODE_MAX_ACT_BYTES
@@ -178,3 +179,19 @@ def test_accumulate_dtype_accepted_by_validation():
     assert call_product(fn, ydt=bl.F32_ADD, y=FAKE + 2) == bl.ERR_ALIGN
     assert call_product(fn, ydt=4) == bl.ERR_ARG
     assert "y_dtype" in bl.last_error()
+
+
+def test_rmsnorm_flag_validation():
+    L = bl.lib()
+    # accepted with either activation dtype (fails later, on the null x_q)
+    for dt in (bl.BF16 | bl.X_RMSNORM, bl.F32 | bl.X_RMSNORM):
+        assert L.bitlinear_quant_act(FAKE, dt, 1, 256, None, FAKE, None, None) == bl.ERR_ARG
+        assert "null" in bl.last_error()
+    # the flag does not make an output dtype valid as an input
+    assert L.bitlinear_quant_act(FAKE, bl.I32 | bl.X_RMSNORM, 1, 256, FAKE, FAKE, None, None) == bl.ERR_ARG
+    assert "x_dtype" in bl.last_error()
+    assert L.bitlinear_forward_decode(FAKE, bl.F32_ADD | bl.X_RMSNORM, 1, 256, FAKE, FAKE, 16, FAKE, bl.F32,
+                                      None) == bl.ERR_ARG
+    # alignment follows the base dtype
+    assert L.bitlinear_forward_decode(FAKE + 2, bl.F32 | bl.X_RMSNORM, 1, 256, FAKE, FAKE, 16, FAKE, bl.F32,
+                                      None) == bl.ERR_ALIGN

@@ -56,6 +56,56 @@ def test_relu2_mul_in_place():
     np.testing.assert_array_equal(gd.cpu().numpy(), oracle.relu2_mul(g, u))
 
 
+# ------------------------------------------------ RMS normalization fused into quantization
+def norm_inputs(M, K, src, seed):
+    xb = workloads.gen_acts_bf16(M, K, seed=seed)
+    xf = workloads.bf16_bits_to_f32(xb)
+    if src == "f32":
+        xf = xf * np.float32(1.37) + np.float32(0.01)  # values beyond bf16 precision
+        x = torch.from_numpy(xf).to(DEV)
+    else:
+        x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(DEV)
+    if M > 1:
+        xf[M // 2] = 0.0
+        x[M // 2] = 0
+    return x, xf
+
+
+@pytest.mark.parametrize("M,K", [(1, 2560), (8, 6912), (3, 13), (2, 512), (33, 28672), (4, 100), (5, 4096)])
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_quant_act_rmsnorm_parity(M, K, src):
+    x, xf = norm_inputs(M, K, src, seed=M * 13 + K)
+    q_ref, ds_ref, rs_ref = oracle.quant_act(oracle.rmsnorm(xf))
+    x_q, x_ds, rs = bl.quant_act(x, with_rowsum=True, rmsnorm=True)
+    torch.cuda.synchronize()
+    q = x_q.cpu().numpy()
+    np.testing.assert_array_equal(q[:, :K], q_ref)
+    assert not q[:, K:].any()
+    np.testing.assert_array_equal(x_ds.cpu().numpy(), ds_ref)
+    np.testing.assert_array_equal(rs.cpu().numpy(), rs_ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2560, 2560), (1, 6912, 640), (3, 13, 40), (4, 100, 33), (8, 2560, 512),
+                                   (2, 6912, 2560)])
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_forward_decode_rmsnorm_parity(M, K, N, src):
+    if not bl.decode_fits(M, K):
+        pytest.skip("rows do not fit the fused kernel's LDS")
+    x, xf = norm_inputs(M, K, src, seed=M * 17 + K + N)
+    w = workloads.gen_weights(N, K, seed=N + 7)
+    beta = oracle.absmean(w)
+    q, ds, _ = oracle.quant_act(oracle.rmsnorm(xf))
+    acc_ref = oracle.matmul_i32(q, oracle.ternarize(w, beta), threads=8)
+    packed, wb = bl.pack_weights(torch.from_numpy(w).to(DEV))
+    acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    bl.bitlinear_forward_decode(x, packed, wb, N, acc, rmsnorm=True)
+    y = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    bl.bitlinear_forward_decode(x, packed, wb, N, y, rmsnorm=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    assert_f32_parity(y.cpu().numpy(), oracle.dequant(acc_ref, ds, beta))
+
+
 # ------------------------------------------------ residual sum in the epilogue
 def oracle_linear_f32(x, w):
     beta = oracle.absmean(w)
@@ -127,9 +177,11 @@ def oracle_layer(x, L, cache):
         beta, t = cache[name]
         q, ds, _ = oracle.quant_act(inp)
         return oracle.dequant(oracle.matmul_i32(q, t, threads=8), ds, beta)
-    q, k, v = lin(x, "q"), lin(x, "k"), lin(x, "v")
+    xn = oracle.rmsnorm(x)
+    q, k, v = lin(xn, "q"), lin(xn, "k"), lin(xn, "v")
     x = oracle.add_f32(x, lin(q, "o"))
-    h = oracle.relu2_mul(lin(x, "gate"), lin(x, "up"))
+    xn = oracle.rmsnorm(x)
+    h = oracle.relu2_mul(lin(xn, "gate"), lin(xn, "up"))
     x = oracle.add_f32(x, lin(h, "down"))
     return x, {"q": q, "k": k, "v": v, "h": h}
 
