@@ -1,6 +1,8 @@
 """Benchmark of the BitLinear forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+    python bench.py --counters            (run under rocprofv3 --pmc, see below)
+    python bench.py --counter-summary FETCH_CSV WRITE_CSV
 
 Headline workload: decode GEMV at batch 1 on the 2B-class shapes, K=2560 ->
 N=6912 and K=6912 -> N=2560, bf16 activations with 1% x20 outliers.  One step
@@ -19,6 +21,14 @@ Also printed on the same JSON line:
                 graph of back-to-back launches), against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) running the same
                 step on the host cores, on a bounded number of repetitions;
+  roofline.traffic  measured HBM bytes per launch of the same kernel, from two
+                rocprofv3 --pmc runs of `bench.py --counters` (FETCH_SIZE, then
+                WRITE_SIZE, KiB per dispatch), each scaled by the factor that
+                makes the same counter read the known size of a 64 MiB device
+                copy in the same run; `--counter-summary` turns the two CSV
+                files into profiles/traffic_gemv_fused_decode_2b_m1.txt, which
+                records a hash of the kernel sources; the field is null when
+                the sources have changed since;
   also          the other workloads: one decode step over the 30-layer 2B-class
                 stack (210 BitLinears + glue, batch 1 and 8) in tokens/s,
                 checked bit for bit against the oracle's chain; 100B-class
@@ -28,6 +38,8 @@ Also printed on the same JSON line:
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +51,10 @@ import torch
 import bitlinear_matmul_02_amd as bl
 import workloads
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_fused_decode_2b_m1.txt")
+KERNEL_SOURCES = ("bitlinear_matmul_02_amd/csrc/gemv.hip", "bitlinear_matmul_02_amd/csrc/bl_internal.h")
+CAL_BYTES = 64 << 20  # calibration copy
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 MALL_BYTES = 256 << 20
@@ -51,6 +67,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--counters", action="store_true",
+                    help="launch the headline kernels and a calibration copy for rocprofv3 --pmc, then exit")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two rocprofv3 --pmc CSV files, then exit")
     return ap.parse_args()
 
 
@@ -209,10 +229,129 @@ def headline(args, dev):
         "unfused_us_per_step": round(el_split / args.steps * 1e6, 2),
         "kernel_us": {"%dx%d->%d" % (L.M, L.K, L.N): round(d * 1e6, 3) for L, d in zip(linears, durs)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "gemv_t2_kernel (fused quantization)", "bytes_per_launch": bytes_per},
     }
     return out, host, wl
+
+
+# ------------------------------------------------------- HBM traffic counters
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def headline_linears(dev, R):
+    wl = workloads.DECODE_2B
+    out = []
+    for i, lin in enumerate(wl.linears):
+        w = workloads.gen_weights(lin.N, lin.K, seed=2 * i)
+        xb = workloads.gen_acts_bf16(lin.M, lin.K, seed=2 * i + 1, outliers=lin.outliers)
+        packed, beta = pack_from_host(w, dev)
+        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        out.append(Linear(lin.M, lin.K, lin.N, copies_of(packed, R), beta, x))
+    return out
+
+
+def counters_run(dev):
+    """Dispatches for counter collection: a 64 MiB device copy (calibration),
+    then each headline kernel COUNTER_LAUNCHES times over rotating weight copies."""
+    launches = COUNTER_LAUNCHES
+    src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    linears = headline_linears(dev, rotation(sum(l.N * l.K // 4 for l in workloads.DECODE_2B.linears)))
+    for L in linears:
+        for i in range(launches):
+            L.run_product(i)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": [L.traffic_bytes() for L in linears]}), flush=True)
+
+
+def _counter_rows(path, counter):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    return sorted(rows)
+
+
+COUNTER_LAUNCHES = 16  # dispatches per headline shape in counters_run, in workload order
+
+
+def counter_summary(fetch_csv, write_csv):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the calibration copy
+    and write the per-launch HBM traffic of the headline kernels."""
+    lins = workloads.DECODE_2B.linears
+    labels = ["%dx%d->%d" % (l.M, l.K, l.N) for l in lins]
+    algo = [l.N * l.K // 4 + l.M * l.K * 2 + l.M * l.N * 4 for l in lins]  # packed + bf16 x + fp32 y
+    factors, med, names = {}, {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        cal = [v for _, name, _, v in rows if "copyBuffer" in name and v * 1024 > CAL_BYTES / 4]
+        if not cal:
+            raise SystemExit("no calibration copy dispatch in %s" % path)
+        factors[counter] = CAL_BYTES / (float(np.median(cal)) * 1024)
+        gemv = [(name, grid, v) for _, name, grid, v in rows if "gemv_t2_kernel" in name]
+        if len(gemv) != COUNTER_LAUNCHES * len(lins):
+            raise SystemExit("expected %d kernel dispatches in %s, found %d" % (COUNTER_LAUNCHES * len(lins), path, len(gemv)))
+        for i in range(len(lins)):
+            part = gemv[i * COUNTER_LAUNCHES:(i + 1) * COUNTER_LAUNCHES]
+            med[(counter, i)] = float(np.median([v for _, _, v in part]))
+            names[i] = (part[0][0].split("(GemvArgs")[0].replace("void ", "").replace("(anonymous namespace)::", ""),
+                        part[0][1])
+    lines, traffic = [], []
+    for i, lab in enumerate(labels):
+        rd = med[("FETCH_SIZE", i)] * 1024 * factors["FETCH_SIZE"]
+        wr = med[("WRITE_SIZE", i)] * 1024 * factors["WRITE_SIZE"]
+        traffic.append(rd + wr)
+        lines.append("%-14s %s grid=%d threads: FETCH_SIZE %.1f KiB, WRITE_SIZE %.1f KiB (median of %d dispatches)"
+                     % (lab, names[i][0], names[i][1], med[("FETCH_SIZE", i)], med[("WRITE_SIZE", i)], COUNTER_LAUNCHES))
+        lines.append("%-14s -> read %.0f B + write %.0f B = %.0f B per launch; algorithmic %d B; ratio %.3f"
+                     % ("", rd, wr, rd + wr, algo[i], (rd + wr) / algo[i]))
+    mean = sum(traffic) / len(traffic)
+    text = [
+        "HBM traffic of the fused decode kernel (gemv_t2_kernel, fused quantization), 2B-class shapes, batch 1",
+        "",
+        "commands (run from the repository root on one MI355X):",
+        "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python bench.py --counters",
+        "  rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o run -- python bench.py --counters",
+        "  python bench.py --counter-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
+        "gpurun_out/pmc_write/run_counter_collection.csv",
+        "",
+        "calibration: a 64 MiB device copy (__amd_rocclr_copyBuffer) in the same run;",
+        "  FETCH_SIZE factor %.5f (the counter reads %.0f KiB for 65536 KiB moved)" % (factors["FETCH_SIZE"], 65536 / factors["FETCH_SIZE"]),
+        "  WRITE_SIZE factor %.5f" % factors["WRITE_SIZE"],
+        "",
+    ] + lines + [
+        "",
+        "traffic_bytes_per_launch_mean = %.0f" % mean,
+        "kernel_source_hash = %s" % kernel_source_hash(),
+    ]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def measured_traffic():
+    """Mean measured HBM bytes per launch of the headline kernel, or None when
+    the summary is missing or older than the kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(l.split(" = ", 1) for l in f.read().splitlines() if " = " in l)
+    except OSError:
+        return None
+    if kv.get("kernel_source_hash", "").strip() != kernel_source_hash():
+        return None
+    return round(float(kv["traffic_bytes_per_launch_mean"]))
 
 
 def cpu_baseline(host, wl, budget_s=10.0):
@@ -377,6 +516,9 @@ def prefill_extra(M, shapes, dev, reps=20):
 
 def main():
     args = parse()
+    if args.counter_summary:
+        counter_summary(*args.counter_summary)
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (the path has no sharding or collectives); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -387,6 +529,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     bl.lib()
+    if args.counters:
+        counters_run(dev)
+        return
 
     head, host, wl = headline(args, dev)
     result = {
