@@ -12,6 +12,10 @@ Functions carry the C names:
     bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None)
     bitlinear_forward_decode(x, packed, w_beta, N, y)
     bitlinear_relu2_mul(g, u, h)
+    bitlinear_gemv_multi(x_q, x_ds, K, packed_list, beta_list, N_list, y_list)
+    bitlinear_forward_decode_multi(x, packed_list, beta_list, N_list, y_list)
+    bitlinear_gemv_glu(x_q, x_ds, K, packed_gate, beta_gate, packed_up, beta_up, N, h)
+    bitlinear_forward_decode_glu(x, packed_gate, beta_gate, packed_up, beta_up, N, h)
 An fp32 output tensor can be passed with ``accumulate=True`` to the product
 calls, which then add their result into it (``BITLINEAR_F32_ADD``); the calls
 that quantize activations take ``rmsnorm=True`` to RMS-normalize each row
@@ -40,7 +44,10 @@ EXPORTS = (
     "bitlinear_pack_workspace_bytes", "bitlinear_gemv_workspace_bytes",
     "bitlinear_gemm_workspace_bytes", "bitlinear_quant_act", "bitlinear_pack_weights",
     "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode", "bitlinear_relu2_mul",
+    "bitlinear_gemv_multi", "bitlinear_forward_decode_multi", "bitlinear_gemv_glu",
+    "bitlinear_forward_decode_glu",
 )
+MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
 
 _DTYPE = {torch.float32: F32, torch.bfloat16: BF16, torch.int32: I32}
@@ -89,6 +96,14 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_forward_decode.argtypes = [p, i32, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_relu2_mul.restype = i32
     L.bitlinear_relu2_mul.argtypes = [p, p, i64, p, p]
+    L.bitlinear_gemv_multi.restype = i32
+    L.bitlinear_gemv_multi.argtypes = [p, p, i64, i64, i32, p, p, p, p, i32, p]
+    L.bitlinear_forward_decode_multi.restype = i32
+    L.bitlinear_forward_decode_multi.argtypes = [p, i32, i64, i64, i32, p, p, p, p, i32, p]
+    L.bitlinear_gemv_glu.restype = i32
+    L.bitlinear_gemv_glu.argtypes = [p, p, i64, i64, p, p, p, p, i64, p, p]
+    L.bitlinear_forward_decode_glu.restype = i32
+    L.bitlinear_forward_decode_glu.argtypes = [p, i32, i64, i64, p, p, p, p, i64, p, p]
     _lib = L
     return L
 
@@ -187,6 +202,56 @@ def bitlinear_forward_decode(x, packed, w_beta, N, y, stream=None, accumulate: b
     M, K = x.shape
     _check(lib().bitlinear_forward_decode(_ptr(x), _xdtype(x, rmsnorm), M, K, _ptr(packed), _ptr(w_beta), N,
                                           _ptr(y), _ydtype(y, accumulate), _stream(stream)))
+
+
+def _arrays(packed, w_beta, N, y, accumulate):
+    count = len(packed)
+    if not (count == len(w_beta) == len(N) == len(y)):
+        raise BitLinearError(ERR_ARG, "multi: lists of different lengths")
+    if len({t.dtype for t in y}) != 1:
+        raise BitLinearError(ERR_ARG, "multi: outputs must share one dtype")
+    vp = ctypes.c_void_p * count
+    return (count, vp(*[t.data_ptr() for t in packed]), vp(*[t.data_ptr() for t in w_beta]),
+            (ctypes.c_int64 * count)(*[int(n) for n in N]), vp(*[t.data_ptr() for t in y]),
+            _ydtype(y[0], accumulate))
+
+
+def bitlinear_gemv_multi(x_q, x_ds, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
+    """y[i] (+)= dequant(x_q . T_i^T) for several BitLinears on one input, one launch."""
+    count, pp, bp, nn, yp, ydt = _arrays(packed, w_beta, N, y, accumulate)
+    _check(lib().bitlinear_gemv_multi(_ptr(x_q), _ptr(x_ds), x_ds.shape[0], K, count, pp, bp, nn, yp, ydt,
+                                      _stream(stream)))
+
+
+def bitlinear_forward_decode_multi(x, packed, w_beta, N, y, stream=None, accumulate: bool = False,
+                                   rmsnorm: bool = False) -> None:
+    """The same with the activation quantization fused (x bf16 / fp32)."""
+    M, K = x.shape
+    count, pp, bp, nn, yp, ydt = _arrays(packed, w_beta, N, y, accumulate)
+    _check(lib().bitlinear_forward_decode_multi(_ptr(x), _xdtype(x, rmsnorm), M, K, count, pp, bp, nn, yp, ydt,
+                                                _stream(stream)))
+
+
+def _glu_out(h):
+    if h.dtype != torch.float32:
+        raise BitLinearError(ERR_ARG, "glu: h must be fp32")
+
+
+def bitlinear_gemv_glu(x_q, x_ds, K, packed_gate, beta_gate, packed_up, beta_up, N, h, stream=None) -> None:
+    """h = ReLU(BL_gate)^2 * BL_up on quantized activations, one launch."""
+    _glu_out(h)
+    _check(lib().bitlinear_gemv_glu(_ptr(x_q), _ptr(x_ds), x_ds.shape[0], K, _ptr(packed_gate), _ptr(beta_gate),
+                                    _ptr(packed_up), _ptr(beta_up), N, _ptr(h), _stream(stream)))
+
+
+def bitlinear_forward_decode_glu(x, packed_gate, beta_gate, packed_up, beta_up, N, h, stream=None,
+                                 rmsnorm: bool = False) -> None:
+    """The same with the activation quantization fused (x bf16 / fp32)."""
+    _glu_out(h)
+    M, K = x.shape
+    _check(lib().bitlinear_forward_decode_glu(_ptr(x), _xdtype(x, rmsnorm), M, K, _ptr(packed_gate),
+                                              _ptr(beta_gate), _ptr(packed_up), _ptr(beta_up), N, _ptr(h),
+                                              _stream(stream)))
 
 
 def bitlinear_relu2_mul(g, u, h, stream=None) -> None:

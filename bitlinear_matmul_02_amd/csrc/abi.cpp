@@ -176,6 +176,110 @@ int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, c
                     fn);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks of one multi / gated call; x_q/x_ds (product) or x (fused) are
+// checked by the caller.
+int check_multi(const char* fn, int64_t M, int64_t K, int count, const void* const* packed,
+                const float* const* w_beta, const int64_t* N, void* const* y, int y_dtype) {
+  if (!packed || !w_beta || !N || !y) return fail(BITLINEAR_ERR_ARG, "%s: null array argument", fn);
+  if (count < 1 || count > BITLINEAR_MULTI_MAX)
+    return fail(BITLINEAR_ERR_ARG, "%s: count %d outside [1, %d]", fn, count, BITLINEAR_MULTI_MAX);
+  for (int i = 0; i < count; ++i) {
+    int st = check_common(fn, M, BITLINEAR_GEMV_MAX_M, K, packed[i], w_beta[i], N[i], y[i], y_dtype);
+    if (st != BITLINEAR_OK) return st;
+  }
+  return BITLINEAR_OK;
+}
+
+int check_x(const char* fn, const void* x, int x_dtype, int64_t M, int64_t K) {
+  const int x_base = x_dtype & ~BITLINEAR_X_RMSNORM;
+  if (x_base != BITLINEAR_BF16 && x_base != BITLINEAR_F32)
+    return fail(BITLINEAR_ERR_ARG, "%s: x_dtype must be BITLINEAR_BF16 or BITLINEAR_F32 (| BITLINEAR_X_RMSNORM)", fn);
+  if (M == 0) return BITLINEAR_OK;
+  if (!x) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x, x_base == BITLINEAR_BF16 ? 2 : 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x not element aligned", fn);
+  if (!bl::decode_fused_fits(M, K))
+    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (act_stride(K) + 16) = %lld exceeds %d bytes", fn,
+                (long long)(M * (act_stride(K) + 16)), BITLINEAR_DECODE_MAX_ACT_BYTES);
+  return BITLINEAR_OK;
+}
+
+int check_q(const char* fn, const int8_t* x_q, const float* x_ds, int64_t M) {
+  if (M == 0) return BITLINEAR_OK;
+  if (!x_q || !x_ds) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(x_q, 16) || !aligned(x_ds, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_q must be 16-byte aligned", fn);
+  return BITLINEAR_OK;
+}
+
+const uint8_t* const* as_bytes(const void* const* p) { return reinterpret_cast<const uint8_t* const*>(p); }
+
+}  // namespace
+
+extern "C" {
+
+int bitlinear_gemv_multi(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, int count,
+                         const void* const* packed, const float* const* w_beta, const int64_t* N, void* const* y,
+                         int y_dtype, void* stream) {
+  const char* fn = "bitlinear_gemv_multi";
+  int st = check_multi(fn, M, K, count, packed, w_beta, N, y, y_dtype);
+  if (st == BITLINEAR_OK) st = check_q(fn, x_q, x_ds, M);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  return hip_status(bl::launch_gemv_multi(x_q, act_stride(K), x_ds, M, K, count, as_bytes(packed), w_beta, N, y,
+                                          y_dtype, false, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_forward_decode_multi(const void* x, int x_dtype, int64_t M, int64_t K, int count,
+                                   const void* const* packed, const float* const* w_beta, const int64_t* N,
+                                   void* const* y, int y_dtype, void* stream) {
+  const char* fn = "bitlinear_forward_decode_multi";
+  int st = check_multi(fn, M, K, count, packed, w_beta, N, y, y_dtype);
+  if (st == BITLINEAR_OK) st = check_x(fn, x, x_dtype, M, K);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  return hip_status(bl::launch_decode_multi(x, x_dtype, M, K, count, as_bytes(packed), w_beta, N, y, y_dtype,
+                                            false, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_gemv_glu(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed_gate,
+                       const float* beta_gate, const void* packed_up, const float* beta_up, int64_t N, float* h,
+                       void* stream) {
+  const char* fn = "bitlinear_gemv_glu";
+  const void* packed[2] = {packed_gate, packed_up};
+  const float* beta[2] = {beta_gate, beta_up};
+  const int64_t n2[2] = {N, N};
+  void* y[2] = {h, h};
+  int st = check_multi(fn, M, K, 2, packed, beta, n2, y, BITLINEAR_F32);
+  if (st == BITLINEAR_OK) st = check_q(fn, x_q, x_ds, M);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  return hip_status(bl::launch_gemv_multi(x_q, act_stride(K), x_ds, M, K, 2, as_bytes(packed), beta, n2, y,
+                                          BITLINEAR_F32, true, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_forward_decode_glu(const void* x, int x_dtype, int64_t M, int64_t K, const void* packed_gate,
+                                 const float* beta_gate, const void* packed_up, const float* beta_up, int64_t N,
+                                 float* h, void* stream) {
+  const char* fn = "bitlinear_forward_decode_glu";
+  const void* packed[2] = {packed_gate, packed_up};
+  const float* beta[2] = {beta_gate, beta_up};
+  const int64_t n2[2] = {N, N};
+  void* y[2] = {h, h};
+  int st = check_multi(fn, M, K, 2, packed, beta, n2, y, BITLINEAR_F32);
+  if (st == BITLINEAR_OK) st = check_x(fn, x, x_dtype, M, K);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  return hip_status(bl::launch_decode_multi(x, x_dtype, M, K, 2, as_bytes(packed), beta, n2, y, BITLINEAR_F32,
+                                            true, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_relu2_mul(const float* g, const float* u, int64_t count, float* h, void* stream) {
   const char* fn = "bitlinear_relu2_mul";
   if (count < 0) return fail(BITLINEAR_ERR_SHAPE, "%s: count %lld < 0", fn, (long long)count);

@@ -19,6 +19,7 @@ constexpr int kBetaChunk = 4096;
 // act_stride(K) + 16 bytes); with its 4 KB reduction buffer it stays < 64 KB.
 constexpr int64_t kDecodeLdsBytes = BITLINEAR_DECODE_MAX_ACT_BYTES;
 constexpr int kXDtypeMask = BITLINEAR_X_RMSNORM - 1;  // x_dtype without its flags
+constexpr int kGemvMaxSeg = BITLINEAR_MULTI_MAX;       // BitLinears per multi launch
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -50,6 +51,13 @@ int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s);
+
+hipError_t launch_gemv_multi(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, int count,
+                             const uint8_t* const* packed, const float* const* beta, const int64_t* N, void* const* y,
+                             int y_dtype, bool glu, hipStream_t s);
+hipError_t launch_decode_multi(const void* x, int x_dtype, int64_t M, int64_t K, int count,
+                               const uint8_t* const* packed, const float* const* beta, const int64_t* N,
+                               void* const* y, int y_dtype, bool glu, hipStream_t s);
 
 hipError_t launch_relu2_mul(const float* g, const float* u, int64_t count, float* h, hipStream_t s);
 

@@ -35,6 +35,16 @@
 //           NB weight tiles of a k-tile.
 // In every mode the first weight tiles are requested before the activations.
 //
+// One launch can serve several BitLinears that read the same activations
+// (segments: e.g. the q, k and v projections of a decoder layer): the output
+// groups of all segments form one grid, and each workgroup finds its segment
+// from the group index.  A gated pair (gate and up projections of the same
+// shape) runs with NB = 2, tile j = 0 from the gate and j = 1 from the up
+// matrix at the same rows, and its epilogue writes h = ReLU(y_gate)^2 * y_up
+// ("Key Technologies Enabling the BitNET Family", Architectural Innovations
+// and Optimizations: squared ReLU in the feed-forward layers) instead of the
+// two outputs.
+//
 // Tiny outputs with a long K (AGLOBAL only) also split K across workgroups:
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
@@ -72,7 +82,7 @@ struct GemvPlan {
   int64_t ws_acc_bytes, ws_bytes;
 };
 
-GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse) {
+GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split = true) {
   GemvPlan p{};
   p.MB = (int)ceil_div(M < 1 ? 1 : M, 16);
   p.Nt = (int)ceil_div(N, kTileN);
@@ -102,7 +112,7 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse) {
   p.tps = (int)ceil_div(p.Kt, waves);
   p.waves = (int)ceil_div(p.Kt, p.tps);
   p.SB = 1;
-  if (p.amode == AGLOBAL && p.Ng < 64 && p.tps >= 16) {
+  if (allow_split && p.amode == AGLOBAL && p.Ng < 64 && p.tps >= 16) {
     // tiny output, long K: split K across workgroups too
     int64_t cap = 512 / p.Ng;
     if (cap < 2) cap = 2;
@@ -118,6 +128,14 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse) {
   return p;
 }
 
+struct GemvSeg {
+  const u4* packed;
+  const float* beta;
+  void* y;
+  int N, Nt;
+  int g0;  // first output group of the segment in the grid
+};
+
 struct GemvArgs {
   const int8_t* q;  // [M][ldq] int8 (modes AGLOBAL, ALDS_Q)
   const void* x;    // [M][K] bf16/fp32 activations (mode ALDS_X)
@@ -125,11 +143,11 @@ struct GemvArgs {
   int x_vec;        // ALDS_X: rows can be read in 16-byte pieces
   int norm;         // fused modes: RMS-normalize each row before quantizing
   const float* ds;  // [M] (modes AGLOBAL, ALDS_Q)
-  int M, K, N, Nt, Kt, tps, SB;
+  int M, K, Kt, tps, SB;
   int64_t ldq, ldl;
-  const u4* packed;
-  const float* beta;
-  void* y;
+  GemvSeg seg[kGemvMaxSeg];
+  int nseg;         // segments in use (1 for a single BitLinear)
+  int glu;          // gated pair: seg[0] gate, seg[1] up, h into seg[0].y
   int y_dtype;
   int32_t* ws_acc;
   uint32_t* ws_cnt;
@@ -427,7 +445,11 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   const int split = sb * waves + wave;
   const int k0 = split * a.tps;
   const int k1 = min(k0 + a.tps, a.Kt);
-  const int nb0 = grp * NB;
+  int si = 0;  // segment of this workgroup (uniform)
+  for (int i = 1; i < a.nseg; ++i) si = grp >= a.seg[i].g0 ? i : si;
+  const GemvSeg sg = a.seg[si];
+  const int lg = grp - sg.g0;                // output group within the segment
+  const int nb0 = a.glu ? lg : lg * NB;      // first 16-row output block
   const int r16 = lane & 15, g4 = lane >> 4;
   const int M = a.M;
 
@@ -440,8 +462,10 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   const u4* bptr[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int nb = min(nb0 + j, a.Nt - 1);  // blocks past Nt are masked at the store
-    bptr[j] = a.packed + (int64_t)nb * a.Kt * 64 + lane;
+    // blocks past Nt are masked at the store; a gated pair reads block nb0
+    // of the gate (j = 0) and of the up matrix (j = 1)
+    const int nb = min(a.glu ? nb0 : nb0 + j, sg.Nt - 1);
+    bptr[j] = (a.glu ? a.seg[j].packed : sg.packed) + (int64_t)nb * a.Kt * 64 + lane;
   }
   // Activation operand rows.  Lanes of token rows >= M read row M-1 instead:
   // their accumulators are never stored, so the loads need no branch.
@@ -580,7 +604,25 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
 
   // ---- dequantize and store: lane holds rows 4*g4 + r of each token block,
   //      column r16 of each output block
-  const float bt = *a.beta;
+  if (a.glu) {
+    // h = (r * r) * y_up with r = max(y_gate, +0), each y dequantized as below
+    const float bg = *a.seg[0].beta, bu = *a.seg[1].beta;
+    const int n = nb0 * kTileN + r16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mb * 16 + 4 * g4 + r;
+        if (m >= M || n >= sg.N) continue;
+        const float dsm = FUSED ? row_g[m] / 127.0f : a.ds[m];
+        const float yg = (float)(acc[mb][0][r] >> 6) * (dsm * bg);
+        const float yu = (float)(acc[mb][NB - 1][r] >> 6) * (dsm * bu);
+        const float rg = yg > 0.0f ? yg : 0.0f;
+        static_cast<float*>(sg.y)[(int64_t)m * sg.N + n] = __fmul_rn(__fmul_rn(rg, rg), yu);
+      }
+    return;
+  }
+  const float bt = *sg.beta;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -592,16 +634,16 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int n = (nb0 + j) * kTileN + r16;
-        if (n < a.N) store_out(a.y, a.y_dtype, (int64_t)m * a.N + n, acc[mb][j][r], scale);
+        if (n < sg.N) store_out(sg.y, a.y_dtype, (int64_t)m * sg.N + n, acc[mb][j][r], scale);
       }
     }
 }
 
 template <int MB, int NB, int AM, bool NORM>
 hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
-  if constexpr (AM == ALDS_X || AM == ALDS_XS) {
-    // static LDS of the fused modes plus the largest activation rows can pass
-    // the default 64 KB per workgroup: raise the limit once
+  if constexpr (AM != AGLOBAL) {
+    // static LDS plus the largest activation rows can pass the default 64 KB
+    // per workgroup: raise the limit once
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
@@ -626,11 +668,9 @@ hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   BL_GEMV_CASE(2, 2);
   BL_GEMV_CASE(3, 1);
   BL_GEMV_CASE(4, 1);
-  if constexpr (AM == AGLOBAL) {
-    BL_GEMV_CASE(3, 2);
-    BL_GEMV_CASE(4, 2);
-    BL_GEMV_CASE(2, 4);
-  }
+  BL_GEMV_CASE(3, 2);  // AGLOBAL, and gated pairs in every mode
+  BL_GEMV_CASE(4, 2);
+  if constexpr (AM == AGLOBAL) BL_GEMV_CASE(2, 4);
 #undef BL_GEMV_CASE
   return hipErrorInvalidValue;
 }
@@ -650,16 +690,13 @@ GemvArgs make_args(const GemvPlan& p, int64_t M, int64_t K, int64_t N, const uin
   GemvArgs a{};
   a.M = (int)M;
   a.K = (int)K;
-  a.N = (int)N;
-  a.Nt = p.Nt;
   a.Kt = p.Kt;
   a.tps = p.tps;
   a.SB = p.SB;
   a.ldq = (int64_t)p.Kt * kTileK;
   a.ldl = lds_row(K);
-  a.packed = reinterpret_cast<const u4*>(packed);
-  a.beta = beta;
-  a.y = y;
+  a.nseg = 1;
+  a.seg[0] = GemvSeg{reinterpret_cast<const u4*>(packed), beta, y, (int)N, p.Nt, 0};
   a.y_dtype = y_dtype;
   if (p.SB > 1) {
     a.ws_acc = static_cast<int32_t*>(ws);
@@ -668,7 +705,60 @@ GemvArgs make_args(const GemvPlan& p, int64_t M, int64_t K, int64_t N, const uin
   return a;
 }
 
+// Plan and arguments for several segments (glu: exactly two of one shape).
+// The plan is the single-matrix plan for the summed output rows (one per
+// matrix for a gated pair), without any K split across workgroups.
+bool make_multi(int64_t M, int64_t K, int count, const uint8_t* const* packed, const float* const* beta,
+                const int64_t* N, void* const* y, int y_dtype, bool glu, bool fuse, GemvPlan& p, GemvArgs& a) {
+  if (count < 1 || count > kGemvMaxSeg || (glu && (count != 2 || N[0] != N[1]))) return false;
+  int64_t ntot = 0;
+  for (int i = 0; i < count; ++i) ntot += N[i];
+  p = make_plan(M, glu ? N[0] : ntot, K, fuse, false);
+  if (glu) p.NB = 2;
+  a = make_args(p, M, K, N[0], packed[0], beta[0], y[0], y_dtype, nullptr);
+  a.nseg = count;
+  a.glu = glu;
+  int g = 0;
+  for (int i = 0; i < count; ++i) {
+    const int Nt = (int)ceil_div(N[i], kTileN);
+    a.seg[i] = GemvSeg{reinterpret_cast<const u4*>(packed[i]), beta[i], y[i], (int)N[i], Nt, g};
+    if (!glu) g += (int)ceil_div(Nt, p.NB);
+  }
+  p.Ng = glu ? a.seg[0].Nt : g;
+  return true;
+}
+
+void set_x(GemvArgs& a, const void* x, int x_dtype, int64_t K) {
+  a.x = x;
+  a.x_dtype = x_dtype & kXDtypeMask;
+  a.norm = (x_dtype & BITLINEAR_X_RMSNORM) != 0;
+  const int per16 = a.x_dtype == BITLINEAR_BF16 ? 8 : 4;
+  a.x_vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+}
+
 }  // namespace
+
+hipError_t launch_gemv_multi(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, int count,
+                             const uint8_t* const* packed, const float* const* beta, const int64_t* N, void* const* y,
+                             int y_dtype, bool glu, hipStream_t s) {
+  GemvPlan p;
+  GemvArgs a;
+  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, false, p, a)) return hipErrorInvalidValue;
+  a.q = q;
+  a.ldq = ldq;
+  a.ds = ds;
+  return dispatch(p, a, s);
+}
+
+hipError_t launch_decode_multi(const void* x, int x_dtype, int64_t M, int64_t K, int count,
+                               const uint8_t* const* packed, const float* const* beta, const int64_t* N,
+                               void* const* y, int y_dtype, bool glu, hipStream_t s) {
+  GemvPlan p;
+  GemvArgs a;
+  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, true, p, a)) return hipErrorInvalidValue;
+  set_x(a, x, x_dtype, K);
+  return dispatch(p, a, s);
+}
 
 int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, false).ws_bytes; }
 
@@ -691,11 +781,7 @@ hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, co
                             const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
   const GemvPlan p = make_plan(M, N, K, true);
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr);
-  a.x = x;
-  a.x_dtype = x_dtype & kXDtypeMask;
-  a.norm = (x_dtype & BITLINEAR_X_RMSNORM) != 0;
-  const int per16 = a.x_dtype == BITLINEAR_BF16 ? 8 : 4;
-  a.x_vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  set_x(a, x, x_dtype, K);
   return dispatch(p, a, s);
 }
 

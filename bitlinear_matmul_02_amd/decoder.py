@@ -18,19 +18,23 @@ The normalization is fused into the BitLinears' activation quantization
 (``rmsnorm``), so N(x) is never written out.
 
 Everything is enqueued on one stream by the library's kernels and allocates
-nothing after construction, so a step can be captured in a HIP graph.  For at
-most ``FUSED_MAX_M`` tokens each BitLinear is one fused launch (quantization
-in the product's prologue); beyond that the input is quantized once and
-shared by the BitLinears that read it.  The residual sums are fused into the
-o / down products' epilogues (``accumulate``).
+nothing after construction, so a step can be captured in a HIP graph.  Up to
+64 tokens a layer is four products: q/k/v in one multi launch, o with the
+residual sum fused into its epilogue (``accumulate``), gate/up as one gated
+launch that writes h directly, and down, again accumulating into x.  For at
+most ``FUSED_MAX_M`` tokens the activation quantization (and normalization)
+runs inside each product's prologue, so a layer is four launches; beyond that
+each input is quantized once by its own launch.  Past 64 tokens the products
+run on the matrix-core GEMM, one BitLinear per launch.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (GEMV_MAX_M, act_stride, bitlinear_forward_decode, bitlinear_gemm, bitlinear_gemv,
-               bitlinear_quant_act, bitlinear_relu2_mul, decode_fits, gemm_workspace_bytes,
-               gemv_workspace_bytes)
+from . import (GEMV_MAX_M, act_stride, bitlinear_forward_decode, bitlinear_forward_decode_glu,
+               bitlinear_forward_decode_multi, bitlinear_gemm, bitlinear_gemv, bitlinear_gemv_glu,
+               bitlinear_gemv_multi, bitlinear_quant_act, bitlinear_relu2_mul, decode_fits,
+               gemm_workspace_bytes, gemv_workspace_bytes)
 
 NAMES = ("q", "k", "v", "o", "gate", "up", "down")
 FUSED_MAX_M = 4
@@ -88,10 +92,29 @@ class DecoderStack:
 
     def layer(self, i: int, x: torch.Tensor, stream=None) -> None:
         L = self.layers[i]
-        self._linears(x, (L["q"], L["k"], L["v"]), (self.q, self.k, self.v), False, stream, rmsnorm=True)
+        if not self.gemv:  # prefill-sized batches: one GEMM per BitLinear
+            self._linears(x, (L["q"], L["k"], L["v"]), (self.q, self.k, self.v), False, stream, rmsnorm=True)
+            self._linears(self.q, (L["o"],), (x,), True, stream)
+            self._linears(x, (L["gate"], L["up"]), (self.g, self.u), False, stream, rmsnorm=True)
+            bitlinear_relu2_mul(self.g, self.u, self.h, stream)
+            self._linears(self.h, (L["down"],), (x,), True, stream)
+            return
+        qkv = [L[n] for n in ("q", "k", "v")]
+        g, u = L["gate"], L["up"]
+        if self.fused:
+            bitlinear_forward_decode_multi(x, [l.packed for l in qkv], [l.beta for l in qkv], [l.N for l in qkv],
+                                           [self.q, self.k, self.v], stream, rmsnorm=True)
+            self._linears(self.q, (L["o"],), (x,), True, stream)
+            bitlinear_forward_decode_glu(x, g.packed, g.beta, u.packed, u.beta, g.N, self.h, stream, rmsnorm=True)
+            self._linears(self.h, (L["down"],), (x,), True, stream)
+            return
+        d = self.d
+        bitlinear_quant_act(x, self.xq[d], self.xds[d], None, stream, rmsnorm=True)
+        bitlinear_gemv_multi(self.xq[d], self.xds[d], d, [l.packed for l in qkv], [l.beta for l in qkv],
+                             [l.N for l in qkv], [self.q, self.k, self.v], stream)
         self._linears(self.q, (L["o"],), (x,), True, stream)
-        self._linears(x, (L["gate"], L["up"]), (self.g, self.u), False, stream, rmsnorm=True)
-        bitlinear_relu2_mul(self.g, self.u, self.h, stream)
+        bitlinear_quant_act(x, self.xq[d], self.xds[d], None, stream, rmsnorm=True)
+        bitlinear_gemv_glu(self.xq[d], self.xds[d], d, g.packed, g.beta, u.packed, u.beta, g.N, self.h, stream)
         self._linears(self.h, (L["down"],), (x,), True, stream)
 
     def step(self, x: torch.Tensor, stream=None) -> None:

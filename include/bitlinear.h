@@ -187,6 +187,50 @@ int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
 int bitlinear_forward_decode(const void *x, int x_dtype, int64_t M, int64_t K, const void *packed,
                              const float *w_beta, int64_t N, void *y, int y_dtype, void *stream);
 
+/* Most BitLinears one multi call computes. */
+#define BITLINEAR_MULTI_MAX 4
+
+/*
+ * Several BitLinears that read the same activations, in one launch (e.g. the
+ * q, k and v projections of a decoder layer): y_i = dequant(x_q . T_i^T) for
+ * i < count, each exactly as bitlinear_gemv would compute it.
+ *   count     1 .. BITLINEAR_MULTI_MAX.
+ *   packed, w_beta, N, y  host arrays of count entries (read during the call
+ *             only), each entry as the single-matrix argument of
+ *             bitlinear_gemv; all outputs share y_dtype.
+ * Uses no workspace.  M in [0, BITLINEAR_GEMV_MAX_M].
+ * Errors: ERR_ARG (null array or entry, count out of range), ERR_SHAPE,
+ * ERR_ALIGN, as bitlinear_gemv for every entry.
+ */
+int bitlinear_gemv_multi(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, int count,
+                         const void *const *packed, const float *const *w_beta, const int64_t *N,
+                         void *const *y, int y_dtype, void *stream);
+
+/* The same with the activation quantization fused (as bitlinear_forward_decode). */
+int bitlinear_forward_decode_multi(const void *x, int x_dtype, int64_t M, int64_t K, int count,
+                                   const void *const *packed, const float *const *w_beta,
+                                   const int64_t *N, void *const *y, int y_dtype, void *stream);
+
+/*
+ * Gated feed-forward pair in one launch ("Key Technologies Enabling the BitNET
+ * Family", Architectural Innovations and Optimizations: squared ReLU in the
+ * feed-forward layers): with g = BL_gate(x), u = BL_up(x) (both N x K,
+ * dequantized to fp32 exactly as bitlinear_gemv),
+ *   h[m][n] = (r * r) * u[m][n],  r = g[m][n] if g[m][n] > 0 else +0,
+ * identical to two products followed by bitlinear_relu2_mul; g and u are
+ * never written.  h [M][N] fp32 device output, 4-byte aligned.
+ * Errors as bitlinear_gemv.  Uses no workspace.
+ */
+int bitlinear_gemv_glu(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K,
+                       const void *packed_gate, const float *beta_gate, const void *packed_up,
+                       const float *beta_up, int64_t N, float *h, void *stream);
+
+/* The same with the activation quantization fused (as bitlinear_forward_decode). */
+int bitlinear_forward_decode_glu(const void *x, int x_dtype, int64_t M, int64_t K,
+                                 const void *packed_gate, const float *beta_gate,
+                                 const void *packed_up, const float *beta_up, int64_t N, float *h,
+                                 void *stream);
+
 /*
  * Feed-forward activation between the gate / up and down BitLinears of a
  * decoder layer ("Key Technologies Enabling the BitNET Family", Architectural

@@ -40,6 +40,7 @@ def test_header_constants_match_binding():
     assert int(consts["BITLINEAR_I32"]) == bl.I32
     assert int(consts["BITLINEAR_F32_ADD"]) == bl.F32_ADD
     assert int(consts["BITLINEAR_X_RMSNORM"]) == bl.X_RMSNORM
+    assert int(consts["BITLINEAR_MULTI_MAX"]) == bl.MULTI_MAX
     assert int(consts["BITLINEAR_MAX_K"]) == bl.MAX_K
     assert int(consts["BITLINEAR_GEMV_MAX_M"]) == bl.GEMV_MAX_M
     assert int(consts["BITLINEAR_DECODE_MAX_ACT_BYTES"]) == bl.DECODE_MAX_ACT_BYTES
@@ -195,3 +196,30 @@ def test_rmsnorm_flag_validation():
     # alignment follows the base dtype
     assert L.bitlinear_forward_decode(FAKE + 2, bl.F32 | bl.X_RMSNORM, 1, 256, FAKE, FAKE, 16, FAKE, bl.F32,
                                       None) == bl.ERR_ALIGN
+
+
+def test_multi_and_glu_validation():
+    import ctypes
+    L = bl.lib()
+    vp = ctypes.c_void_p * 4
+    packed, beta, y = vp(FAKE, FAKE, FAKE, FAKE), vp(FAKE, FAKE, FAKE, FAKE), vp(FAKE, FAKE, FAKE, FAKE)
+    N = (ctypes.c_int64 * 4)(16, 16, 16, 16)
+    for fn, lead in ((L.bitlinear_gemv_multi, (FAKE, FAKE)), (L.bitlinear_forward_decode_multi, (FAKE, bl.BF16))):
+        assert fn(*lead, 1, 256, 0, packed, beta, N, y, bl.F32, None) == bl.ERR_ARG
+        assert "count" in bl.last_error()
+        assert fn(*lead, 1, 256, 5, packed, beta, N, y, bl.F32, None) == bl.ERR_ARG
+        assert fn(*lead, 1, 256, 2, None, beta, N, y, bl.F32, None) == bl.ERR_ARG
+        bad = vp(FAKE, None, FAKE, FAKE)
+        assert fn(*lead, 1, 256, 2, bad, beta, N, y, bl.F32, None) == bl.ERR_ARG
+        Nb = (ctypes.c_int64 * 4)(16, 0, 16, 16)
+        assert fn(*lead, 1, 256, 2, packed, beta, Nb, y, bl.F32, None) == bl.ERR_SHAPE
+        assert fn(*lead, 65, 256, 2, packed, beta, N, y, bl.F32, None) == bl.ERR_SHAPE
+        assert fn(*lead, 0, 256, 2, packed, beta, N, y, bl.F32, None) == bl.OK  # empty batch
+    assert L.bitlinear_gemv_multi(None, FAKE, 1, 256, 1, packed, beta, N, y, bl.F32, None) == bl.ERR_ARG
+    assert L.bitlinear_gemv_multi(FAKE + 8, FAKE, 1, 256, 1, packed, beta, N, y, bl.F32, None) == bl.ERR_ALIGN
+    assert L.bitlinear_forward_decode_multi(FAKE, bl.BF16, 8, 8192, 1, packed, beta, N, y, bl.F32,
+                                            None) == bl.ERR_UNSUPPORTED
+    assert L.bitlinear_gemv_glu(FAKE, FAKE, 1, 256, FAKE, FAKE, None, FAKE, 16, FAKE, None) == bl.ERR_ARG
+    assert L.bitlinear_gemv_glu(FAKE, FAKE, 1, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE + 2, None) == bl.ERR_ALIGN
+    assert L.bitlinear_forward_decode_glu(FAKE, bl.I32, 1, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == bl.ERR_ARG
+    assert L.bitlinear_forward_decode_glu(FAKE, bl.BF16, 0, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == bl.OK

@@ -106,6 +106,79 @@ def test_forward_decode_rmsnorm_parity(M, K, N, src):
     assert_f32_parity(y.cpu().numpy(), oracle.dequant(acc_ref, ds, beta))
 
 
+# ------------------------------------------------ several BitLinears / gated pair in one launch
+def oracle_acc_y(xf, w, norm):
+    beta = oracle.absmean(w)
+    q, ds, _ = oracle.quant_act(oracle.rmsnorm(xf) if norm else xf)
+    acc = oracle.matmul_i32(q, oracle.ternarize(w, beta), threads=8)
+    return acc, oracle.dequant(acc, ds, beta)
+
+
+MULTI_CASES = [(1, 2560, (2560, 640, 640)), (3, 700, (40, 333)), (8, 2560, (2560, 640, 640, 16)),
+               (33, 512, (300, 17, 1000)), (64, 256, (64,)), (1, 6912, (2560,)), (5, 13, (7, 40))]
+
+
+@pytest.mark.parametrize("M,K,Ns", MULTI_CASES)
+@pytest.mark.parametrize("path", ["gemv", "fused"])
+def test_multi_parity(M, K, Ns, path):
+    norm = path == "fused" and K >= 256
+    if path == "fused" and not bl.decode_fits(M, K):
+        pytest.skip("rows do not fit the fused kernel's LDS")
+    x, xf = norm_inputs(M, K, "f32", seed=M * 5 + K)
+    ws = [workloads.gen_weights(N, K, seed=N * 3 + i) for i, N in enumerate(Ns)]
+    packs = [bl.pack_weights(torch.from_numpy(w).to(DEV)) for w in ws]
+    for dtype in (torch.int32, torch.float32):
+        ys = [torch.full((M, N), 3.0, dtype=dtype, device=DEV) for N in Ns]
+        if path == "fused":
+            bl.bitlinear_forward_decode_multi(x, [p for p, _ in packs], [b for _, b in packs], Ns, ys, rmsnorm=norm)
+        else:
+            x_q, x_ds = bl.quant_act(x)
+            bl.bitlinear_gemv_multi(x_q, x_ds, K, [p for p, _ in packs], [b for _, b in packs], Ns, ys)
+        torch.cuda.synchronize()
+        for w, y in zip(ws, ys):
+            acc, yr = oracle_acc_y(xf, w, norm)
+            if dtype == torch.int32:
+                np.testing.assert_array_equal(y.cpu().numpy(), acc)
+            else:
+                assert_f32_parity(y.cpu().numpy(), yr)
+
+
+def test_multi_accumulate():
+    M, K, Ns = 2, 2560, (2560, 640)
+    x, xf = norm_inputs(M, K, "f32", seed=9)
+    ws = [workloads.gen_weights(N, K, seed=N + 1) for N in Ns]
+    packs = [bl.pack_weights(torch.from_numpy(w).to(DEV)) for w in ws]
+    rng = np.random.default_rng(3)
+    y0 = [rng.standard_normal((M, N)).astype(np.float32) for N in Ns]
+    ys = [torch.from_numpy(v).to(DEV) for v in y0]
+    bl.bitlinear_forward_decode_multi(x, [p for p, _ in packs], [b for _, b in packs], Ns, ys, accumulate=True)
+    torch.cuda.synchronize()
+    for w, v, y in zip(ws, y0, ys):
+        assert_f32_parity(y.cpu().numpy(), oracle.add_f32(v, oracle_acc_y(xf, w, False)[1]))
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2560, 6912), (3, 700, 333), (8, 2560, 6912), (33, 512, 100), (64, 256, 48),
+                                   (2, 13, 20)])
+@pytest.mark.parametrize("path", ["gemv", "fused"])
+def test_glu_parity(M, K, N, path):
+    norm = path == "fused"
+    if path == "fused" and not bl.decode_fits(M, K):
+        pytest.skip("rows do not fit the fused kernel's LDS")
+    x, xf = norm_inputs(M, K, "f32", seed=M + K + N)
+    wg = workloads.gen_weights(N, K, seed=N + 11)
+    wu = workloads.gen_weights(N, K, seed=N + 12)
+    (pg, bg), (pu, bu) = (bl.pack_weights(torch.from_numpy(w).to(DEV)) for w in (wg, wu))
+    h = torch.full((M, N), 5.0, dtype=torch.float32, device=DEV)
+    if path == "fused":
+        bl.bitlinear_forward_decode_glu(x, pg, bg, pu, bu, N, h, rmsnorm=norm)
+    else:
+        x_q, x_ds = bl.quant_act(x)
+        bl.bitlinear_gemv_glu(x_q, x_ds, K, pg, bg, pu, bu, N, h)
+    torch.cuda.synchronize()
+    ref = oracle.relu2_mul(oracle_acc_y(xf, wg, norm)[1], oracle_acc_y(xf, wu, norm)[1])
+    assert_f32_parity(h.cpu().numpy(), ref)
+
+
 # ------------------------------------------------ residual sum in the epilogue
 def oracle_linear_f32(x, w):
     beta = oracle.absmean(w)
@@ -191,7 +264,7 @@ def two_layers():
     return stack_inputs(2)
 
 
-@pytest.mark.parametrize("M", list(workloads.DECODE_STEP_BATCHES) + [3, 64])
+@pytest.mark.parametrize("M", list(workloads.DECODE_STEP_BATCHES) + [3, 64, 80])
 def test_decode_step_layers_match_oracle(two_layers, M):
     x0 = workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, workloads.D_MODEL, seed=workloads.DECODER_X0_SEED))
     stack = gpu_stack(two_layers, M)
