@@ -57,6 +57,9 @@ namespace bl {
 namespace {
 
 constexpr float kEpsX = 1e-5f;
+// 16-byte activation pieces a thread of a fused launch loads before the
+// weight prefetch and holds in registers until the weight loads are in flight.
+constexpr int kXReg = 8;
 constexpr int kLdsPad = 16;  // bytes added to each LDS activation row
 enum AMode { AGLOBAL = 0, ALDS_Q = 1, ALDS_X = 2, ALDS_XS = 3 };
 
@@ -82,7 +85,9 @@ struct GemvPlan {
   int64_t ws_acc_bytes, ws_bytes;
 };
 
-GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split = true) {
+// xpieces: 16-byte activation pieces of a fused launch whose rows are whole
+// pieces (0 otherwise).
+GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split = true, int64_t xpieces = 0) {
   GemvPlan p{};
   p.MB = (int)ceil_div(M < 1 ? 1 : M, 16);
   p.Nt = (int)ceil_div(N, kTileN);
@@ -107,10 +112,21 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   const int maxw = max_waves(p.MB);
   const int target = p.MB == 1 ? (p.Kt >= 32 ? 16 : 8) : 5;
   int waves = (int)ceil_div(p.Kt, target);
+  if (p.MB == 1 && p.Ng < 512) {
+    // about one workgroup per CU: keep all four SIMDs busy with whole
+    // multiples of four waves (measured on the 2B- and 100B-class shapes)
+    waves = p.Kt < 32 ? 4 : (int)ceil_div(waves, 4) * 4;
+  }
   if (waves > maxw) waves = maxw;
   if (waves < 1) waves = 1;
   p.tps = (int)ceil_div(p.Kt, waves);
   p.waves = (int)ceil_div(p.Kt, p.tps);
+  if (fuse && xpieces > 0) {
+    // enough threads to hold the activation rows in registers; the extra
+    // waves only help with the prologue
+    const int64_t need = ceil_div(xpieces, (int64_t)kXReg * 64);
+    if (p.waves < need) p.waves = (int)(need < maxw ? need : maxw);
+  }
   p.SB = 1;
   if (allow_split && p.amode == AGLOBAL && p.Ng < 64 && p.tps >= 16) {
     // tiny output, long K: split K across workgroups too
@@ -159,9 +175,6 @@ __device__ inline float x_at(const void* x, int dt, int64_t i) {
 }
 
 
-// 16-byte activation pieces a thread loads before the weight prefetch and
-// holds in registers until the weight loads are in flight.
-constexpr int kXReg = 8;
 
 // Staged prologue, part 1 (issued before the weight loads, so that waiting
 // for these pieces never waits for the weight stream): piece c of the
@@ -281,7 +294,8 @@ __device__ inline int piece_row(int c, int M, float inv_cpr) {
   return M == 1 ? 0 : (int)(((float)c + 0.5f) * inv_cpr);
 }
 
-// Part 2 for bf16/fp32 rows (16-byte aligned, K a multiple of the piece):
+// Part 2 for bf16/fp32 rows (16-byte aligned, K a multiple of the piece) that
+// the threads hold entirely in registers (M * K / piece <= kXReg * threads):
 // gamma_m = max |x[m][:]| from the held pieces (per-wave maxima in LDS slots,
 // combined by thread m), then each piece quantized with
 // q = rint(x * (127 / max(gamma, 1e-5))) into LDS.  `slots` holds at least
@@ -296,7 +310,6 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
   const int per16 = bf16 ? 8 : 4;
   const int M = a.M, cpr = a.K / per16, npieces = M * cpr;
   const float inv_cpr = 1.0f / (float)cpr;
-  const u4* src = static_cast<const u4*>(a.x);
   const int64_t Kp = (int64_t)a.Kt * kTileK;
   // zero the padding columns [K, Kp) of every row (4-byte stores)
   const int padw = (int)((Kp - a.K) / 4);
@@ -316,11 +329,6 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
         if (norm) s2 += piece_sumsq(v[r], bf16);
       }
     }
-    for (int c = tid + kXReg * nthr; c < npieces; c += nthr)  // pieces beyond the held ones
-      if (piece_row(c, M, inv_cpr) == m) {
-        amax = max(amax, piece_absmax_bits(src[c], bf16));
-        if (norm) s2 += piece_sumsq(src[c], bf16);
-      }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
     if (lane == 0) slots[wave * M + m] = amax;
@@ -360,7 +368,68 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
     const int c = tid + r * nthr;
     if (c < npieces) quant(v[r], c);
   }
-  for (int c = tid + kXReg * nthr; c < npieces; c += nthr) quant(src[c], c);
+  __syncthreads();
+}
+
+// The same for one token row, with less bookkeeping: the slots a wave holds
+// are skipped by a uniform branch past the last piece, every thread combines
+// the per-wave maxima (and sums of squares) itself, in wave order, so one
+// barrier fewer is needed.
+template <bool NORM>
+__device__ void stage_store_x1(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds, uint32_t* slots, double* sq,
+                               float* row_g, float* row_r) {
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6, waves = nthr >> 6;
+  const bool bf16 = a.x_dtype == BITLINEAR_BF16;
+  const int per16 = bf16 ? 8 : 4;
+  const int npieces = a.K / per16;
+  const int nslots = (npieces + nthr - 1) / nthr;  // uniform
+  const int64_t Kp = (int64_t)a.Kt * kTileK;
+  for (int64_t k = a.K + 4 * (int64_t)tid; k < Kp; k += 4 * nthr) *reinterpret_cast<uint32_t*>(lds + k) = 0u;
+  uint32_t amax = 0;
+  double s2 = 0.0;
+#pragma unroll
+  for (int r = 0; r < kXReg; ++r) {
+    if (r < nslots && tid + r * nthr < npieces) {
+      amax = max(amax, piece_absmax_bits(v[r], bf16));
+      if (NORM) s2 += piece_sumsq(v[r], bf16);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+  if (NORM) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+  }
+  if (lane == 0) {
+    slots[wave] = amax;
+    if (NORM) sq[wave] = s2;
+  }
+  __syncthreads();
+  uint32_t g = 0;
+  for (int w = 0; w < waves; ++w) g = max(g, slots[w]);
+  float gamma = __uint_as_float(g), rn = 1.0f;
+  if (NORM) {
+    double t = 0.0;
+    for (int w = 0; w < waves; ++w) t += sq[w];
+    rn = rms_scale(t, a.K);
+    gamma = __fmul_rn(gamma, rn);
+  }
+  const float gm = fmaxf(gamma, kEpsX);
+  const float qs = 127.0f / gm;  // IEEE division, as the standalone quantizer
+  if (tid == 0) {
+    row_g[0] = gm;
+    if (NORM) row_r[0] = rn;
+  }
+#pragma unroll
+  for (int r = 0; r < kXReg; ++r) {
+    const int c = tid + r * nthr;
+    if (r < nslots && c < npieces) {
+      if (NORM)
+        piece_quant_store_norm(v[r], bf16, rn, qs, lds + c * per16);
+      else
+        piece_quant_store(v[r], bf16, qs, lds + c * per16);
+    }
+  }
   __syncthreads();
 }
 
@@ -502,11 +571,21 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   };
 
   const bool has_work = k0 < k1;
-  // activation pieces first (few, cache-resident), then the weight stream
+  // activation pieces first (few, cache-resident), then the weight stream.
+  // Rows the threads cannot hold in registers (and rows that are not whole
+  // pieces) are quantized completely before the weight loads are issued: a
+  // loop of activation loads after them would make every later wait cover
+  // the whole weight stream.
   u4 stage[kXReg];
+  const int xpieces = a.M * (a.K / (a.x_dtype == BITLINEAR_BF16 ? 8 : 4));
+  const bool held = xpieces <= kXReg * (int)blockDim.x;
   if constexpr (AM == ALDS_X) {
-    stage_load(static_cast<const u4*>(a.x), a.M * (a.K / (a.x_dtype == BITLINEAR_BF16 ? 8 : 4)), stage);
+    if (held)
+      stage_load(static_cast<const u4*>(a.x), xpieces, stage);
+    else
+      quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
   }
+  if constexpr (AM == ALDS_XS) quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
   if constexpr (AM == ALDS_Q) stage_load(reinterpret_cast<const u4*>(a.q), a.M * (int)(a.ldq / 16), stage);
   // Unconditional, so the wait for the staged pieces never has to assume a
   // path without weight loads (a wave without k-tiles reads tile 0 of its
@@ -518,9 +597,15 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // weight loads (that would wait for the pieces before the stream starts)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AM == ALDS_Q) stage_store_q(a, stage, act_lds);
-  if constexpr (AM == ALDS_X)
-    stage_store_x<NORM>(a, stage, act_lds, reinterpret_cast<uint32_t*>(&red[0][0]), sq_slots, row_g, row_qs, row_r);
-  if constexpr (AM == ALDS_XS) quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
+  if constexpr (AM == ALDS_X) {
+    if (held) {
+      if (M == 1)
+        stage_store_x1<NORM>(a, stage, act_lds, reinterpret_cast<uint32_t*>(&red[0][0]), sq_slots, row_g, row_r);
+      else
+        stage_store_x<NORM>(a, stage, act_lds, reinterpret_cast<uint32_t*>(&red[0][0]), sq_slots, row_g, row_qs,
+                            row_r);
+    }
+  }
 
   if (has_work) {
     // ring of kU k-tiles in flight; re-loads past the end read tile k1-1
@@ -709,11 +794,12 @@ GemvArgs make_args(const GemvPlan& p, int64_t M, int64_t K, int64_t N, const uin
 // The plan is the single-matrix plan for the summed output rows (one per
 // matrix for a gated pair), without any K split across workgroups.
 bool make_multi(int64_t M, int64_t K, int count, const uint8_t* const* packed, const float* const* beta,
-                const int64_t* N, void* const* y, int y_dtype, bool glu, bool fuse, GemvPlan& p, GemvArgs& a) {
+                const int64_t* N, void* const* y, int y_dtype, bool glu, bool fuse, int64_t xpieces, GemvPlan& p,
+                GemvArgs& a) {
   if (count < 1 || count > kGemvMaxSeg || (glu && (count != 2 || N[0] != N[1]))) return false;
   int64_t ntot = 0;
   for (int i = 0; i < count; ++i) ntot += N[i];
-  p = make_plan(M, glu ? N[0] : ntot, K, fuse, false);
+  p = make_plan(M, glu ? N[0] : ntot, K, fuse, false, xpieces);
   if (glu) p.NB = 2;
   a = make_args(p, M, K, N[0], packed[0], beta[0], y[0], y_dtype, nullptr);
   a.nseg = count;
@@ -736,6 +822,13 @@ void set_x(GemvArgs& a, const void* x, int x_dtype, int64_t K) {
   a.x_vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
 }
 
+// 16-byte pieces of the activation rows when they are read as pieces, else 0.
+int64_t x_pieces(const void* x, int x_dtype, int64_t M, int64_t K) {
+  const int per16 = (x_dtype & kXDtypeMask) == BITLINEAR_BF16 ? 8 : 4;
+  const bool vec = (K % per16 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  return vec ? M * (K / per16) : 0;
+}
+
 }  // namespace
 
 hipError_t launch_gemv_multi(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, int count,
@@ -743,7 +836,7 @@ hipError_t launch_gemv_multi(const int8_t* q, int64_t ldq, const float* ds, int6
                              int y_dtype, bool glu, hipStream_t s) {
   GemvPlan p;
   GemvArgs a;
-  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, false, p, a)) return hipErrorInvalidValue;
+  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, false, 0, p, a)) return hipErrorInvalidValue;
   a.q = q;
   a.ldq = ldq;
   a.ds = ds;
@@ -755,7 +848,8 @@ hipError_t launch_decode_multi(const void* x, int x_dtype, int64_t M, int64_t K,
                                void* const* y, int y_dtype, bool glu, hipStream_t s) {
   GemvPlan p;
   GemvArgs a;
-  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, true, p, a)) return hipErrorInvalidValue;
+  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, true, x_pieces(x, x_dtype, M, K), p, a))
+    return hipErrorInvalidValue;
   set_x(a, x, x_dtype, K);
   return dispatch(p, a, s);
 }
@@ -779,7 +873,7 @@ hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t
 
 hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
                             const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
-  const GemvPlan p = make_plan(M, N, K, true);
+  const GemvPlan p = make_plan(M, N, K, true, true, x_pieces(x, x_dtype, M, K));
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr);
   set_x(a, x, x_dtype, K);
   return dispatch(p, a, s);
