@@ -68,6 +68,14 @@ def _load():
     lib.oracle_relu2_mul.argtypes = [p, p, i64, p]
     lib.oracle_add_f32.restype = None
     lib.oracle_add_f32.argtypes = [p, p, i64]
+    lib.oracle_b1_bytes.restype = i64
+    lib.oracle_b1_bytes.argtypes = [i64, i64]
+    lib.oracle_binarize.restype = None
+    lib.oracle_binarize.argtypes = [p, i64, p]
+    lib.oracle_pack_b1.restype = None
+    lib.oracle_pack_b1.argtypes = [p, i64, i64, p]
+    lib.oracle_unpack_b1.restype = None
+    lib.oracle_unpack_b1.argtypes = [p, i64, i64, p]
     lib.oracle_rmsnorm_f32.restype = None
     lib.oracle_rmsnorm_f32.argtypes = [p, i64, i64, p]
     _lib = lib
@@ -216,6 +224,46 @@ def add_f32(x: np.ndarray, r: np.ndarray) -> np.ndarray:
     assert out.shape == r.shape
     _load().oracle_add_f32(_ptr(out), _ptr(r), out.size)
     return out
+
+
+# ------------------------------------------------------------ binary weights
+def binarize(w: np.ndarray) -> np.ndarray:
+    """int8 codes t = +1 where w >= 0, else -1."""
+    w = _c(w, np.float32)
+    t = np.empty(w.shape, dtype=np.int8)
+    _load().oracle_binarize(_ptr(w), w.size, _ptr(t))
+    return t
+
+
+def b1_bytes(N: int, K: int) -> int:
+    return int(_load().oracle_b1_bytes(N, K))
+
+
+def pack_b1(t: np.ndarray) -> np.ndarray:
+    t = _c(t, np.int8)
+    N, K = t.shape
+    out = np.empty(b1_bytes(N, K), dtype=np.uint8)
+    _load().oracle_pack_b1(_ptr(t), N, K, _ptr(out))
+    return out
+
+
+def unpack_b1(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    assert packed.size >= b1_bytes(N, K)
+    t = np.empty((N, K), dtype=np.int8)
+    _load().oracle_unpack_b1(_ptr(packed), N, K, _ptr(t))
+    return t
+
+
+def bitlinear_forward_b1(x_bf16_bits: np.ndarray, w: np.ndarray, threads: int = 1) -> dict:
+    """BitLinear forward with binary weights; every intermediate as a dict."""
+    beta = absmean(w)
+    t = binarize(w)
+    q, ds, rs = quant_act(x_bf16_bits, bf16_bits=True)
+    acc = matmul_i32(q, t, threads=threads)
+    y = dequant(acc, ds, beta)
+    return {"beta": beta, "t": t, "q": q, "ds": ds, "rowsum": rs, "acc": acc, "y": y,
+            "y_bf16": to_bf16_bits(y)}
 
 
 # ------------------------------------------------------------ whole forward

@@ -36,6 +36,11 @@
  *      BitLinears of one layer ("Key Technologies Enabling the BitNET
  *      Family", Architectural Innovations and Optimizations: squared ReLU in
  *      the feed-forward layers); the residual sums of a decoder layer.
+ *  - oracle_binarize, oracle_pack_b1 / oracle_unpack_b1: the binary
+ *      variant BitNet b1 ("BitNet / Ternary / Binary - Les LLMs 1-bit",
+ *      TL;DR and Mecanisme technique: every weight is exactly +1 or -1), one
+ *      bit per weight; its layout is this project's own choice, written here
+ *      from its specification.
  *  - oracle_pack_t2 / oracle_unpack_t2: 2 bits per ternary weight
  *      ("BitNet Technical Notes", Appendix glossary: bit-packing at 2 bits per
  *      ternary weight; "BitNet: Inference framework for 1-bit LLMs", post #139:
@@ -46,6 +51,9 @@
  *  - beta: mean |w| in fp64, summed in a fixed order (consecutive chunks of
  *    4096 elements in row-major order, each chunk summed in index order, the
  *    chunk sums added in ascending chunk order), then rounded once to fp32.
+ *  - binary weights (the pages give no binarization rule): t = +1 where
+ *    w >= 0, else -1 (so zero maps to +1 and the set stays {-1, +1}); the
+ *    scale is the same beta = mean |w| as for the ternary weights.
  *  - rounding: half to even (torch.round semantics, the IEEE default).
  *  - activations: gamma = max |x|; g = max(gamma, 1e-5); q = clamp(rint(x *
  *    (127 / g)), -127, 127); ds = g / 127.
@@ -281,6 +289,62 @@ int64_t oracle_unpack_t2(const uint8_t *packed, int64_t N, int64_t K, int8_t *t)
             }
         }
     return bad;
+}
+
+/*
+ * Format B1 (1 bit per weight).  Tiles of 16 rows x 512 columns; tile
+ * (nb, kb) is 1024 bytes at byte offset (nb * ceil(K/512) + kb) * 1024.
+ * Inside a tile, 32-bit word d of lane L (bytes 16*L + 4*d .. +3, little
+ * endian; L in 0..63, d in 0..3) holds in bit 16*h + j (h in 0..1, j in
+ * 0..15) the weight
+ *     n = 16*nb + (L mod 16),
+ *     k = 512*kb + 64*(2*d + h) + 16*(L div 16) + j.
+ * Bit 1 is +1, bit 0 is -1.  Positions with n >= N or k >= K hold 0.
+ */
+int64_t oracle_b1_bytes(int64_t N, int64_t K)
+{
+    return ((N + 15) / 16) * ((K + 511) / 512) * 1024;
+}
+
+/* t = +1 where w >= 0, else -1 */
+void oracle_binarize(const float *w, int64_t count, int8_t *t)
+{
+    for (int64_t i = 0; i < count; ++i)
+        t[i] = w[i] >= 0.0f ? 1 : -1;
+}
+
+void oracle_pack_b1(const int8_t *t, int64_t N, int64_t K, uint8_t *packed)
+{
+    int64_t Kt = (K + 511) / 512;
+    memset(packed, 0, (size_t)oracle_b1_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            if (t[n * K + k] != 1)
+                continue;
+            int64_t nb = n / 16, kb = k / 512;
+            int64_t r = n % 16, c = k % 512;
+            int64_t s = c / 64, g = (c % 64) / 16, j = c % 16;
+            int64_t L = 16 * g + r, d = s / 2, h = s % 2;
+            int64_t bit = 16 * h + j;
+            int64_t byte = (nb * Kt + kb) * 1024 + 16 * L + 4 * d + bit / 8;
+            packed[byte] |= (uint8_t)(1u << (bit % 8));
+        }
+}
+
+/* Inverse of oracle_pack_b1 over the N x K weights. */
+void oracle_unpack_b1(const uint8_t *packed, int64_t N, int64_t K, int8_t *t)
+{
+    int64_t Kt = (K + 511) / 512;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t nb = n / 16, kb = k / 512;
+            int64_t r = n % 16, c = k % 512;
+            int64_t s = c / 64, g = (c % 64) / 16, j = c % 16;
+            int64_t L = 16 * g + r, d = s / 2, h = s % 2;
+            int64_t bit = 16 * h + j;
+            int64_t byte = (nb * Kt + kb) * 1024 + 16 * L + 4 * d + bit / 8;
+            t[n * K + k] = (packed[byte] >> (bit % 8)) & 1 ? 1 : -1;
+        }
 }
 
 /* --------------------------------------------------------- whole forward */

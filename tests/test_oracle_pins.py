@@ -513,3 +513,94 @@ def test_rmsnorm_sign_symmetry_and_row_independence():
     np.testing.assert_array_equal(oracle.rmsnorm(-x), -out)
     np.testing.assert_array_equal(oracle.rmsnorm(x[2:3]), out[2:3])
     np.testing.assert_array_equal(oracle.rmsnorm(x[:, ::-1].copy())[:, ::-1] != 0, out != 0)
+
+
+# ------------------------------------------------------------- binary weights (b1)
+def test_binarize_signs_and_zero():
+    w = np.array([-2.0, -1e-30, -0.0, 0.0, 1e-30, 3.0, np.float32(-1e-45)], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.binarize(w), [-1, -1, 1, 1, 1, 1, -1])
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(100000).astype(np.float32)
+    t = oracle.binarize(x)
+    assert set(np.unique(t)) == {-1, 1}
+    np.testing.assert_array_equal(t, np.where(np.signbit(x) & (x != 0), -1, 1))
+    np.testing.assert_array_equal(oracle.binarize(-x), -t)  # no zeros drawn
+    # half of a symmetric distribution is positive: within 5 sigma
+    assert abs((t == 1).mean() - 0.5) < 5 * 0.5 / np.sqrt(x.size)
+
+
+def _mfma_sim_b1(packed, q, N, K):
+    """acc = q . t^T computed the way a 16x16x64 int8 matrix core consumes the
+    1-bit tiles: for step s of a 512-column tile, lane (n, g) supplies the 16
+    bits 16*(s%2) .. +15 of its dword s//2, which must be the codes of
+    columns 64 s + 16 g + j of row n (bit 1 = +1, bit 0 = -1)."""
+    M = q.shape[0]
+    Kt, Nt = -(-K // 512), -(-N // 16)
+    qp = np.zeros((M, Kt * 512), dtype=np.int64)
+    qp[:, :K] = q
+    acc = np.zeros((M, Nt * 16), dtype=np.int64)
+    tiles = packed.reshape(Nt, Kt, 64, 16)
+    for nb in range(Nt):
+        for kb in range(Kt):
+            words = tiles[nb, kb].copy().view("<u4").reshape(64, 4)
+            for s in range(8):
+                for lane in range(64):
+                    n, g = lane % 16, lane // 16
+                    bits = (int(words[lane, s // 2]) >> (16 * (s % 2))) & 0xFFFF
+                    b = np.array([(bits >> j) & 1 for j in range(16)], dtype=np.int64) * 2 - 1
+                    cols = kb * 512 + 64 * s + 16 * g + np.arange(16)
+                    acc[:, nb * 16 + n] += qp[:, cols] @ b
+    return acc[:, :N]
+
+
+@pytest.mark.parametrize("N,K", [(16, 512), (17, 600), (5, 1030)])
+def test_pack_b1_feeds_the_matrix_core_contraction(N, K):
+    rng = np.random.default_rng(N + K)
+    t = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
+    q = rng.integers(-127, 128, size=(3, K)).astype(np.int8)
+    p = oracle.pack_b1(t)
+    assert p.size == -(-N // 16) * -(-K // 512) * 1024 == oracle.b1_bytes(N, K)
+    sim = _mfma_sim_b1(p, q, N, K)
+    # padded columns read -1 codes against zero activations: no contribution
+    np.testing.assert_array_equal(sim, q.astype(np.int64) @ t.astype(np.int64).T)
+    np.testing.assert_array_equal(oracle.matmul_i32(q, t), sim)
+
+
+def test_pack_b1_round_trip_and_padding():
+    rng = np.random.default_rng(5)
+    for N, K in ((1, 1), (16, 512), (33, 1100), (7, 513)):
+        t = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
+        p = oracle.pack_b1(t)
+        np.testing.assert_array_equal(oracle.unpack_b1(p, N, K), t)
+        # one set bit per +1 weight, none in the padding
+        assert int(np.unpackbits(p).sum()) == int((t == 1).sum())
+    t = -np.ones((16, 512), dtype=np.int8)
+    t[3, 200] = 1  # column 200: step 3, group 0, bit 8 of the high half of dword 1 of lane 3
+    p = oracle.pack_b1(t)
+    assert np.flatnonzero(p).tolist() == [16 * 3 + 4 * 1 + (16 + 8) // 8]
+    assert p[16 * 3 + 4 + 3] == 1 << ((16 + 8) % 8)
+
+
+def test_b1_product_equals_xnor_popcount():
+    # textbook identity for +-1 vectors: a . w = K - 2 * popcount(a xor w) on their sign bits
+    rng = np.random.default_rng(8)
+    K = 777
+    a = np.where(rng.random((4, K)) < 0.5, 1, -1).astype(np.int8)
+    w = rng.standard_normal((9, K)).astype(np.float32)
+    t = oracle.binarize(w)
+    acc = oracle.matmul_i32(a, t)
+    for m in range(4):
+        for n in range(9):
+            x = int(np.sum((a[m] > 0) != (t[n] > 0)))
+            assert acc[m, n] == K - 2 * x
+
+
+def test_forward_b1_bound():
+    w = workloads.gen_weights(64, 512, seed=3)
+    xb = workloads.gen_acts_bf16(4, 512, seed=4)
+    out = oracle.bitlinear_forward_b1(xb, w)
+    assert set(np.unique(out["t"])) == {-1, 1}
+    x = workloads.bf16_bits_to_f32(xb).astype(np.float64)
+    approx = x @ (float(out["beta"]) * out["t"].astype(np.float64)).T
+    bound = (out["ds"][:, None].astype(np.float64) / 2) * float(out["beta"]) * 512
+    assert np.all(np.abs(out["y"] - approx) <= bound * (1 + 1e-6) + 1e-6)
