@@ -16,6 +16,8 @@ Functions carry the C names:
     bitlinear_forward_decode_multi(x, packed_list, beta_list, N_list, y_list)
     bitlinear_gemv_glu(x_q, x_ds, K, packed_gate, beta_gate, packed_up, beta_up, N, h)
     bitlinear_forward_decode_glu(x, packed_gate, beta_gate, packed_up, beta_up, N, h)
+    bitlinear_pack_weights_b1(w, packed, w_beta, workspace)      (binary weights)
+    bitlinear_gemv_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
 An fp32 output tensor can be passed with ``accumulate=True`` to the product
 calls, which then add their result into it (``BITLINEAR_F32_ADD``); the calls
 that quantize activations take ``rmsnorm=True`` to RMS-normalize each row
@@ -45,7 +47,8 @@ EXPORTS = (
     "bitlinear_gemm_workspace_bytes", "bitlinear_quant_act", "bitlinear_pack_weights",
     "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode", "bitlinear_relu2_mul",
     "bitlinear_gemv_multi", "bitlinear_forward_decode_multi", "bitlinear_gemv_glu",
-    "bitlinear_forward_decode_glu",
+    "bitlinear_forward_decode_glu", "bitlinear_packed_bytes_b1", "bitlinear_pack_weights_b1",
+    "bitlinear_gemv_b1",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -94,6 +97,12 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).argtypes = [p, p, i64, i64, p, p, i64, p, i32, p, sz, p]
     L.bitlinear_forward_decode.restype = i32
     L.bitlinear_forward_decode.argtypes = [p, i32, i64, i64, p, p, i64, p, i32, p]
+    L.bitlinear_packed_bytes_b1.restype = i64
+    L.bitlinear_packed_bytes_b1.argtypes = [i64, i64]
+    L.bitlinear_pack_weights_b1.restype = i32
+    L.bitlinear_pack_weights_b1.argtypes = [p, i64, i64, p, p, p, p]
+    L.bitlinear_gemv_b1.restype = i32
+    L.bitlinear_gemv_b1.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_relu2_mul.restype = i32
     L.bitlinear_relu2_mul.argtypes = [p, p, i64, p, p]
     L.bitlinear_gemv_multi.restype = i32
@@ -136,6 +145,10 @@ def packed_bytes(N: int, K: int) -> int:
     return int(lib().bitlinear_packed_bytes(N, K))
 
 
+def packed_bytes_b1(N: int, K: int) -> int:
+    return int(lib().bitlinear_packed_bytes_b1(N, K))
+
+
 def pack_workspace_bytes(N: int, K: int) -> int:
     return int(lib().bitlinear_pack_workspace_bytes(N, K))
 
@@ -165,6 +178,19 @@ def bitlinear_pack_weights(w, packed, w_beta, workspace, stream=None) -> None:
     N, K = w.shape
     _check(lib().bitlinear_pack_weights(_ptr(w), N, K, _ptr(packed), _ptr(w_beta), _ptr(workspace),
                                         _stream(stream)))
+
+
+def bitlinear_pack_weights_b1(w, packed, w_beta, workspace, stream=None) -> None:
+    """w [N][K] fp32 latent weights -> 1-bit tiles (t = +1 where w >= 0, else -1) + w_beta."""
+    N, K = w.shape
+    _check(lib().bitlinear_pack_weights_b1(_ptr(w), N, K, _ptr(packed), _ptr(w_beta), _ptr(workspace),
+                                           _stream(stream)))
+
+
+def bitlinear_gemv_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
+    """y [M][N] = dequant(x_q . T^T) for binary weights, M <= 64 tokens."""
+    _check(lib().bitlinear_gemv_b1(_ptr(x_q), _ptr(x_ds), _ptr(x_rowsum), x_ds.shape[0], K, _ptr(packed),
+                                   _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate), _stream(stream)))
 
 
 def _ydtype(y, accumulate: bool) -> int:
@@ -262,7 +288,7 @@ def bitlinear_relu2_mul(g, u, h, stream=None) -> None:
 
 
 def decode_fits(M: int, K: int) -> bool:
-    return 1 <= M <= GEMV_MAX_M and M * (act_stride(K) + 16) <= DECODE_MAX_ACT_BYTES
+    return 1 <= M <= GEMV_MAX_M and M * ((K + 255) // 256 * 256 + 16) <= DECODE_MAX_ACT_BYTES
 
 
 # ------------------------------------------------------------- conveniences
@@ -296,6 +322,15 @@ def pack_weights(w, stream=None):
     beta = torch.empty((1,), dtype=torch.float32, device=w.device)
     ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
     bitlinear_pack_weights(w, packed, beta, ws, stream)
+    return packed, beta
+
+
+def pack_weights_b1(w, stream=None):
+    N, K = w.shape
+    packed = torch.empty((packed_bytes_b1(N, K),), dtype=torch.uint8, device=w.device)
+    beta = torch.empty((1,), dtype=torch.float32, device=w.device)
+    ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    bitlinear_pack_weights_b1(w, packed, beta, ws, stream)
     return packed, beta
 
 

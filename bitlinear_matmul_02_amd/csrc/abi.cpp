@@ -33,7 +33,10 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 bool k_ok(int64_t K) { return K >= 1 && K <= BITLINEAR_MAX_K; }
 bool n_ok(int64_t N) { return N >= 1 && N <= BITLINEAR_MAX_N; }
 
-int64_t act_stride(int64_t K) { return bl::ceil_div(K, bl::kTileK) * bl::kTileK; }
+int64_t act_stride(int64_t K) { return bl::ceil_div(K, bl::kActAlign) * bl::kActAlign; }
+
+// Activation rows the fused decode kernels stage in LDS: K rounded up to 256, + 16.
+int64_t fused_row(int64_t K) { return bl::ceil_div(K, bl::kTileK) * bl::kTileK + 16; }
 
 // Shape, dtype and weight/output checks shared by every product call.
 int check_common(const char* fn, int64_t M, int64_t max_m, int64_t K, const void* packed, const float* w_beta,
@@ -74,7 +77,7 @@ int check_product(const char* fn, const int8_t* x_q, const float* x_ds, int64_t 
 
 extern "C" {
 
-int bitlinear_version(void) { return (1 << 16) | 1; }
+int bitlinear_version(void) { return (1 << 16) | 2; }
 
 const char* bitlinear_last_error(void) { return g_err; }
 
@@ -83,6 +86,11 @@ int64_t bitlinear_act_stride(int64_t K) { return k_ok(K) ? act_stride(K) : -1; }
 int64_t bitlinear_packed_bytes(int64_t N, int64_t K) {
   if (!n_ok(N) || !k_ok(K)) return -1;
   return bl::ceil_div(N, bl::kTileN) * bl::ceil_div(K, bl::kTileK) * bl::kTileBytes;
+}
+
+int64_t bitlinear_packed_bytes_b1(int64_t N, int64_t K) {
+  if (!n_ok(N) || !k_ok(K)) return -1;
+  return bl::ceil_div(N, bl::kTileN) * bl::ceil_div(K, bl::kTileKB1) * bl::kTileBytes;
 }
 
 int64_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
@@ -131,6 +139,19 @@ int bitlinear_pack_weights(const float* w, int64_t N, int64_t K, void* packed, f
                     fn);
 }
 
+int bitlinear_pack_weights_b1(const float* w, int64_t N, int64_t K, void* packed, float* w_beta, void* workspace,
+                              void* stream) {
+  const char* fn = "bitlinear_pack_weights_b1";
+  if (!n_ok(N) || !k_ok(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld or K=%lld out of range", fn, (long long)N, (long long)K);
+  if (!w || !packed || !w_beta || !workspace) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(w, 4) || !aligned(packed, 16) || !aligned(w_beta, 4) || !aligned(workspace, 8))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bl::launch_pack_b1(w, N, K, static_cast<uint8_t*>(packed), w_beta, static_cast<double*>(workspace),
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_gemv(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed,
                    const float* w_beta, int64_t N, void* y, int y_dtype, void* workspace,
                    size_t workspace_bytes, void* stream) {
@@ -157,6 +178,19 @@ int bitlinear_gemm(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, c
                     fn);
 }
 
+int bitlinear_gemv_b1(const int8_t* x_q, const float* x_ds, const int32_t* x_rowsum, int64_t M, int64_t K,
+                      const void* packed, const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
+  const char* fn = "bitlinear_gemv_b1";
+  int st = check_product(fn, x_q, x_ds, M, BITLINEAR_GEMV_MAX_M, K, packed, w_beta, N, y, y_dtype, nullptr, 0, 0);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  if (!x_rowsum) return fail(BITLINEAR_ERR_ARG, "%s: x_rowsum is required", fn);
+  if (!aligned(x_rowsum, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_rowsum not element aligned", fn);
+  return hip_status(bl::launch_gemv_b1(x_q, act_stride(K), x_ds, x_rowsum, M, K, static_cast<const uint8_t*>(packed),
+                                       w_beta, N, y, y_dtype, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, const void* packed,
                              const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
   const char* fn = "bitlinear_forward_decode";
@@ -169,8 +203,8 @@ int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, c
   if (!x) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
   if (!aligned(x, x_base == BITLINEAR_BF16 ? 2 : 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x not element aligned", fn);
   if (!bl::decode_fused_fits(M, K))
-    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (act_stride(K) + 16) = %lld exceeds %d bytes", fn,
-                (long long)(M * (act_stride(K) + 16)), BITLINEAR_DECODE_MAX_ACT_BYTES);
+    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (K rounded up to 256 + 16) = %lld exceeds %d bytes", fn,
+                (long long)(M * fused_row(K)), BITLINEAR_DECODE_MAX_ACT_BYTES);
   return hip_status(bl::launch_decode_t2(x, x_dtype, M, K, static_cast<const uint8_t*>(packed), w_beta, N, y,
                                          y_dtype, static_cast<hipStream_t>(stream)),
                     fn);
@@ -202,8 +236,8 @@ int check_x(const char* fn, const void* x, int x_dtype, int64_t M, int64_t K) {
   if (!x) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
   if (!aligned(x, x_base == BITLINEAR_BF16 ? 2 : 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x not element aligned", fn);
   if (!bl::decode_fused_fits(M, K))
-    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (act_stride(K) + 16) = %lld exceeds %d bytes", fn,
-                (long long)(M * (act_stride(K) + 16)), BITLINEAR_DECODE_MAX_ACT_BYTES);
+    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: M * (K rounded up to 256 + 16) = %lld exceeds %d bytes", fn,
+                (long long)(M * fused_row(K)), BITLINEAR_DECODE_MAX_ACT_BYTES);
   return BITLINEAR_OK;
 }
 

@@ -45,6 +45,13 @@
 // and Optimizations: squared ReLU in the feed-forward layers) instead of the
 // two outputs.
 //
+// Binary weights (format B1, "BitNet / Ternary / Binary - Les LLMs 1-bit",
+// TL;DR: every weight +1 or -1) use the same kernel with 16 x 512 tiles of
+// one bit per weight: lane (n, g) of step s holds the 16 bits of columns
+// 64 s + 16 g + j, expanded to bytes b in {0, 1} with one multiply per four
+// bits; the matrix cores sum q * b and the epilogue takes 2 * sum - rowsum(q)
+// = sum q * (2 b - 1), exact.
+//
 // Tiny outputs with a long K (AGLOBAL only) also split K across workgroups:
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
@@ -66,14 +73,18 @@ enum AMode { AGLOBAL = 0, ALDS_Q = 1, ALDS_X = 2, ALDS_XS = 3 };
 // k-tiles in flight per wave, chosen to keep the prefetch ring within the
 // register budget (weights: 4 VGPRs per output block; activations in the
 // ring only for AGLOBAL: 16 VGPRs per token block).
-constexpr int ring_depth(int mb, int nb, int amode) {
-  return amode == AGLOBAL ? ((mb * 4 + nb) * 4 <= 24 ? 4 : ((mb * 4 + nb) * 4 <= 40 ? 2 : 1))
+// Binary tiles carry twice the MFMA steps, so twice the activation operands.
+constexpr int ring_depth(int mb, int nb, int amode, int fmt = 0) {
+  return amode == AGLOBAL ? (((fmt ? 8 : 4) * mb + nb) * 4 <= 24 ? 4 : (((fmt ? 8 : 4) * mb + nb) * 4 <= 40 ? 2 : 1))
                           : (nb == 1 ? 8 : (nb == 2 ? 4 : 2));
 }
+
+// Columns per weight tile: 256 (T2, 2 bits) or 512 (B1, 1 bit); 1 KB either way.
+constexpr int tile_cols(int fmt) { return fmt ? 512 : kTileK; }
 // Largest workgroup, in waves, for MB token blocks.
 constexpr int max_waves(int mb) { return mb <= 2 ? 16 : 8; }
 
-int64_t lds_row(int64_t K) { return ceil_div(K, kTileK) * kTileK + kLdsPad; }
+int64_t lds_row(int64_t K, int fmt = 0) { return ceil_div(K, tile_cols(fmt)) * tile_cols(fmt) + kLdsPad; }
 
 struct GemvPlan {
   int MB, NB;      // 16-row token blocks, 16-row output blocks per workgroup
@@ -87,12 +98,13 @@ struct GemvPlan {
 
 // xpieces: 16-byte activation pieces of a fused launch whose rows are whole
 // pieces (0 otherwise).
-GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split = true, int64_t xpieces = 0) {
+GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split = true, int64_t xpieces = 0,
+                   int fmt = 0) {
   GemvPlan p{};
   p.MB = (int)ceil_div(M < 1 ? 1 : M, 16);
   p.Nt = (int)ceil_div(N, kTileN);
-  p.Kt = (int)ceil_div(K, kTileK);
-  const int64_t lds = M * lds_row(K);
+  p.Kt = (int)ceil_div(K, tile_cols(fmt));
+  const int64_t lds = M * lds_row(K, fmt);
   p.amode = fuse ? ALDS_X : (lds <= kDecodeLdsBytes ? ALDS_Q : AGLOBAL);
   p.lds_bytes = p.amode == AGLOBAL ? 0 : lds;
   // Output blocks per workgroup: each activation operand is reused over NB
@@ -121,7 +133,7 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   if (waves < 1) waves = 1;
   p.tps = (int)ceil_div(p.Kt, waves);
   p.waves = (int)ceil_div(p.Kt, p.tps);
-  if (fuse && xpieces > 0) {
+  if (xpieces > 0 && p.amode != AGLOBAL) {
     // enough threads to hold the activation rows in registers; the extra
     // waves only help with the prologue
     const int64_t need = ceil_div(xpieces, (int64_t)kXReg * 64);
@@ -162,6 +174,7 @@ struct GemvArgs {
   int M, K, Kt, tps, SB;
   int64_t ldq, ldl;
   GemvSeg seg[kGemvMaxSeg];
+  const int32_t* rowsum;  // B1: per-token sum of the int8 codes
   int nseg;         // segments in use (1 for a single BitLinear)
   int glu;          // gated pair: seg[0] gate, seg[1] up, h into seg[0].y
   int y_dtype;
@@ -193,18 +206,29 @@ __device__ inline void stage_load(const u4* src, int npieces, u4 (&v)[kXReg]) {
 __device__ void stage_store_q(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int cpr = (int)(a.ldq / 16), npieces = a.M * cpr;
-  const u4* src = reinterpret_cast<const u4*>(a.q);
+  const int rowp = (int)((a.ldl - kLdsPad) / 16);  // pieces of a row the kernel reads
 #pragma unroll
   for (int r = 0; r < kXReg; ++r) {
     const int c = tid + r * nthr;
     if (c < npieces) {
-      const int m = c / cpr;
-      *reinterpret_cast<u4*>(lds + (int64_t)m * a.ldl + (c - m * cpr) * 16) = v[r];
+      const int m = c / cpr, pc = c - m * cpr;
+      if (pc < rowp) *reinterpret_cast<u4*>(lds + (int64_t)m * a.ldl + pc * 16) = v[r];
     }
   }
-  for (int c = tid + kXReg * nthr; c < npieces; c += nthr) {
-    const int m = c / cpr;
-    *reinterpret_cast<u4*>(lds + (int64_t)m * a.ldl + (c - m * cpr) * 16) = src[c];
+  __syncthreads();
+}
+
+// The same copy for rows the threads cannot hold in registers; issued before
+// the weight loads (a loop of loads after them would make every later wait
+// cover the weight stream).
+__device__ void copy_rows_q(const GemvArgs& a, int8_t* lds) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int cpr = (int)(a.ldq / 16), npieces = a.M * cpr;
+  const int rowp = (int)((a.ldl - kLdsPad) / 16);
+  const u4* src = reinterpret_cast<const u4*>(a.q);
+  for (int c = tid; c < npieces; c += nthr) {
+    const int m = c / cpr, pc = c - m * cpr;
+    if (pc < rowp) *reinterpret_cast<u4*>(lds + (int64_t)m * a.ldl + pc * 16) = src[c];
   }
   __syncthreads();
 }
@@ -496,8 +520,20 @@ __device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, double* sq,
   __syncthreads();
 }
 
-template <int MB, int NB, int AM, bool NORM, int kU = ring_depth(MB, NB, AM)>
+// Expand step s (0..7) of a B1 lane chunk: bits 16 (s % 2) .. +15 of dword
+// s / 2 become 16 bytes in {0, 1} (bit j -> byte j).  A nibble times
+// 0x00204081 places its bits 0..3 at bits 0, 8, 16, 24 without carries.
+__device__ inline v4i b1_field(const u4 w, int s) {
+  const uint32_t bits = w[s >> 1] >> (16 * (s & 1));
+  v4i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = (int)((((bits >> (4 * q)) & 0xFu) * 0x00204081u) & 0x01010101u);
+  return r;
+}
+
+template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT)>
 __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
+  constexpr int KT = tile_cols(FMT), NS = KT / 64;  // columns and MFMA steps per k-tile
   constexpr int E = MB * NB * 4;  // accumulator values per lane
   constexpr int UA = AM == AGLOBAL ? kU : 1;
   __shared__ int red[E][64];
@@ -544,7 +580,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     aoff[mb] = (int64_t)min(mb * 16 + r16, M - 1) * (AM == AGLOBAL ? a.ldq : a.ldl) + 16 * g4;
 
   u4 wbuf[kU][NB];
-  v4i abuf[UA][MB][4];
+  v4i abuf[UA][MB][NS];
   auto load_w = [&](int slot, int kt) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) wbuf[slot][j] = __builtin_nontemporal_load(bptr[j] + (int64_t)kt * 64);
@@ -554,17 +590,17 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        abuf[slot][mb][i] = *reinterpret_cast<const v4i*>(base + aoff[mb] + (int64_t)kt * kTileK + 64 * i);
+      for (int i = 0; i < NS; ++i)
+        abuf[slot][mb][i] = *reinterpret_cast<const v4i*>(base + aoff[mb] + (int64_t)kt * KT + 64 * i);
   };
   auto mma_tile = [&](int slot, int kt) {
     const int as = AM == AGLOBAL ? slot : 0;
     if (AM != AGLOBAL) load_a(0, kt);  // LDS operands: read at use
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NS; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const v4i b = t2_field(wbuf[slot][j], i);
+        const v4i b = FMT ? b1_field(wbuf[slot][j], i) : t2_field(wbuf[slot][j], i);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma16(abuf[as][mb][i], b, acc[mb][j]);
       }
@@ -586,7 +622,12 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
       quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
   }
   if constexpr (AM == ALDS_XS) quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
-  if constexpr (AM == ALDS_Q) stage_load(reinterpret_cast<const u4*>(a.q), a.M * (int)(a.ldq / 16), stage);
+  if constexpr (AM == ALDS_Q) {
+    if (a.M * (int)(a.ldq / 16) <= kXReg * (int)blockDim.x)
+      stage_load(reinterpret_cast<const u4*>(a.q), a.M * (int)(a.ldq / 16), stage);
+    else
+      copy_rows_q(a, act_lds);
+  }
   // Unconditional, so the wait for the staged pieces never has to assume a
   // path without weight loads (a wave without k-tiles reads tile 0 of its
   // first block, in bounds, and never uses it).
@@ -596,7 +637,9 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // keep the compiler from hoisting work on the staged pieces above the
   // weight loads (that would wait for the pieces before the stream starts)
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (AM == ALDS_Q) stage_store_q(a, stage, act_lds);
+  if constexpr (AM == ALDS_Q) {
+    if (a.M * (int)(a.ldq / 16) <= kXReg * (int)blockDim.x) stage_store_q(a, stage, act_lds);
+  }
   if constexpr (AM == ALDS_X) {
     if (held) {
       if (M == 1)
@@ -716,15 +759,18 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
       if (m >= M) continue;
       const float dsm = FUSED ? row_g[m] / 127.0f : a.ds[m];  // g of the normalized row with a.norm
       const float scale = dsm * bt;
+      const int rs = FMT ? a.rowsum[m] : 0;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int n = (nb0 + j) * kTileN + r16;
-        if (n < sg.N) store_out(sg.y, a.y_dtype, (int64_t)m * sg.N + n, acc[mb][j][r], scale);
+        // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum, scaled as the T2 sums (64 t)
+        const int v = FMT ? (2 * acc[mb][j][r] - rs) * 64 : acc[mb][j][r];
+        if (n < sg.N) store_out(sg.y, a.y_dtype, (int64_t)m * sg.N + n, v, scale);
       }
     }
 }
 
-template <int MB, int NB, int AM, bool NORM>
+template <int MB, int NB, int AM, bool NORM, int FMT = 0>
 hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if constexpr (AM != AGLOBAL) {
     // static LDS plus the largest activation rows can pass the default 64 KB
@@ -732,20 +778,20 @@ hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr = hipSuccess;
     std::call_once(once, [] {
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM>),
+      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT>),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLdsBytes);
     });
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),
+  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM, FMT>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),
                      (size_t)p.lds_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int AM, bool NORM = false>
+template <int AM, bool NORM = false, int FMT = 0>
 hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 #define BL_GEMV_CASE(mb, nb) \
-  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM, NORM>(p, a, s)
+  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM, NORM, FMT>(p, a, s)
   // the (MB, NB) pairs make_plan can produce for this mode
   BL_GEMV_CASE(1, 1);
   BL_GEMV_CASE(1, 2);
@@ -755,7 +801,7 @@ hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   BL_GEMV_CASE(4, 1);
   BL_GEMV_CASE(3, 2);  // AGLOBAL, and gated pairs in every mode
   BL_GEMV_CASE(4, 2);
-  if constexpr (AM == AGLOBAL) BL_GEMV_CASE(2, 4);
+  if constexpr (AM == AGLOBAL && FMT == 0) BL_GEMV_CASE(2, 4);
 #undef BL_GEMV_CASE
   return hipErrorInvalidValue;
 }
@@ -771,15 +817,15 @@ hipError_t dispatch(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 }
 
 GemvArgs make_args(const GemvPlan& p, int64_t M, int64_t K, int64_t N, const uint8_t* packed, const float* beta,
-                   void* y, int y_dtype, void* ws) {
+                   void* y, int y_dtype, void* ws, int fmt = 0) {
   GemvArgs a{};
   a.M = (int)M;
   a.K = (int)K;
   a.Kt = p.Kt;
   a.tps = p.tps;
   a.SB = p.SB;
-  a.ldq = (int64_t)p.Kt * kTileK;
-  a.ldl = lds_row(K);
+  a.ldq = (int64_t)p.Kt * tile_cols(fmt);
+  a.ldl = lds_row(K, fmt);
   a.nseg = 1;
   a.seg[0] = GemvSeg{reinterpret_cast<const u4*>(packed), beta, y, (int)N, p.Nt, 0};
   a.y_dtype = y_dtype;
@@ -854,6 +900,19 @@ hipError_t launch_decode_multi(const void* x, int x_dtype, int64_t M, int64_t K,
   return dispatch(p, a, s);
 }
 
+hipError_t launch_gemv_b1(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M,
+                          int64_t K, const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype,
+                          hipStream_t s) {
+  const GemvPlan p = make_plan(M, N, K, false, false, M * (ldq / 16), 1);
+  GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr, 1);
+  a.q = q;
+  a.ldq = ldq;
+  a.ds = ds;
+  a.rowsum = rowsum;
+  if (p.amode == ALDS_Q) return dispatch_mb_nb<ALDS_Q, false, 1>(p, a, s);
+  return dispatch_mb_nb<AGLOBAL, false, 1>(p, a, s);
+}
+
 int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, false).ws_bytes; }
 
 bool decode_fused_fits(int64_t M, int64_t K) {
@@ -863,7 +922,7 @@ bool decode_fused_fits(int64_t M, int64_t K) {
 hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s) {
-  const GemvPlan p = make_plan(M, N, K, false);
+  const GemvPlan p = make_plan(M, N, K, false, true, M * (ldq / 16));
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, ws);
   a.q = q;
   a.ldq = ldq;

@@ -12,6 +12,10 @@
 //   3. one thread per packed 32-bit word ternarizes its 16 weights and writes
 //      the word.  A wave writes one 256-byte quarter of a tile.
 // The fixed summation order makes beta reproducible bit for bit.
+//
+// Binary weights (BitNet b1, "BitNet / Ternary / Binary - Les LLMs 1-bit",
+// TL;DR: every weight +1 or -1) take the same beta and one bit per weight,
+// 1 for w >= 0, in 16 x 512 tiles (pack_b1_kernel).
 #include "bl_internal.h"
 
 namespace bl {
@@ -87,18 +91,59 @@ __global__ __launch_bounds__(256) void pack_t2_kernel(const float* __restrict__ 
   packed[idx] = word;
 }
 
-}  // namespace
+// Word `idx` of a B1 buffer: tile = idx / 256, lane L = (idx % 256) / 4,
+// dword d = idx % 4.  Bit 16*h + j of the word is weight
+// (16*nb + L%16, 512*kb + 64*(2*d + h) + 16*(L/16) + j), 1 where w >= 0.
+__global__ __launch_bounds__(256) void pack_b1_kernel(const float* __restrict__ w, int64_t N, int64_t K,
+                                                      int64_t Kt, uint32_t* __restrict__ packed, int64_t nwords) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nwords) return;
+  const int64_t tile = idx >> 8;
+  const int L = (int)((idx >> 2) & 63), d = (int)(idx & 3);
+  const int64_t nb = tile / Kt, kb = tile - nb * Kt;
+  const int64_t n = nb * kTileN + (L & 15);
+  uint32_t word = 0;
+  if (n < N) {
+    const float* row = w + n * K;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t k0 = kb * 512 + 64 * (2 * d + h) + 16 * (L >> 4);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t k = k0 + j;
+        if (k < K && row[k] >= 0.0f) word |= 1u << (16 * h + j);
+      }
+    }
+  }
+  packed[idx] = word;
+}
 
-hipError_t launch_pack_t2(const float* w, int64_t N, int64_t K, uint8_t* packed, float* beta,
-                          double* partials, hipStream_t s) {
-  const int64_t count = N * K;
+hipError_t launch_absmean(const float* w, int64_t count, float* beta, double* partials, hipStream_t s) {
   const int64_t nchunks = ceil_div(count, kBetaChunk);
   hipLaunchKernelGGL(absmean_chunks_kernel, dim3((unsigned)ceil_div(nchunks, 256)), dim3(256), 0, s,
                      w, count, nchunks, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(absmean_final_kernel, dim3(1), dim3(64), 0, s, partials, nchunks, count, beta);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack_b1(const float* w, int64_t N, int64_t K, uint8_t* packed, float* beta, double* partials,
+                          hipStream_t s) {
+  hipError_t e = launch_absmean(w, N * K, beta, partials, s);
+  if (e != hipSuccess) return e;
+  const int64_t Kt = ceil_div(K, kTileKB1), Nt = ceil_div(N, kTileN);
+  const int64_t nwords = Nt * Kt * (kTileBytes / 4);
+  hipLaunchKernelGGL(pack_b1_kernel, dim3((unsigned)ceil_div(nwords, 256)), dim3(256), 0, s, w, N, K, Kt,
+                     reinterpret_cast<uint32_t*>(packed), nwords);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_t2(const float* w, int64_t N, int64_t K, uint8_t* packed, float* beta,
+                          double* partials, hipStream_t s) {
+  hipError_t e = launch_absmean(w, N * K, beta, partials, s);
   if (e != hipSuccess) return e;
   const int64_t Kt = ceil_div(K, kTileK), Nt = ceil_div(N, kTileN);
   const int64_t nwords = Nt * Kt * (kTileBytes / 4);

@@ -79,8 +79,9 @@ const char *bitlinear_last_error(void);
 
 /*
  * Bytes per row of the int8 activation buffer x_q: K rounded up to a multiple
- * of 256.  Entries k >= K of each row are written as 0 by bitlinear_quant_act
- * and must stay 0.  Returns -1 for K outside [1, BITLINEAR_MAX_K].
+ * of 512 (the columns of a binary weight tile).  Entries k >= K of each row
+ * are written as 0 by bitlinear_quant_act and must stay 0.  Returns -1 for K
+ * outside [1, BITLINEAR_MAX_K].
  */
 int64_t bitlinear_act_stride(int64_t K);
 
@@ -91,7 +92,14 @@ int64_t bitlinear_act_stride(int64_t K);
  */
 int64_t bitlinear_packed_bytes(int64_t N, int64_t K);
 
-/* Workspace bytes bitlinear_pack_weights needs: 8 * ceil(N*K / 4096). */
+/*
+ * Size in bytes of packed binary weights (bitlinear_pack_weights_b1) for an
+ * N x K matrix: ceil(N/16) * ceil(K/512) * 1024 (1 bit per weight, padded to
+ * whole tiles).  Returns -1 for N or K outside the supported range.
+ */
+int64_t bitlinear_packed_bytes_b1(int64_t N, int64_t K);
+
+/* Workspace bytes bitlinear_pack_weights(_b1) needs: 8 * ceil(N*K / 4096). */
 int64_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
 
 /*
@@ -166,6 +174,32 @@ int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
                    const float *w_beta, int64_t N, void *y, int y_dtype, void *workspace,
                    size_t workspace_bytes, void *stream);
 
+/*
+ * Binary weights, BitNet b1 ("BitNet / Ternary / Binary - Les LLMs 1-bit",
+ * TL;DR and Mecanisme technique: every weight is exactly +1 or -1).
+ * bitlinear_pack_weights_b1: t = +1 where w >= 0, else -1 (the pages give no
+ * rule; zero maps to +1), beta as bitlinear_pack_weights; packed holds
+ * bitlinear_packed_bytes_b1(N, K) bytes: tile (nb, kb) of 16 rows x 512
+ * columns is 1024 bytes at offset (nb * ceil(K/512) + kb) * 1024; 32-bit word
+ * d of lane L (bytes 16*L + 4*d, little endian) holds in bit 16*h + j the
+ * weight (n = 16*nb + L%16, k = 512*kb + 64*(2*d + h) + 16*(L/16) + j),
+ * bit 1 = +1, bit 0 = -1; padding bits are 0.  Errors as bitlinear_pack_weights.
+ */
+int bitlinear_pack_weights_b1(const float *w, int64_t N, int64_t K, void *packed, float *w_beta,
+                              void *workspace, void *stream);
+
+/*
+ * Binary-weight product for few tokens: y = dequant(acc), acc[m][n] =
+ * sum_k q[m][k] * t[n][k] with t in {-1, +1}, dequantized exactly as
+ * bitlinear_gemv.  x_rowsum [M] int32 (required): the row sums written by
+ * bitlinear_quant_act for the same x_q.  Other arguments as bitlinear_gemv;
+ * uses no workspace.  M in [0, BITLINEAR_GEMV_MAX_M].
+ * Errors: ERR_ARG (null pointer, x_rowsum missing), ERR_SHAPE, ERR_ALIGN.
+ */
+int bitlinear_gemv_b1(const int8_t *x_q, const float *x_ds, const int32_t *x_rowsum, int64_t M,
+                      int64_t K, const void *packed, const float *w_beta, int64_t N, void *y,
+                      int y_dtype, void *stream);
+
 /* LDS budget of the decode kernels for int8 activation rows (see below). */
 #define BITLINEAR_DECODE_MAX_ACT_BYTES 58368
 
@@ -180,7 +214,7 @@ int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
  *   x       [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32,
  *           optionally | BITLINEAR_X_RMSNORM (element alignment).
  *   packed, w_beta, y, y_dtype  as bitlinear_gemv.
- * Needs M * (bitlinear_act_stride(K) + 16) <= BITLINEAR_DECODE_MAX_ACT_BYTES,
+ * Needs M * (K rounded up to 256, + 16) <= BITLINEAR_DECODE_MAX_ACT_BYTES,
  * else BITLINEAR_ERR_UNSUPPORTED (use bitlinear_quant_act + bitlinear_gemv).
  * Other errors as bitlinear_gemv.  Uses no workspace.
  */

@@ -47,9 +47,10 @@ def test_header_constants_match_binding():
 
 
 def test_size_helpers():
-    assert bl.act_stride(1) == 256
-    assert bl.act_stride(256) == 256
-    assert bl.act_stride(257) == 512
+    assert bl.act_stride(1) == 512
+    assert bl.act_stride(512) == 512
+    assert bl.act_stride(513) == 1024
+    assert bl.act_stride(6912) == 7168
     assert bl.act_stride(0) == -1
     assert bl.act_stride(bl.MAX_K + 1) == -1
     assert bl.packed_bytes(16, 256) == 1024
@@ -223,3 +224,21 @@ def test_multi_and_glu_validation():
     assert L.bitlinear_gemv_glu(FAKE, FAKE, 1, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE + 2, None) == bl.ERR_ALIGN
     assert L.bitlinear_forward_decode_glu(FAKE, bl.I32, 1, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == bl.ERR_ARG
     assert L.bitlinear_forward_decode_glu(FAKE, bl.BF16, 0, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE, None) == bl.OK
+
+
+def test_b1_sizes_and_validation():
+    assert bl.packed_bytes_b1(16, 512) == 1024
+    assert bl.packed_bytes_b1(17, 513) == 4 * 1024
+    assert bl.packed_bytes_b1(6912, 2560) == 6912 * 2560 // 8
+    assert bl.packed_bytes_b1(0, 5) == -1
+    L = bl.lib()
+    assert L.bitlinear_pack_weights_b1(None, 16, 512, FAKE, FAKE, FAKE, None) == bl.ERR_ARG
+    assert L.bitlinear_pack_weights_b1(FAKE, 0, 512, FAKE, FAKE, FAKE, None) == bl.ERR_SHAPE
+    assert L.bitlinear_pack_weights_b1(FAKE, 16, 512, FAKE + 8, FAKE, FAKE, None) == bl.ERR_ALIGN
+    fn = L.bitlinear_gemv_b1
+    assert fn(FAKE, FAKE, None, 1, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_ARG
+    assert "rowsum" in bl.last_error()
+    assert fn(FAKE, FAKE, FAKE + 2, 1, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_ALIGN
+    assert fn(FAKE, FAKE, FAKE, 65, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_SHAPE
+    assert fn(FAKE, FAKE, FAKE, 1, 512, FAKE, FAKE, 16, FAKE, 7, None) == bl.ERR_ARG
+    assert fn(None, None, None, 0, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.OK
