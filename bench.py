@@ -32,8 +32,9 @@ Also printed on the same JSON line:
   also          the other workloads: one decode step over the 30-layer 2B-class
                 stack (210 BitLinears + glue, batch 1 and 8) in tokens/s,
                 checked bit for bit against the oracle's chain; 100B-class
-                decode (M = 1, 8, 32) in GB/s; prefill GEMMs (2B M=2048,
-                100B M=512) in int8 TOPS.
+                decode (M = 1, 8, 32) in GB/s; binary-weight (b1) decode on
+                the 2B and 100B shapes (M = 1, 8); prefill GEMMs (2B M=2048,
+                100B M=512), ternary and binary, in int8 TOPS.
 """
 from __future__ import annotations
 
@@ -490,6 +491,75 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
     return res
 
 
+def decode_b1_extra(shapes, Ms, dev, steps=100):
+    """Binary weights (BitNet b1, 1 bit per weight): per BitLinear the
+    standalone quantizer then bitlinear_gemv_b1.  GB/s counts the packed
+    bytes (half of the 2-bit format); weights_per_s is the same stream in
+    weights per second, comparable across formats."""
+    res = {}
+    packs = []
+    for i, (K, N) in enumerate(shapes):
+        g = torch.Generator(device=dev).manual_seed(500 + i)
+        w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * workloads.W_STD
+        packs.append(bl.pack_weights_b1(w))
+        del w
+    per_step = sum(N * K // 8 for K, N in shapes)
+    R = rotation(per_step)
+    copies = [copies_of(p, R) for p, _ in packs]
+    for M in Ms:
+        bufs = []
+        for i, (K, N) in enumerate(shapes):
+            x = gpu_acts(M, K, 600 + i, dev)
+            bufs.append((x, torch.empty((M, bl.act_stride(K)), dtype=torch.int8, device=dev),
+                         torch.empty((M,), dtype=torch.float32, device=dev),
+                         torch.empty((M,), dtype=torch.int32, device=dev),
+                         torch.empty((M, N), dtype=torch.float32, device=dev)))
+
+        def step(r, quant=True):
+            for (K, N), (x, xq, xds, rs, y), c, (_, beta) in zip(shapes, bufs, copies, packs):
+                if quant:
+                    bl.bitlinear_quant_act(x, xq, xds, rs)
+                bl.bitlinear_gemv_b1(xq, xds, rs, K, c[r % R], beta, N, y)
+        g = capture(step, steps)
+        time_graph(g)
+        el, _ = time_graph(g)
+        step(0)
+        gk = capture(lambda r: step(r, quant=False), steps)
+        time_graph(gk)
+        elk, _ = time_graph(gk)
+        res["M%d" % M] = {"GB_s": round(per_step * steps / el / 1e9, 1),
+                          "gemv_GB_s": round(per_step * steps / elk / 1e9, 1),
+                          "us_per_step": round(el / steps * 1e6, 2),
+                          "weights_per_s_T": round(per_step * 8 * steps / el / 1e12, 3),
+                          "frac_hbm_gemv": round(per_step * steps / elk / 1e9 / HBM_PEAK_GBS, 4)}
+        del g, gk, bufs
+    del copies, packs
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_b1_extra(M, shapes, dev, reps=20):
+    """Binary-weight prefill GEMM (bitlinear_gemm_b1) TOPS on the same shapes."""
+    res = {}
+    for i, (K, N) in enumerate(shapes):
+        g = torch.Generator(device=dev).manual_seed(700 + i)
+        w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * workloads.W_STD
+        packed, beta = bl.pack_weights_b1(w)
+        del w
+        x_q, x_ds, rs = bl.quant_act(gpu_acts(M, K, 800 + i, dev), with_rowsum=True)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        g2 = capture(lambda r: bl.bitlinear_gemm_b1(x_q, x_ds, rs, K, packed, beta, N, y), reps)
+        time_graph(g2)
+        el, _ = time_graph(g2)
+        d = el / reps
+        tops = 2.0 * M * N * K / d / 1e12
+        res["%dx%d->%d" % (M, K, N)] = {"gemm_us": round(d * 1e6, 1), "TOPS": round(tops, 1),
+                                        "frac_mfma": round(tops / INT8_PEAK_TOPS, 4)}
+        del packed, x_q, y, g2
+        torch.cuda.empty_cache()
+    return res
+
+
 def prefill_extra(M, shapes, dev, reps=20):
     res = {}
     for i, (K, N) in enumerate(shapes):
@@ -561,8 +631,12 @@ def main():
         result["also"] = {
             "decode_step_2b_30l": decode_step(workloads.DECODE_STEP_BATCHES, dev),
             "decode_100b": decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
+            "decode_b1_2b": decode_b1_extra([(l.K, l.N) for l in workloads.DECODE_2B.linears], (1, 8), dev),
+            "decode_b1_100b": decode_b1_extra(workloads.SHAPES_100B, (1, 8), dev),
             "prefill_2b_m2048": prefill_extra(2048, ((2560, 6912), (6912, 2560)), dev),
             "prefill_100b_m512": prefill_extra(512, workloads.SHAPES_100B, dev),
+            "prefill_b1_2b_m2048": prefill_b1_extra(2048, ((2560, 6912), (6912, 2560)), dev),
+            "prefill_b1_100b_m512": prefill_b1_extra(512, workloads.SHAPES_100B, dev),
         }
     print(json.dumps(result), flush=True)
 

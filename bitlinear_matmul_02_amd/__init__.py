@@ -18,6 +18,7 @@ Functions carry the C names:
     bitlinear_forward_decode_glu(x, packed_gate, beta_gate, packed_up, beta_up, N, h)
     bitlinear_pack_weights_b1(w, packed, w_beta, workspace)      (binary weights)
     bitlinear_gemv_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
+    bitlinear_gemm_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
 An fp32 output tensor can be passed with ``accumulate=True`` to the product
 calls, which then add their result into it (``BITLINEAR_F32_ADD``); the calls
 that quantize activations take ``rmsnorm=True`` to RMS-normalize each row
@@ -48,7 +49,7 @@ EXPORTS = (
     "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode", "bitlinear_relu2_mul",
     "bitlinear_gemv_multi", "bitlinear_forward_decode_multi", "bitlinear_gemv_glu",
     "bitlinear_forward_decode_glu", "bitlinear_packed_bytes_b1", "bitlinear_pack_weights_b1",
-    "bitlinear_gemv_b1",
+    "bitlinear_gemv_b1", "bitlinear_gemm_b1",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_weights_b1.argtypes = [p, i64, i64, p, p, p, p]
     L.bitlinear_gemv_b1.restype = i32
     L.bitlinear_gemv_b1.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
+    L.bitlinear_gemm_b1.restype = i32
+    L.bitlinear_gemm_b1.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_relu2_mul.restype = i32
     L.bitlinear_relu2_mul.argtypes = [p, p, i64, p, p]
     L.bitlinear_gemv_multi.restype = i32
@@ -190,6 +193,12 @@ def bitlinear_pack_weights_b1(w, packed, w_beta, workspace, stream=None) -> None
 def bitlinear_gemv_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
     """y [M][N] = dequant(x_q . T^T) for binary weights, M <= 64 tokens."""
     _check(lib().bitlinear_gemv_b1(_ptr(x_q), _ptr(x_ds), _ptr(x_rowsum), x_ds.shape[0], K, _ptr(packed),
+                                   _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate), _stream(stream)))
+
+
+def bitlinear_gemm_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
+    """The binary-weight product for any number of tokens, on the int8 matrix cores."""
+    _check(lib().bitlinear_gemm_b1(_ptr(x_q), _ptr(x_ds), _ptr(x_rowsum), x_ds.shape[0], K, _ptr(packed),
                                    _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate), _stream(stream)))
 
 

@@ -191,6 +191,19 @@ int bitlinear_gemv_b1(const int8_t* x_q, const float* x_ds, const int32_t* x_row
                     fn);
 }
 
+int bitlinear_gemm_b1(const int8_t* x_q, const float* x_ds, const int32_t* x_rowsum, int64_t M, int64_t K,
+                      const void* packed, const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
+  const char* fn = "bitlinear_gemm_b1";
+  int st = check_product(fn, x_q, x_ds, M, BITLINEAR_MAX_M, K, packed, w_beta, N, y, y_dtype, nullptr, 0, 0);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  if (!x_rowsum) return fail(BITLINEAR_ERR_ARG, "%s: x_rowsum is required", fn);
+  if (!aligned(x_rowsum, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_rowsum not element aligned", fn);
+  return hip_status(bl::launch_gemm_b1(x_q, act_stride(K), x_ds, x_rowsum, M, K, static_cast<const uint8_t*>(packed),
+                                       w_beta, N, y, y_dtype, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_forward_decode(const void* x, int x_dtype, int64_t M, int64_t K, const void* packed,
                              const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
   const char* fn = "bitlinear_forward_decode";

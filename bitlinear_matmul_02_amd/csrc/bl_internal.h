@@ -67,6 +67,9 @@ hipError_t launch_gemv_b1(const int8_t* q, int64_t ldq, const float* ds, const i
                           int64_t K, const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype,
                           hipStream_t s);
 
+hipError_t launch_gemm_b1(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
+                          const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s);
+
 hipError_t launch_relu2_mul(const float* g, const float* u, int64_t count, float* h, hipStream_t s);
 
 // ------------------------------------------------------- device helpers

@@ -34,26 +34,37 @@
 //     weight tiles keep their 1 KB lane-major layout (conflict-free reads);
 //   * each MFMA step's next operands (LDS reads, 2-bit expansion) are issued
 //     while the current step's MFMAs run.
+// Binary weights (BitNet b1, "BitNet / Ternary / Binary - Les LLMs 1-bit",
+// TL;DR: weights +1 or -1) use 16 x 512 tiles of one bit per weight (format
+// B1): a 256-column k-step reads dwords 2 (kt % 2) and 2 (kt % 2) + 1 of
+// every lane of the tile, i.e. an 8-byte half of each lane's chunk.  Step s
+// of the k-step takes, from tile lane 16 * (2 (s % 2) + g) + n % 16, the 16
+// bits of dword s / 4, half (s / 2) % 2; they become 16 bytes in {0, 1} and
+// the epilogue takes 2 * sum(q * b) - rowsum(q).
+//
 // Workgroups are numbered so that each of the 8 XCDs (blocks are dealt to
 // them round-robin) works on a contiguous run of output tiles, walked in
 // groups of 4 token blocks along N, which share both operands in its L2.
 #include <mutex>
+#include <type_traits>
 
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
-template <int BM, int BN>
+template <int BM, int BN, int FMT = 0>
 struct GemmTile {
   static constexpr int WGM = 2, WGN = 4;              // waves along M x along N
   static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave block
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA tiles per wave
   static constexpr int SLAB_A = BM * kTileK;          // activation slab bytes
-  static constexpr int SLAB_B = BN / kTileN * kTileBytes;  // weight slab bytes
+  static constexpr int TB = FMT ? kTileBytes / 2 : kTileBytes;  // weight bytes per 16-row tile per k-step
+  static constexpr int SLAB_B = BN / kTileN * TB;     // weight slab bytes
+  static constexpr int BP = FMT ? 8 : 16;             // bytes per weight piece
   static constexpr int PA = SLAB_A / 16 / NT;         // 16-byte pieces per thread
-  static constexpr int PB = SLAB_B / 16 / NT;
+  static constexpr int PB = SLAB_B / BP / NT;
   static constexpr int LDS = 2 * (SLAB_A + SLAB_B);   // double-buffered
 };
 
@@ -67,13 +78,24 @@ __device__ inline int xcd_tile(int b, int T) {
   return start + i;
 }
 
-template <int BM, int BN, int D>
+// Step s of a B1 chunk pair: 16 bits -> 16 bytes in {0, 1} (bit j -> byte j).
+__device__ inline v4i b1_bytes(uint32_t bits16) {
+  v4i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = (int)((((bits16 >> (4 * q)) & 0xFu) * 0x00204081u) & 0x01010101u);
+  return r;
+}
+
+template <int BM, int BN, int D, int FMT>
 __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__ q, int64_t ldq,
-                                                      const float* __restrict__ ds, int M,
-                                                      const u4* __restrict__ packed,
+                                                      const float* __restrict__ ds,
+                                                      const int32_t* __restrict__ rowsum, int M,
+                                                      const uint8_t* __restrict__ packed,
                                                       const float* __restrict__ beta, int N, int Nt,
-                                                      int Kt, int tiles_n, void* __restrict__ y, int y_dtype) {
-  using G = GemmTile<BM, BN>;
+                                                      int Kt, int KtW, int tiles_n, void* __restrict__ y,
+                                                      int y_dtype) {
+  using G = GemmTile<BM, BN, FMT>;
+  using BT = typename std::conditional<FMT != 0, uint2, u4>::type;  // one weight piece
   constexpr int MB = G::MB, NB = G::NB;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
   // LDS: activation halves [0, 2 SLAB_A), then weight halves
@@ -109,13 +131,16 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
     const int s = p * G::NT + tid, row = s >> 4;
     asrc[p] = q + (int64_t)min(m0 + row, M - 1) * ldq + (((s & 15) ^ (row & 15)) * 16);
   }
-  // weight pieces this thread moves: piece c = p*NT + tid is 16-byte piece
-  // c % 64 of local tile c / 64; tiles past Nt read the last tile
-  const u4* bsrc[G::PB];
+  // weight pieces this thread moves: piece c = p*NT + tid is lane c % 64's
+  // piece of local tile c / 64 (T2: the lane's 16 bytes; B1: the 8-byte half
+  // of them this k-step reads); tiles past Nt read the last tile.  KtW is the
+  // number of weight tiles per 16-row block (1 KB each).
+  const BT* bsrc[G::PB];
 #pragma unroll
   for (int p = 0; p < G::PB; ++p) {
     const int c = p * G::NT + tid;
-    bsrc[p] = packed + (int64_t)min(nt0 + (c >> 6), Nt - 1) * Kt * 64 + (c & 63);
+    bsrc[p] = reinterpret_cast<const BT*>(packed + (int64_t)min(nt0 + (c >> 6), Nt - 1) * KtW * kTileBytes) +
+              (FMT ? 2 * (c & 63) : (c & 63));
   }
   // this lane's weight chunks in the LDS slab: block j, chunk h
   int boff[NB][2];
@@ -124,25 +149,36 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int lt = (wn * G::WN + 32 * j + r32) >> 4;  // local 16-row tile
-      boff[j][h] = lt * kTileBytes + (16 * (2 * h + g2) + (r32 & 15)) * 16;
+      boff[j][h] = lt * G::TB + (16 * (2 * h + g2) + (r32 & 15)) * G::BP;
     }
   // LDS rows of this lane's activation operands; the swizzle term only
   // depends on r32 because every block starts on a multiple of 16 rows
   const int arow0 = wm * G::WM + r32;
 
   u4 aring[D][G::PA];
-  u4 bring[D][G::PB];
+  BT bring[D][G::PB];
   auto load = [&](int u, int kt) {
 #pragma unroll
     for (int p = 0; p < G::PA; ++p) aring[u][p] = *reinterpret_cast<const u4*>(asrc[p] + (int64_t)kt * kTileK);
 #pragma unroll
-    for (int p = 0; p < G::PB; ++p) bring[u][p] = bsrc[p][(int64_t)kt * 64];
+    for (int p = 0; p < G::PB; ++p)
+      bring[u][p] = FMT ? bsrc[p][(int64_t)(kt >> 1) * (kTileBytes / 8) + (kt & 1)] : bsrc[p][(int64_t)kt * 64];
   };
   auto stage_piece = [&](int u, int buf, int i) {  // i in [0, PA + PB)
     if (i < G::PA)
       *reinterpret_cast<u4*>(slabA(buf) + (i * G::NT + tid) * 16) = aring[u][i];
     else
-      *reinterpret_cast<u4*>(slabB(buf) + ((i - G::PA) * G::NT + tid) * 16) = bring[u][i - G::PA];
+      *reinterpret_cast<BT*>(slabB(buf) + ((i - G::PA) * G::NT + tid) * G::BP) = bring[u][i - G::PA];
+  };
+  // MFMA operand of step st from this lane's chunk pair
+  auto expand = [&](const BT (&ch)[2], int st) -> v4i {
+    if constexpr (FMT != 0) {
+      const uint2 c = ch[st & 1];
+      const uint32_t dw = (st >> 2) ? c.y : c.x;
+      return b1_bytes((dw >> (16 * ((st >> 1) & 1))) & 0xFFFFu);
+    } else {
+      return t2_field(ch[st & 1], st >> 1);
+    }
   };
   auto read_a = [&](v4i (&a)[MB], int buf, int s_) {
     const int c = 2 * s_ + g2;  // 16-byte piece: columns 32s + 16g
@@ -154,23 +190,23 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
   // One k-step: 8 MFMA steps s = 2f + h, software-pipelined; the next
   // k-step's pieces are written to the other LDS half along the way.
   auto compute = [&](int buf, bool stage_next, int unext) {
-    u4 wch[NB][2];
+    BT wch[NB][2];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) wch[j][h] = *reinterpret_cast<const u4*>(slabB(buf) + boff[j][h]);
+      for (int h = 0; h < 2; ++h) wch[j][h] = *reinterpret_cast<const BT*>(slabB(buf) + boff[j][h]);
     v4i a[2][MB];
     v4i b[2][NB];
     read_a(a[0], buf, 0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) b[0][j] = t2_field(wch[j][0], 0);
+    for (int j = 0; j < NB; ++j) b[0][j] = expand(wch[j], 0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const int cur = st & 1, nx = cur ^ 1;
       if (st + 1 < 8) {
         read_a(a[nx], buf, st + 1);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) b[nx][j] = t2_field(wch[j][(st + 1) & 1], (st + 1) >> 1);
+        for (int j = 0; j < NB; ++j) b[nx][j] = expand(wch[j], st + 1);
       }
       if (stage_next) {
 #pragma unroll
@@ -221,30 +257,44 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
       const int m = m0 + wm * G::WM + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
       if (m >= M) continue;
       const float scale = ds[m] * bt;
+      const int rs = FMT ? rowsum[m] : 0;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int n = n_wave + 32 * j + r32;
-        if (n < N) store_out(y, y_dtype, (int64_t)m * N + n, acc[mb][j][e], scale);
+        // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum, scaled like the T2 sums (64 t)
+        const int v = FMT ? (2 * acc[mb][j][e] - rs) * 64 : acc[mb][j][e];
+        if (n < N) store_out(y, y_dtype, (int64_t)m * N + n, v, scale);
       }
     }
 }
 
-template <int BM, int BN, int D>
-hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, const uint8_t* packed,
-                       const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
-  using G = GemmTile<BM, BN>;
+template <int BM, int BN, int D, int FMT>
+hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
+                       const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+  using G = GemmTile<BM, BN, FMT>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   });
   if (attr != hipSuccess) return attr;
   const int Nt = (int)ceil_div(N, kTileN), Kt = (int)ceil_div(K, kTileK);
+  const int KtW = (int)ceil_div(K, FMT ? kTileKB1 : kTileK);
   const int tiles_n = (int)ceil_div(N, BN), tiles_m = (int)ceil_div(M, BM);
-  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D>), dim3((unsigned)(tiles_m * tiles_n)), dim3(G::NT), G::LDS, s, q,
-                     ldq, ds, (int)M, reinterpret_cast<const u4*>(packed), beta, (int)N, Nt, Kt, tiles_n, y, y_dtype);
+  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D, FMT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(G::NT), G::LDS, s,
+                     q, ldq, ds, rowsum, (int)M, packed, beta, (int)N, Nt, Kt, KtW, tiles_n, y, y_dtype);
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
+                      const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+  // 128 x 256 blocks when that still gives a few hundred workgroups,
+  // 128 x 128 otherwise
+  const int64_t big = ceil_div(M, 128) * ceil_div(N, 256);
+  if (big >= 384) return launch_tile<128, 256, 2, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s);
+  return launch_tile<128, 128, 2, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s);
 }
 
 }  // namespace
@@ -254,11 +304,12 @@ int64_t gemm_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
 hipError_t launch_gemm_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void*, hipStream_t s) {
-  // 128 x 256 blocks when that still gives a few hundred workgroups,
-  // 128 x 128 otherwise
-  const int64_t big = ceil_div(M, 128) * ceil_div(N, 256);
-  if (big >= 384) return launch_tile<128, 256, 2>(q, ldq, ds, M, K, packed, beta, N, y, y_dtype, s);
-  return launch_tile<128, 128, 2>(q, ldq, ds, M, K, packed, beta, N, y, y_dtype, s);
+  return launch_fmt<0>(q, ldq, ds, nullptr, M, K, packed, beta, N, y, y_dtype, s);
+}
+
+hipError_t launch_gemm_b1(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
+                          const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+  return launch_fmt<1>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s);
 }
 
 }  // namespace bl

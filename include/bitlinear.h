@@ -200,6 +200,12 @@ int bitlinear_gemv_b1(const int8_t *x_q, const float *x_ds, const int32_t *x_row
                       int64_t K, const void *packed, const float *w_beta, int64_t N, void *y,
                       int y_dtype, void *stream);
 
+/* The same binary-weight product for any number of tokens (prefill), on the
+ * int8 matrix cores.  Arguments as bitlinear_gemv_b1; M in [0, BITLINEAR_MAX_M]. */
+int bitlinear_gemm_b1(const int8_t *x_q, const float *x_ds, const int32_t *x_rowsum, int64_t M,
+                      int64_t K, const void *packed, const float *w_beta, int64_t N, void *y,
+                      int y_dtype, void *stream);
+
 /* LDS budget of the decode kernels for int8 activation rows (see below). */
 #define BITLINEAR_DECODE_MAX_ACT_BYTES 58368
 

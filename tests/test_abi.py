@@ -235,6 +235,10 @@ def test_b1_sizes_and_validation():
     assert L.bitlinear_pack_weights_b1(None, 16, 512, FAKE, FAKE, FAKE, None) == bl.ERR_ARG
     assert L.bitlinear_pack_weights_b1(FAKE, 0, 512, FAKE, FAKE, FAKE, None) == bl.ERR_SHAPE
     assert L.bitlinear_pack_weights_b1(FAKE, 16, 512, FAKE + 8, FAKE, FAKE, None) == bl.ERR_ALIGN
+    fn = L.bitlinear_gemm_b1
+    assert fn(FAKE, FAKE, None, 1, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_ARG
+    assert fn(FAKE, FAKE, FAKE, 1 << 21, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_SHAPE
+    assert fn(None, None, None, 0, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.OK
     fn = L.bitlinear_gemv_b1
     assert fn(FAKE, FAKE, None, 1, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_ARG
     assert "rowsum" in bl.last_error()

@@ -35,13 +35,13 @@ def test_pack_b1_parity(N, K):
     assert beta.cpu().numpy()[0] == oracle.absmean(w)
 
 
-def gpu_b1(xb, w, out_dtype):
+def gpu_b1(xb, w, out_dtype, gemm=False):
     M, K = xb.shape
     N = w.shape[0]
     packed, beta = bl.pack_weights_b1(torch.from_numpy(w).to(DEV))
     x_q, x_ds, rs = bl.quant_act(to_dev_bf16(xb), with_rowsum=True)
     y = torch.empty((M, N), dtype=out_dtype, device=DEV)
-    bl.bitlinear_gemv_b1(x_q, x_ds, rs, K, packed, beta, N, y)
+    (bl.bitlinear_gemm_b1 if gemm else bl.bitlinear_gemv_b1)(x_q, x_ds, rs, K, packed, beta, N, y)
     torch.cuda.synchronize()
     return y
 
@@ -89,3 +89,17 @@ def test_gemv_b1_empty_batch():
     y = torch.zeros((0, 16), dtype=torch.float32, device=DEV)
     bl.bitlinear_gemv_b1(x_q, x_ds, rs, 512, packed, beta, 16, y)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 512, 16), (65, 1030, 48), (128, 2560, 256), (129, 768, 300), (300, 6912, 640),
+                                   (2048, 2560, 512), (256, 13, 20)])
+def test_gemm_b1_parity(M, K, N):
+    w = workloads.gen_weights(N, K, seed=M * 11 + K + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=M + 2 * K)
+    xb[M // 3] = 0
+    ref = oracle.bitlinear_forward_b1(xb, w, threads=8)
+    acc = gpu_b1(xb, w, torch.int32, gemm=True).cpu().numpy()
+    np.testing.assert_array_equal(acc, ref["acc"])
+    y = gpu_b1(xb, w, torch.float32, gemm=True).cpu().numpy()
+    assert rel_ok(y, ref["y"], 1e-3)
+    np.testing.assert_array_equal(y, ref["y"])
