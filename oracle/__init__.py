@@ -76,6 +76,12 @@ def _load():
     lib.oracle_pack_b1.argtypes = [p, i64, i64, p]
     lib.oracle_unpack_b1.restype = None
     lib.oracle_unpack_b1.argtypes = [p, i64, i64, p]
+    lib.oracle_b3_bytes.restype = i64
+    lib.oracle_b3_bytes.argtypes = [i64, i64]
+    lib.oracle_pack_b3.restype = None
+    lib.oracle_pack_b3.argtypes = [p, i64, i64, p]
+    lib.oracle_unpack_b3.restype = None
+    lib.oracle_unpack_b3.argtypes = [p, i64, i64, p]
     lib.oracle_rmsnorm_f32.restype = None
     lib.oracle_rmsnorm_f32.argtypes = [p, i64, i64, p]
     _lib = lib
@@ -252,6 +258,27 @@ def unpack_b1(packed: np.ndarray, N: int, K: int) -> np.ndarray:
     assert packed.size >= b1_bytes(N, K)
     t = np.empty((N, K), dtype=np.int8)
     _load().oracle_unpack_b1(_ptr(packed), N, K, _ptr(t))
+    return t
+
+
+def b3_bytes(N: int, K: int) -> int:
+    return int(_load().oracle_b3_bytes(N, K))
+
+
+def pack_b3(t: np.ndarray) -> np.ndarray:
+    """Ternary codes [N][K] -> base-3 tiles (five weights per byte)."""
+    t = _c(t, np.int8)
+    N, K = t.shape
+    out = np.empty(b3_bytes(N, K), dtype=np.uint8)
+    _load().oracle_pack_b3(_ptr(t), N, K, _ptr(out))
+    return out
+
+
+def unpack_b3(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = _c(packed, np.uint8)
+    assert packed.size >= b3_bytes(N, K)
+    t = np.empty((N, K), dtype=np.int8)
+    _load().oracle_unpack_b3(_ptr(packed), N, K, _ptr(t))
     return t
 
 

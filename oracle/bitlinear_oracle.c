@@ -41,6 +41,11 @@
  *      TL;DR and Mecanisme technique: every weight is exactly +1 or -1), one
  *      bit per weight; its layout is this project's own choice, written here
  *      from its specification.
+ *  - oracle_pack_b3 / oracle_unpack_b3: ternary weights five to a byte in
+ *      base 3 (1.6 bits per weight; "BitNet Technical Notes" and the
+ *      "BitNet: Inference framework for 1-bit LLMs" thread discuss packing
+ *      trits more densely than 2 bits); the layout is this project's own
+ *      choice, written here from its specification.
  *  - oracle_pack_t2 / oracle_unpack_t2: 2 bits per ternary weight
  *      ("BitNet Technical Notes", Appendix glossary: bit-packing at 2 bits per
  *      ternary weight; "BitNet: Inference framework for 1-bit LLMs", post #139:
@@ -344,6 +349,52 @@ void oracle_unpack_b1(const uint8_t *packed, int64_t N, int64_t K, int8_t *t)
             int64_t bit = 16 * h + j;
             int64_t byte = (nb * Kt + kb) * 1024 + 16 * L + 4 * d + bit / 8;
             t[n * K + k] = (packed[byte] >> (bit % 8)) & 1 ? 1 : -1;
+        }
+}
+
+/*
+ * Format B3 (five ternary weights per byte, base 3).  Tiles of 16 rows x 320
+ * columns; tile (nb, kb) is 1024 bytes at byte offset (nb * ceil(K/320) + kb)
+ * * 1024.  Byte 16*L + i of a tile (L in 0..63, i in 0..15) is
+ *     sum_{s=0..4} c_s * 3^s,  c_s = t(n, k_s) + 1 in {0, 1, 2},
+ *     n = 16*nb + (L mod 16),  k_s = 320*kb + 64*s + 16*(L div 16) + i.
+ * Positions with n >= N or k >= K contribute c = 0.
+ */
+int64_t oracle_b3_bytes(int64_t N, int64_t K)
+{
+    return ((N + 15) / 16) * ((K + 319) / 320) * 1024;
+}
+
+void oracle_pack_b3(const int8_t *t, int64_t N, int64_t K, uint8_t *packed)
+{
+    static const int pow3[5] = {1, 3, 9, 27, 81};
+    int64_t Kt = (K + 319) / 320;
+    memset(packed, 0, (size_t)oracle_b3_bytes(N, K));
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t nb = n / 16, kb = k / 320;
+            int64_t r = n % 16, c = k % 320;
+            int64_t s = c / 64, g = (c % 64) / 16, i = c % 16;
+            int64_t L = 16 * g + r;
+            int64_t byte = (nb * Kt + kb) * 1024 + 16 * L + i;
+            packed[byte] = (uint8_t)(packed[byte] + (t[n * K + k] + 1) * pow3[s]);
+        }
+}
+
+/* Inverse of oracle_pack_b3 over the N x K weights. */
+void oracle_unpack_b3(const uint8_t *packed, int64_t N, int64_t K, int8_t *t)
+{
+    int64_t Kt = (K + 319) / 320;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t nb = n / 16, kb = k / 320;
+            int64_t r = n % 16, c = k % 320;
+            int64_t s = c / 64, g = (c % 64) / 16, i = c % 16;
+            int64_t L = 16 * g + r;
+            int v = packed[(nb * Kt + kb) * 1024 + 16 * L + i];
+            for (int64_t j = 0; j < s; ++j)
+                v /= 3;
+            t[n * K + k] = (int8_t)(v % 3 - 1);
         }
 }
 

@@ -604,3 +604,74 @@ def test_forward_b1_bound():
     approx = x @ (float(out["beta"]) * out["t"].astype(np.float64)).T
     bound = (out["ds"][:, None].astype(np.float64) / 2) * float(out["beta"]) * 512
     assert np.all(np.abs(out["y"] - approx) <= bound * (1 + 1e-6) + 1e-6)
+
+
+# ------------------------------------------------------------- base-3 packing (b3)
+def _mfma_sim_b3(packed, q, N, K):
+    """acc = q . t^T computed the way the matrix cores consume base-3 tiles:
+    for step s of a 320-column tile, lane (n, g) supplies the base-3 digit s
+    of its 16 bytes as operand bytes c in {0, 1, 2} (column 64 s + 16 g + j
+    from byte j), and sum q * c - rowsum(q) = sum q * (c - 1)."""
+    M = q.shape[0]
+    Kt, Nt = -(-K // 320), -(-N // 16)
+    qp = np.zeros((M, Kt * 320), dtype=np.int64)
+    qp[:, :K] = q
+    acc = np.zeros((M, Nt * 16), dtype=np.int64)
+    tiles = packed.reshape(Nt, Kt, 64, 16).astype(np.int64)
+    for nb in range(Nt):
+        for kb in range(Kt):
+            for s in range(5):
+                digits = (tiles[nb, kb] // 3 ** s) % 3  # [lane][byte]
+                for lane in range(64):
+                    n, g = lane % 16, lane // 16
+                    cols = kb * 320 + 64 * s + 16 * g + np.arange(16)
+                    acc[:, nb * 16 + n] += qp[:, cols] @ digits[lane]
+    return acc[:, :N] - q.astype(np.int64).sum(1, keepdims=True)
+
+
+@pytest.mark.parametrize("N,K", [(16, 320), (17, 700), (5, 1030)])
+def test_pack_b3_feeds_the_matrix_core_contraction(N, K):
+    rng = np.random.default_rng(N * 3 + K)
+    t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    q = rng.integers(-127, 128, size=(3, K)).astype(np.int8)
+    p = oracle.pack_b3(t)
+    assert p.size == -(-N // 16) * -(-K // 320) * 1024 == oracle.b3_bytes(N, K)
+    assert p.max() <= 242
+    np.testing.assert_array_equal(_mfma_sim_b3(p, q, N, K), q.astype(np.int64) @ t.astype(np.int64).T)
+
+
+def test_pack_b3_closed_forms_and_round_trip():
+    # all-zero weights: every byte of a full tile is 1 + 3 + 9 + 27 + 81 = 121
+    p = oracle.pack_b3(np.zeros((16, 320), dtype=np.int8))
+    assert np.all(p == 121)
+    # all +1: 2 * 121 = 242, all -1: 0
+    assert np.all(oracle.pack_b3(np.ones((16, 320), dtype=np.int8)) == 242)
+    assert not oracle.pack_b3(-np.ones((16, 320), dtype=np.int8)).any()
+    # padding contributes nothing: a 1 x 1 zero weight sets digit 0 of byte 0 only
+    p = oracle.pack_b3(np.zeros((1, 1), dtype=np.int8))
+    assert p[0] == 1 and not p[1:].any()
+    # one weight at (3, 200): step 3, group 0, byte 8 of lane 3 -> +2 * 27 over the -1 background
+    t = -np.ones((16, 320), dtype=np.int8)
+    t[3, 200] = 1
+    p = oracle.pack_b3(t)
+    assert np.flatnonzero(p).tolist() == [16 * 3 + 8] and p[16 * 3 + 8] == 2 * 27
+    rng = np.random.default_rng(13)
+    for N, K in ((1, 1), (33, 1100), (7, 321), (64, 2560)):
+        t = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+        np.testing.assert_array_equal(oracle.unpack_b3(oracle.pack_b3(t), N, K), t)
+
+
+def test_b3_digits_cover_every_byte_value():
+    # every byte value 0..242 is reachable and decodes to its base-3 digits
+    vals = np.arange(243)
+    digits = np.stack([(vals // 3 ** s) % 3 for s in range(5)], 1)  # [243][5]
+    t = np.zeros((16, 320), dtype=np.int8)
+    for v in range(243):
+        lane, i = divmod(v, 16)
+        if lane >= 64:
+            break
+        n, g = lane % 16, lane // 16
+        for s in range(5):
+            t[n, 64 * s + 16 * g + i] = digits[v, s] - 1
+    p = oracle.pack_b3(t).reshape(64, 16)
+    np.testing.assert_array_equal(p.reshape(-1)[:243], vals)
