@@ -32,8 +32,8 @@ Also printed on the same JSON line:
   also          the other workloads: one decode step over the 30-layer 2B-class
                 stack (210 BitLinears + glue, batch 1 and 8) in tokens/s,
                 checked bit for bit against the oracle's chain; 100B-class
-                decode (M = 1, 8, 32) in GB/s; binary-weight (b1) decode on
-                the 2B and 100B shapes (M = 1, 8); prefill GEMMs (2B M=2048,
+                decode (M = 1, 8, 32) in GB/s; binary-weight (b1) and base-3
+                (b3) decode on the 2B and 100B shapes (M = 1, 8); prefill GEMMs (2B M=2048,
                 100B M=512), ternary and binary, in int8 TOPS.
 """
 from __future__ import annotations
@@ -491,19 +491,23 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
     return res
 
 
-def decode_b1_extra(shapes, Ms, dev, steps=100):
-    """Binary weights (BitNet b1, 1 bit per weight): per BitLinear the
-    standalone quantizer then bitlinear_gemv_b1.  GB/s counts the packed
-    bytes (half of the 2-bit format); weights_per_s is the same stream in
-    weights per second, comparable across formats."""
+def decode_fmt_extra(fmt, shapes, Ms, dev, steps=100):
+    """Other weight formats at decode: "b1" binary weights (BitNet b1, 1 bit
+    per weight, bitlinear_gemv_b1) or "b3" ternary weights five to a byte
+    (1.6 bits, bitlinear_gemv_b3); per BitLinear the standalone quantizer
+    then the product.  GB/s counts the packed bytes; weights_per_s is the same
+    stream in weights per second, comparable across formats."""
+    pack_fn = bl.pack_weights_b1 if fmt == "b1" else bl.pack_weights_b3
+    gemv_fn = bl.bitlinear_gemv_b1 if fmt == "b1" else bl.bitlinear_gemv_b3
     res = {}
     packs = []
     for i, (K, N) in enumerate(shapes):
         g = torch.Generator(device=dev).manual_seed(500 + i)
         w = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * workloads.W_STD
-        packs.append(bl.pack_weights_b1(w))
+        packs.append(pack_fn(w))
         del w
-    per_step = sum(N * K // 8 for K, N in shapes)
+    per_step = sum(p.numel() for p, _ in packs)
+    weights = sum(N * K for K, N in shapes)
     R = rotation(per_step)
     copies = [copies_of(p, R) for p, _ in packs]
     for M in Ms:
@@ -519,7 +523,7 @@ def decode_b1_extra(shapes, Ms, dev, steps=100):
             for (K, N), (x, xq, xds, rs, y), c, (_, beta) in zip(shapes, bufs, copies, packs):
                 if quant:
                     bl.bitlinear_quant_act(x, xq, xds, rs)
-                bl.bitlinear_gemv_b1(xq, xds, rs, K, c[r % R], beta, N, y)
+                gemv_fn(xq, xds, rs, K, c[r % R], beta, N, y)
         g = capture(step, steps)
         time_graph(g)
         el, _ = time_graph(g)
@@ -530,7 +534,7 @@ def decode_b1_extra(shapes, Ms, dev, steps=100):
         res["M%d" % M] = {"GB_s": round(per_step * steps / el / 1e9, 1),
                           "gemv_GB_s": round(per_step * steps / elk / 1e9, 1),
                           "us_per_step": round(el / steps * 1e6, 2),
-                          "weights_per_s_T": round(per_step * 8 * steps / el / 1e12, 3),
+                          "weights_per_s_T": round(weights * steps / el / 1e12, 3),
                           "frac_hbm_gemv": round(per_step * steps / elk / 1e9 / HBM_PEAK_GBS, 4)}
         del g, gk, bufs
     del copies, packs
@@ -631,8 +635,10 @@ def main():
         result["also"] = {
             "decode_step_2b_30l": decode_step(workloads.DECODE_STEP_BATCHES, dev),
             "decode_100b": decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
-            "decode_b1_2b": decode_b1_extra([(l.K, l.N) for l in workloads.DECODE_2B.linears], (1, 8), dev),
-            "decode_b1_100b": decode_b1_extra(workloads.SHAPES_100B, (1, 8), dev),
+            "decode_b1_2b": decode_fmt_extra("b1", [(l.K, l.N) for l in workloads.DECODE_2B.linears], (1, 8), dev),
+            "decode_b1_100b": decode_fmt_extra("b1", workloads.SHAPES_100B, (1, 8), dev),
+            "decode_b3_2b": decode_fmt_extra("b3", [(l.K, l.N) for l in workloads.DECODE_2B.linears], (1, 8), dev),
+            "decode_b3_100b": decode_fmt_extra("b3", workloads.SHAPES_100B, (1, 8), dev),
             "prefill_2b_m2048": prefill_extra(2048, ((2560, 6912), (6912, 2560)), dev),
             "prefill_100b_m512": prefill_extra(512, workloads.SHAPES_100B, dev),
             "prefill_b1_2b_m2048": prefill_b1_extra(2048, ((2560, 6912), (6912, 2560)), dev),

@@ -19,6 +19,8 @@ Functions carry the C names:
     bitlinear_pack_weights_b1(w, packed, w_beta, workspace)      (binary weights)
     bitlinear_gemv_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
     bitlinear_gemm_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
+    bitlinear_pack_weights_b3(w, packed, w_beta, workspace)      (base-3 ternary)
+    bitlinear_gemv_b3(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
 An fp32 output tensor can be passed with ``accumulate=True`` to the product
 calls, which then add their result into it (``BITLINEAR_F32_ADD``); the calls
 that quantize activations take ``rmsnorm=True`` to RMS-normalize each row
@@ -49,7 +51,8 @@ EXPORTS = (
     "bitlinear_gemv", "bitlinear_gemm", "bitlinear_forward_decode", "bitlinear_relu2_mul",
     "bitlinear_gemv_multi", "bitlinear_forward_decode_multi", "bitlinear_gemv_glu",
     "bitlinear_forward_decode_glu", "bitlinear_packed_bytes_b1", "bitlinear_pack_weights_b1",
-    "bitlinear_gemv_b1", "bitlinear_gemm_b1",
+    "bitlinear_gemv_b1", "bitlinear_gemm_b1", "bitlinear_packed_bytes_b3", "bitlinear_pack_weights_b3",
+    "bitlinear_gemv_b3",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -104,6 +107,12 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_weights_b1.argtypes = [p, i64, i64, p, p, p, p]
     L.bitlinear_gemv_b1.restype = i32
     L.bitlinear_gemv_b1.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
+    L.bitlinear_packed_bytes_b3.restype = i64
+    L.bitlinear_packed_bytes_b3.argtypes = [i64, i64]
+    L.bitlinear_pack_weights_b3.restype = i32
+    L.bitlinear_pack_weights_b3.argtypes = [p, i64, i64, p, p, p, p]
+    L.bitlinear_gemv_b3.restype = i32
+    L.bitlinear_gemv_b3.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_gemm_b1.restype = i32
     L.bitlinear_gemm_b1.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_relu2_mul.restype = i32
@@ -150,6 +159,10 @@ def packed_bytes(N: int, K: int) -> int:
 
 def packed_bytes_b1(N: int, K: int) -> int:
     return int(lib().bitlinear_packed_bytes_b1(N, K))
+
+
+def packed_bytes_b3(N: int, K: int) -> int:
+    return int(lib().bitlinear_packed_bytes_b3(N, K))
 
 
 def pack_workspace_bytes(N: int, K: int) -> int:
@@ -199,6 +212,19 @@ def bitlinear_gemv_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None,
 def bitlinear_gemm_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
     """The binary-weight product for any number of tokens, on the int8 matrix cores."""
     _check(lib().bitlinear_gemm_b1(_ptr(x_q), _ptr(x_ds), _ptr(x_rowsum), x_ds.shape[0], K, _ptr(packed),
+                                   _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate), _stream(stream)))
+
+
+def bitlinear_pack_weights_b3(w, packed, w_beta, workspace, stream=None) -> None:
+    """w [N][K] fp32 latent weights -> ternary codes five to a byte (base 3) + w_beta."""
+    N, K = w.shape
+    _check(lib().bitlinear_pack_weights_b3(_ptr(w), N, K, _ptr(packed), _ptr(w_beta), _ptr(workspace),
+                                           _stream(stream)))
+
+
+def bitlinear_gemv_b3(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
+    """y [M][N] = dequant(x_q . T^T) from base-3 packed ternary weights, M <= 64 tokens."""
+    _check(lib().bitlinear_gemv_b3(_ptr(x_q), _ptr(x_ds), _ptr(x_rowsum), x_ds.shape[0], K, _ptr(packed),
                                    _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate), _stream(stream)))
 
 
@@ -340,6 +366,15 @@ def pack_weights_b1(w, stream=None):
     beta = torch.empty((1,), dtype=torch.float32, device=w.device)
     ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
     bitlinear_pack_weights_b1(w, packed, beta, ws, stream)
+    return packed, beta
+
+
+def pack_weights_b3(w, stream=None):
+    N, K = w.shape
+    packed = torch.empty((packed_bytes_b3(N, K),), dtype=torch.uint8, device=w.device)
+    beta = torch.empty((1,), dtype=torch.float32, device=w.device)
+    ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
+    bitlinear_pack_weights_b3(w, packed, beta, ws, stream)
     return packed, beta
 
 

@@ -77,7 +77,7 @@ int check_product(const char* fn, const int8_t* x_q, const float* x_ds, int64_t 
 
 extern "C" {
 
-int bitlinear_version(void) { return (1 << 16) | 2; }
+int bitlinear_version(void) { return (1 << 16) | 3; }
 
 const char* bitlinear_last_error(void) { return g_err; }
 
@@ -91,6 +91,11 @@ int64_t bitlinear_packed_bytes(int64_t N, int64_t K) {
 int64_t bitlinear_packed_bytes_b1(int64_t N, int64_t K) {
   if (!n_ok(N) || !k_ok(K)) return -1;
   return bl::ceil_div(N, bl::kTileN) * bl::ceil_div(K, bl::kTileKB1) * bl::kTileBytes;
+}
+
+int64_t bitlinear_packed_bytes_b3(int64_t N, int64_t K) {
+  if (!n_ok(N) || !k_ok(K)) return -1;
+  return bl::ceil_div(N, bl::kTileN) * bl::ceil_div(K, bl::kTileKB3) * bl::kTileBytes;
 }
 
 int64_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K) {
@@ -152,6 +157,19 @@ int bitlinear_pack_weights_b1(const float* w, int64_t N, int64_t K, void* packed
                     fn);
 }
 
+int bitlinear_pack_weights_b3(const float* w, int64_t N, int64_t K, void* packed, float* w_beta, void* workspace,
+                              void* stream) {
+  const char* fn = "bitlinear_pack_weights_b3";
+  if (!n_ok(N) || !k_ok(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld or K=%lld out of range", fn, (long long)N, (long long)K);
+  if (!w || !packed || !w_beta || !workspace) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(w, 4) || !aligned(packed, 16) || !aligned(w_beta, 4) || !aligned(workspace, 8))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned pointer", fn);
+  return hip_status(bl::launch_pack_b3(w, N, K, static_cast<uint8_t*>(packed), w_beta, static_cast<double*>(workspace),
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_gemv(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed,
                    const float* w_beta, int64_t N, void* y, int y_dtype, void* workspace,
                    size_t workspace_bytes, void* stream) {
@@ -187,6 +205,19 @@ int bitlinear_gemv_b1(const int8_t* x_q, const float* x_ds, const int32_t* x_row
   if (!x_rowsum) return fail(BITLINEAR_ERR_ARG, "%s: x_rowsum is required", fn);
   if (!aligned(x_rowsum, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_rowsum not element aligned", fn);
   return hip_status(bl::launch_gemv_b1(x_q, act_stride(K), x_ds, x_rowsum, M, K, static_cast<const uint8_t*>(packed),
+                                       w_beta, N, y, y_dtype, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_gemv_b3(const int8_t* x_q, const float* x_ds, const int32_t* x_rowsum, int64_t M, int64_t K,
+                      const void* packed, const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
+  const char* fn = "bitlinear_gemv_b3";
+  int st = check_product(fn, x_q, x_ds, M, BITLINEAR_GEMV_MAX_M, K, packed, w_beta, N, y, y_dtype, nullptr, 0, 0);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  if (!x_rowsum) return fail(BITLINEAR_ERR_ARG, "%s: x_rowsum is required", fn);
+  if (!aligned(x_rowsum, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: x_rowsum not element aligned", fn);
+  return hip_status(bl::launch_gemv_b3(x_q, act_stride(K), x_ds, x_rowsum, M, K, static_cast<const uint8_t*>(packed),
                                        w_beta, N, y, y_dtype, static_cast<hipStream_t>(stream)),
                     fn);
 }

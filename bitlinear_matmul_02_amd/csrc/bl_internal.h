@@ -18,6 +18,7 @@ constexpr int kBetaChunk = 4096;
 // LDS a decode workgroup may use for its int8 activation rows (each row is
 // act_stride(K) + 16 bytes); with its 4 KB reduction buffer it stays < 64 KB.
 constexpr int kTileKB1 = 512;  // columns of a 1 KB binary (B1) tile
+constexpr int kTileKB3 = 320;  // columns of a 1 KB base-3 (B3) tile
 constexpr int kActAlign = 512;  // int8 activation rows are padded to a multiple of this
 constexpr int64_t kDecodeLdsBytes = BITLINEAR_DECODE_MAX_ACT_BYTES;
 constexpr int kXDtypeMask = BITLINEAR_X_RMSNORM - 1;  // x_dtype without its flags
@@ -69,6 +70,12 @@ hipError_t launch_gemv_b1(const int8_t* q, int64_t ldq, const float* ds, const i
 
 hipError_t launch_gemm_b1(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s);
+
+hipError_t launch_pack_b3(const float* w, int64_t N, int64_t K, uint8_t* packed, float* beta, double* partials,
+                          hipStream_t s);
+hipError_t launch_gemv_b3(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M,
+                          int64_t K, const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype,
+                          hipStream_t s);
 
 hipError_t launch_relu2_mul(const float* g, const float* u, int64_t count, float* h, hipStream_t s);
 

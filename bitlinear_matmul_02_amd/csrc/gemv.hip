@@ -52,6 +52,13 @@
 // bits; the matrix cores sum q * b and the epilogue takes 2 * sum - rowsum(q)
 // = sum q * (2 b - 1), exact.
 //
+// Base-3 tiles (format B3, five ternary weights per byte) hold 16 x 320
+// weights per 1 KB: byte i of lane (n, g) carries, in base 3, the codes
+// c = t + 1 of columns 64 s + 16 g + i for the five steps s.  Digit s of four
+// bytes at a time comes from exact 16-bit multiply-shift divisions by 3^s
+// (two bytes per 16-bit half), the matrix cores sum q * c with c in {0, 1, 2},
+// and the epilogue subtracts rowsum(q): sum q * (c - 1) = sum q * t.
+//
 // Tiny outputs with a long K (AGLOBAL only) also split K across workgroups:
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
@@ -73,14 +80,16 @@ enum AMode { AGLOBAL = 0, ALDS_Q = 1, ALDS_X = 2, ALDS_XS = 3 };
 // k-tiles in flight per wave, chosen to keep the prefetch ring within the
 // register budget (weights: 4 VGPRs per output block; activations in the
 // ring only for AGLOBAL: 16 VGPRs per token block).
-// Binary tiles carry twice the MFMA steps, so twice the activation operands.
+// MFMA steps per 1 KB weight tile: 4 (T2), 8 (B1), 5 (B3).
+constexpr int tile_steps(int fmt) { return fmt == 1 ? 8 : (fmt == 2 ? 5 : 4); }
+// Columns per weight tile: 256 (T2, 2 bits), 512 (B1, 1 bit), 320 (B3, 1.6 bits).
+constexpr int tile_cols(int fmt) { return 64 * tile_steps(fmt); }
+
+// Formats with more steps per tile carry more activation operands per tile.
 constexpr int ring_depth(int mb, int nb, int amode, int fmt = 0) {
-  return amode == AGLOBAL ? (((fmt ? 8 : 4) * mb + nb) * 4 <= 24 ? 4 : (((fmt ? 8 : 4) * mb + nb) * 4 <= 40 ? 2 : 1))
+  return amode == AGLOBAL ? ((tile_steps(fmt) * mb + nb) * 4 <= 24 ? 4 : ((tile_steps(fmt) * mb + nb) * 4 <= 40 ? 2 : 1))
                           : (nb == 1 ? 8 : (nb == 2 ? 4 : 2));
 }
-
-// Columns per weight tile: 256 (T2, 2 bits) or 512 (B1, 1 bit); 1 KB either way.
-constexpr int tile_cols(int fmt) { return fmt ? 512 : kTileK; }
 // Largest workgroup, in waves, for MB token blocks.
 constexpr int max_waves(int mb) { return mb <= 2 ? 16 : 8; }
 
@@ -531,6 +540,25 @@ __device__ inline v4i b1_field(const u4 w, int s) {
   return r;
 }
 
+// Base-3 digits of the four bytes of dw, as bytes: d[s] byte j = digit s of
+// byte j.  Bytes 0/2 and 1/3 are processed as 16-bit pairs; q_s = floor(b /
+// 3^s) = (b * m_s) >> sh_s is exact for b <= 242 with products below 2^16.
+typedef unsigned short us2v __attribute__((ext_vector_type(2)));
+__device__ inline void b3_digits(uint32_t dw, uint32_t (&d)[5]) {
+  const us2v e = __builtin_bit_cast(us2v, dw & 0x00FF00FFu);
+  const us2v o = __builtin_bit_cast(us2v, (dw >> 8) & 0x00FF00FFu);
+  auto qd = [](us2v x, unsigned short m, unsigned short sh) -> us2v {
+    return (us2v)((x * (us2v){m, m}) >> (us2v){sh, sh});
+  };
+  const us2v three = {3, 3};
+  const us2v e1 = qd(e, 171, 9), e2 = qd(e, 228, 11), e3 = qd(e, 152, 12), e4 = qd(e, 203, 14);
+  const us2v o1 = qd(o, 171, 9), o2 = qd(o, 228, 11), o3 = qd(o, 152, 12), o4 = qd(o, 203, 14);
+  const us2v de[5] = {e - three * e1, e1 - three * e2, e2 - three * e3, e3 - three * e4, e4};
+  const us2v dd[5] = {o - three * o1, o1 - three * o2, o2 - three * o3, o3 - three * o4, o4};
+#pragma unroll
+  for (int s = 0; s < 5; ++s) d[s] = __builtin_bit_cast(uint32_t, de[s]) | (__builtin_bit_cast(uint32_t, dd[s]) << 8);
+}
+
 template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT)>
 __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int KT = tile_cols(FMT), NS = KT / 64;  // columns and MFMA steps per k-tile
@@ -596,11 +624,23 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   auto mma_tile = [&](int slot, int kt) {
     const int as = AM == AGLOBAL ? slot : 0;
     if (AM != AGLOBAL) load_a(0, kt);  // LDS operands: read at use
+    v4i b3ops[FMT == 2 ? NB : 1][FMT == 2 ? 5 : 1];
+    if constexpr (FMT == 2) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        uint32_t dg[4][5];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) b3_digits(wbuf[slot][j][w], dg[w]);
+#pragma unroll
+        for (int st = 0; st < 5; ++st) b3ops[j][st] = v4i{(int)dg[0][st], (int)dg[1][st], (int)dg[2][st], (int)dg[3][st]};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NS; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const v4i b = FMT ? b1_field(wbuf[slot][j], i) : t2_field(wbuf[slot][j], i);
+        const v4i b = FMT == 2 ? b3ops[FMT == 2 ? j : 0][FMT == 2 ? i : 0]
+                               : (FMT == 1 ? b1_field(wbuf[slot][j], i) : t2_field(wbuf[slot][j], i));
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma16(abuf[as][mb][i], b, acc[mb][j]);
       }
@@ -763,8 +803,10 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int n = (nb0 + j) * kTileN + r16;
-        // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum, scaled as the T2 sums (64 t)
-        const int v = FMT ? (2 * acc[mb][j][r] - rs) * 64 : acc[mb][j][r];
+        // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum; B3: sum q * (c - 1) =
+        // sum q * c - rowsum; both scaled as the T2 sums (64 t)
+        const int v = FMT == 1 ? (2 * acc[mb][j][r] - rs) * 64
+                               : (FMT == 2 ? (acc[mb][j][r] - rs) * 64 : acc[mb][j][r]);
         if (n < sg.N) store_out(sg.y, a.y_dtype, (int64_t)m * sg.N + n, v, scale);
       }
     }
@@ -911,6 +953,19 @@ hipError_t launch_gemv_b1(const int8_t* q, int64_t ldq, const float* ds, const i
   a.rowsum = rowsum;
   if (p.amode == ALDS_Q) return dispatch_mb_nb<ALDS_Q, false, 1>(p, a, s);
   return dispatch_mb_nb<AGLOBAL, false, 1>(p, a, s);
+}
+
+hipError_t launch_gemv_b3(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M,
+                          int64_t K, const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype,
+                          hipStream_t s) {
+  const GemvPlan p = make_plan(M, N, K, false, false, M * (ldq / 16), 2);
+  GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr, 2);
+  a.q = q;
+  a.ldq = ldq;
+  a.ds = ds;
+  a.rowsum = rowsum;
+  if (p.amode == ALDS_Q) return dispatch_mb_nb<ALDS_Q, false, 2>(p, a, s);
+  return dispatch_mb_nb<AGLOBAL, false, 2>(p, a, s);
 }
 
 int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, false).ws_bytes; }

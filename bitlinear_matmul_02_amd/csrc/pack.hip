@@ -16,6 +16,10 @@
 // Binary weights (BitNet b1, "BitNet / Ternary / Binary - Les LLMs 1-bit",
 // TL;DR: every weight +1 or -1) take the same beta and one bit per weight,
 // 1 for w >= 0, in 16 x 512 tiles (pack_b1_kernel).
+//
+// Base-3 packing (pack_b3_kernel) stores the same ternary codes five to a
+// byte: 16 x 320 tiles, byte i of lane L = sum_s (t + 1) * 3^s over the
+// columns 64 s + 16 (L / 16) + i of row L % 16.
 #include "bl_internal.h"
 
 namespace bl {
@@ -118,6 +122,36 @@ __global__ __launch_bounds__(256) void pack_b1_kernel(const float* __restrict__ 
   packed[idx] = word;
 }
 
+// Word `idx` of a B3 buffer: tile = idx / 256, lane L = (idx % 256) / 4,
+// dword d = idx % 4; byte b of the word is byte i = 4 d + b of the lane.
+__global__ __launch_bounds__(256) void pack_b3_kernel(const float* __restrict__ w, int64_t N, int64_t K,
+                                                      int64_t Kt, const float* __restrict__ beta,
+                                                      uint32_t* __restrict__ packed, int64_t nwords) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nwords) return;
+  const int64_t tile = idx >> 8;
+  const int L = (int)((idx >> 2) & 63), d = (int)(idx & 3);
+  const int64_t nb = tile / Kt, kb = tile - nb * Kt;
+  const int64_t n = nb * kTileN + (L & 15);
+  const float dd = *beta + kEpsW;
+  uint32_t word = 0;
+  if (n < N) {
+    const float* row = w + n * K;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      uint32_t v = 0, p3 = 1;
+#pragma unroll
+      for (int st = 0; st < 5; ++st) {
+        const int64_t k = kb * kTileKB3 + 64 * st + 16 * (L >> 4) + 4 * d + b;
+        if (k < K) v += (uint32_t)((int)fminf(fmaxf(rintf(row[k] / dd), -1.0f), 1.0f) + 1) * p3;
+        p3 *= 3;
+      }
+      word |= v << (8 * b);
+    }
+  }
+  packed[idx] = word;
+}
+
 hipError_t launch_absmean(const float* w, int64_t count, float* beta, double* partials, hipStream_t s) {
   const int64_t nchunks = ceil_div(count, kBetaChunk);
   hipLaunchKernelGGL(absmean_chunks_kernel, dim3((unsigned)ceil_div(nchunks, 256)), dim3(256), 0, s,
@@ -137,6 +171,17 @@ hipError_t launch_pack_b1(const float* w, int64_t N, int64_t K, uint8_t* packed,
   const int64_t Kt = ceil_div(K, kTileKB1), Nt = ceil_div(N, kTileN);
   const int64_t nwords = Nt * Kt * (kTileBytes / 4);
   hipLaunchKernelGGL(pack_b1_kernel, dim3((unsigned)ceil_div(nwords, 256)), dim3(256), 0, s, w, N, K, Kt,
+                     reinterpret_cast<uint32_t*>(packed), nwords);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_b3(const float* w, int64_t N, int64_t K, uint8_t* packed, float* beta, double* partials,
+                          hipStream_t s) {
+  hipError_t e = launch_absmean(w, N * K, beta, partials, s);
+  if (e != hipSuccess) return e;
+  const int64_t Kt = ceil_div(K, kTileKB3), Nt = ceil_div(N, kTileN);
+  const int64_t nwords = Nt * Kt * (kTileBytes / 4);
+  hipLaunchKernelGGL(pack_b3_kernel, dim3((unsigned)ceil_div(nwords, 256)), dim3(256), 0, s, w, N, K, Kt, beta,
                      reinterpret_cast<uint32_t*>(packed), nwords);
   return hipGetLastError();
 }

@@ -206,6 +206,27 @@ int bitlinear_gemm_b1(const int8_t *x_q, const float *x_ds, const int32_t *x_row
                       int64_t K, const void *packed, const float *w_beta, int64_t N, void *y,
                       int y_dtype, void *stream);
 
+/*
+ * Base-3 packing of the ternary weights, five to a byte (1.6 bits per
+ * weight; "BitNet Technical Notes" and the "BitNet: Inference framework for
+ * 1-bit LLMs" thread discuss packing trits more densely than 2 bits).
+ * bitlinear_packed_bytes_b3(N, K) = ceil(N/16) * ceil(K/320) * 1024.
+ * bitlinear_pack_weights_b3: the same beta and codes t as
+ * bitlinear_pack_weights, stored as tiles (nb, kb) of 16 rows x 320 columns,
+ * 1024 bytes at offset (nb * ceil(K/320) + kb) * 1024; byte 16*L + i of a tile
+ * (L in 0..63, i in 0..15) is sum_{s=0..4} (t + 1) * 3^s over the weights
+ * (n = 16*nb + L%16, k = 320*kb + 64*s + 16*(L/16) + i); padding adds 0.
+ * bitlinear_gemv_b3: the decode product on those tiles, identical to
+ * bitlinear_gemv on the same weights; x_rowsum [M] int32 is required (from
+ * bitlinear_quant_act).  Arguments and errors as bitlinear_gemv_b1.
+ */
+int64_t bitlinear_packed_bytes_b3(int64_t N, int64_t K);
+int bitlinear_pack_weights_b3(const float *w, int64_t N, int64_t K, void *packed, float *w_beta,
+                              void *workspace, void *stream);
+int bitlinear_gemv_b3(const int8_t *x_q, const float *x_ds, const int32_t *x_rowsum, int64_t M,
+                      int64_t K, const void *packed, const float *w_beta, int64_t N, void *y,
+                      int y_dtype, void *stream);
+
 /* LDS budget of the decode kernels for int8 activation rows (see below). */
 #define BITLINEAR_DECODE_MAX_ACT_BYTES 58368
 

@@ -246,3 +246,17 @@ def test_b1_sizes_and_validation():
     assert fn(FAKE, FAKE, FAKE, 65, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_SHAPE
     assert fn(FAKE, FAKE, FAKE, 1, 512, FAKE, FAKE, 16, FAKE, 7, None) == bl.ERR_ARG
     assert fn(None, None, None, 0, 512, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.OK
+
+
+def test_b3_sizes_and_validation():
+    assert bl.packed_bytes_b3(16, 320) == 1024
+    assert bl.packed_bytes_b3(17, 321) == 4 * 1024
+    assert bl.packed_bytes_b3(6912, 2560) == 432 * 8 * 1024
+    assert bl.packed_bytes_b3(1, 0) == -1
+    L = bl.lib()
+    assert L.bitlinear_pack_weights_b3(None, 16, 320, FAKE, FAKE, FAKE, None) == bl.ERR_ARG
+    assert L.bitlinear_pack_weights_b3(FAKE, 16, 0, FAKE, FAKE, FAKE, None) == bl.ERR_SHAPE
+    fn = L.bitlinear_gemv_b3
+    assert fn(FAKE, FAKE, None, 1, 320, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_ARG
+    assert fn(FAKE, FAKE, FAKE, 65, 320, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_SHAPE
+    assert fn(None, None, None, 0, 320, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.OK
