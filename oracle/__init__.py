@@ -82,6 +82,12 @@ def _load():
     lib.oracle_pack_b3.argtypes = [p, i64, i64, p]
     lib.oracle_unpack_b3.restype = None
     lib.oracle_unpack_b3.argtypes = [p, i64, i64, p]
+    lib.oracle_train_forward.restype = None
+    lib.oracle_train_forward.argtypes = [p, i64, i64, p, ctypes.c_float, i64, p, ctypes.c_int]
+    lib.oracle_train_dx.restype = None
+    lib.oracle_train_dx.argtypes = [p, i64, i64, p, ctypes.c_float, i64, p, ctypes.c_int]
+    lib.oracle_train_dw.restype = None
+    lib.oracle_train_dw.argtypes = [p, p, i64, i64, i64, p, ctypes.c_int]
     lib.oracle_rmsnorm_f32.restype = None
     lib.oracle_rmsnorm_f32.argtypes = [p, i64, i64, p]
     _lib = lib
@@ -291,6 +297,40 @@ def bitlinear_forward_b1(x_bf16_bits: np.ndarray, w: np.ndarray, threads: int = 
     y = dequant(acc, ds, beta)
     return {"beta": beta, "t": t, "q": q, "ds": ds, "rowsum": rs, "acc": acc, "y": y,
             "y_bf16": to_bf16_bits(y)}
+
+
+# ------------------------------------------------------------ training step
+def train_forward(x_bf16_bits: np.ndarray, t: np.ndarray, beta, threads: int = 1) -> np.ndarray:
+    """y = x . (beta t)^T from bf16 x [M][K] and ternary codes t [N][K]."""
+    xb = _c(x_bf16_bits, np.uint16)
+    t = _c(t, np.int8)
+    M, K = xb.shape
+    N = t.shape[0]
+    y = np.empty((M, N), dtype=np.float32)
+    _load().oracle_train_forward(_ptr(xb), M, K, _ptr(t), float(beta), N, _ptr(y), threads)
+    return y
+
+
+def train_dx(dy_bf16_bits: np.ndarray, t: np.ndarray, beta, threads: int = 1) -> np.ndarray:
+    """dx = dy . (beta t) from bf16 dy [M][N] and ternary codes t [N][K]."""
+    dyb = _c(dy_bf16_bits, np.uint16)
+    t = _c(t, np.int8)
+    M, N = dyb.shape
+    K = t.shape[1]
+    dx = np.empty((M, K), dtype=np.float32)
+    _load().oracle_train_dx(_ptr(dyb), M, N, _ptr(t), float(beta), K, _ptr(dx), threads)
+    return dx
+
+
+def train_dw(dy_bf16_bits: np.ndarray, x_bf16_bits: np.ndarray, threads: int = 1) -> np.ndarray:
+    """dw = dy^T . x (the straight-through gradient of the latent weights)."""
+    dyb = _c(dy_bf16_bits, np.uint16)
+    xb = _c(x_bf16_bits, np.uint16)
+    M, N = dyb.shape
+    K = xb.shape[1]
+    dw = np.empty((N, K), dtype=np.float32)
+    _load().oracle_train_dw(_ptr(dyb), _ptr(xb), M, N, K, _ptr(dw), threads)
+    return dw
 
 
 # ------------------------------------------------------------ whole forward

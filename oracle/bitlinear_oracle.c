@@ -46,6 +46,11 @@
  *      "BitNet: Inference framework for 1-bit LLMs" thread discuss packing
  *      trits more densely than 2 bits); the layout is this project's own
  *      choice, written here from its specification.
+ *  - oracle_train_forward / oracle_train_dx / oracle_train_dw: the training
+ *      step of a BitLinear with the straight-through estimator ("BitNet /
+ *      Ternary / Binary - Les LLMs 1-bit", Apercu de l'entrainement d'un
+ *      BitLinear: the forward multiplies by the quantized weights, the
+ *      backward lets the gradient pass to the latent weights unchanged).
  *  - oracle_pack_t2 / oracle_unpack_t2: 2 bits per ternary weight
  *      ("BitNet Technical Notes", Appendix glossary: bit-packing at 2 bits per
  *      ternary weight; "BitNet: Inference framework for 1-bit LLMs", post #139:
@@ -66,6 +71,11 @@
  *  - RMS normalization (gain 1, no bias; placement and epsilon not given on
  *    the pages): S = sum_k x_k^2 in fp64 (each square exact), ms = (float)(S /
  *    K), r = 1 / sqrt(ms + 1e-5) in fp32, xn_k = x_k * r.
+ *  - training products: bf16 inputs (activations and output gradients are not
+ *    quantized, as in the pages' training snippet), the quantized weights
+ *    scaled by beta (as at inference; the snippet omits the rescale):
+ *    y = x . (beta t)^T, dx = dy . (beta t), dw = dy^T . x, each sum exact in
+ *    fp64, times beta in fp64, rounded once to fp32.
  *  - feed-forward glue: h = (r * r) * u with r = g if g > 0 else 0, fp32 in
  *    this order; the gate / up / down form is the plainest reading of an FFN
  *    with ReLU^2 between its projections.
@@ -449,4 +459,49 @@ void oracle_rmsnorm_f32(const float *x, int64_t M, int64_t K, float *xn)
         for (int64_t k = 0; k < K; ++k)
             xn[m * K + k] = row[k] * r;
     }
+}
+
+/* ------------------------------------------------------------ training */
+
+/* y[m][n] = beta * sum_k x[m][k] t[n][k]  (x bf16 [M][K], t [N][K]) */
+void oracle_train_forward(const uint16_t *xb, int64_t M, int64_t K, const int8_t *t, float beta, int64_t N,
+                          float *y, int threads)
+{
+#pragma omp parallel for num_threads(threads) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (double)bf16_bits_to_f32(xb[m * K + k]) * (double)t[n * K + k];
+            y[m * N + n] = (float)((double)beta * s);
+        }
+}
+
+/* dx[m][k] = beta * sum_n dy[m][n] t[n][k]  (dy bf16 [M][N]) */
+void oracle_train_dx(const uint16_t *dyb, int64_t M, int64_t N, const int8_t *t, float beta, int64_t K,
+                     float *dx, int threads)
+{
+#pragma omp parallel for num_threads(threads) schedule(static)
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                s += (double)bf16_bits_to_f32(dyb[m * N + n]) * (double)t[n * K + k];
+            dx[m * K + k] = (float)((double)beta * s);
+        }
+}
+
+/* dw[n][k] = sum_m dy[m][n] x[m][k]: the straight-through gradient of the
+ * latent weights (dy bf16 [M][N], x bf16 [M][K]) */
+void oracle_train_dw(const uint16_t *dyb, const uint16_t *xb, int64_t M, int64_t N, int64_t K, float *dw,
+                     int threads)
+{
+#pragma omp parallel for num_threads(threads) schedule(static)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            double s = 0.0;
+            for (int64_t m = 0; m < M; ++m)
+                s += (double)bf16_bits_to_f32(dyb[m * N + n]) * (double)bf16_bits_to_f32(xb[m * K + k]);
+            dw[n * K + k] = (float)s;
+        }
 }

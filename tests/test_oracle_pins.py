@@ -675,3 +675,44 @@ def test_b3_digits_cover_every_byte_value():
             t[n, 64 * s + 16 * g + i] = digits[v, s] - 1
     p = oracle.pack_b3(t).reshape(64, 16)
     np.testing.assert_array_equal(p.reshape(-1)[:243], vals)
+
+
+# ------------------------------------------------------------- training products (STE)
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_train_products_small_exact():
+    # integers: every product and sum is exact, beta a power of two
+    x = np.array([[1, 2, 3], [-1, 0, 4]], dtype=np.float32)
+    t = np.array([[1, 0, -1], [-1, 1, 1], [0, 0, 1], [1, 1, 1]], dtype=np.int8)
+    dy = np.array([[1, -2, 0, 3], [2, 1, -1, 0]], dtype=np.float32)
+    beta = np.float32(0.5)
+    np.testing.assert_array_equal(oracle.train_forward(_bf16(x), t, beta), 0.5 * (x @ t.T.astype(np.float32)))
+    np.testing.assert_array_equal(oracle.train_dx(_bf16(dy), t, beta), 0.5 * (dy @ t.astype(np.float32)))
+    np.testing.assert_array_equal(oracle.train_dw(_bf16(dy), _bf16(x)), dy.T @ x)
+
+
+def test_train_products_match_library_matmul_and_adjoints():
+    rng = np.random.default_rng(41)
+    M, K, N = 7, 300, 13
+    xb = _bf16(rng.standard_normal((M, K)))
+    dyb = _bf16(rng.standard_normal((M, N)))
+    w = rng.standard_normal((N, K)).astype(np.float32) * 0.02
+    beta = oracle.absmean(w)
+    t = oracle.ternarize(w, beta)
+    x = workloads.bf16_bits_to_f32(xb).astype(np.float64)
+    dy = workloads.bf16_bits_to_f32(dyb).astype(np.float64)
+    wq = float(beta) * t.astype(np.float64)
+    y = oracle.train_forward(xb, t, beta, threads=4)
+    dx = oracle.train_dx(dyb, t, beta, threads=4)
+    dw = oracle.train_dw(dyb, xb, threads=4)
+    # one fp32 rounding of the exact value (numpy's fp64 products as the independent routine)
+    for got, ref in ((y, x @ wq.T), (dx, dy @ wq), (dw, dy.T @ x)):
+        assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -23 + 1e-30)
+    # adjoint identities tie the three products together: <dy, y> = <dx, x> = <dw, wq>
+    a = float((dy * y.astype(np.float64)).sum())
+    b = float((dx.astype(np.float64) * x).sum())
+    c = float((dw.astype(np.float64) * wq).sum())
+    scale = float(np.abs(dy).sum() * np.abs(x).sum())
+    assert abs(a - b) <= 1e-6 * scale and abs(a - c) <= 1e-6 * scale
