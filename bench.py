@@ -34,7 +34,9 @@ Also printed on the same JSON line:
                 checked bit for bit against the oracle's chain; 100B-class
                 decode (M = 1, 8, 32) in GB/s; binary-weight (b1) and base-3
                 (b3) decode on the 2B and 100B shapes (M = 1, 8); prefill GEMMs (2B M=2048,
-                100B M=512), ternary and binary, in int8 TOPS.
+                100B M=512), ternary and binary, in int8 TOPS; the training
+                products (straight-through forward, input and weight
+                gradients, 2B shapes, 2048 tokens) in bf16 TFLOP/s.
 """
 from __future__ import annotations
 
@@ -58,6 +60,7 @@ KERNEL_SOURCES = ("bitlinear_matmul_02_amd/csrc/gemv.hip", "bitlinear_matmul_02_
 CAL_BYTES = 64 << 20  # calibration copy
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 MALL_BYTES = 256 << 20
 
 
@@ -542,6 +545,38 @@ def decode_fmt_extra(fmt, shapes, Ms, dev, steps=100):
     return res
 
 
+def train_extra(M, shapes, dev, reps=10):
+    """Training step of one BitLinear with straight-through gradients, per
+    shape: forward y = beta x t^T, input gradient dx = beta dy t, weight
+    gradient dw = dy^T x (bf16 in, fp32 out, bf16 matrix cores); TFLOP/s on
+    2 M N K per product against the dense bf16 peak."""
+    res = {}
+    for i, (K, N) in enumerate(shapes):
+        packed, beta = gpu_weights(N, K, 900 + i, dev)
+        x = gpu_acts(M, K, 910 + i, dev)
+        dy = gpu_acts(M, N, 920 + i, dev)
+        y = torch.empty((M, N), device=dev)
+        dx = torch.empty((M, K), device=dev)
+        dw = torch.empty((N, K), device=dev)
+        ops = {"forward": lambda r: bl.bitlinear_train_forward(x, packed, beta, N, y),
+               "backward_input": lambda r: bl.bitlinear_train_backward_input(dy, packed, beta, K, dx),
+               "backward_weight": lambda r: bl.bitlinear_train_backward_weight(dy, x, dw)}
+        flop = 2.0 * M * N * K
+        row = {}
+        for name, fn in ops.items():
+            g = capture(fn, reps)
+            time_graph(g)
+            el, _ = time_graph(g)
+            d = el / reps
+            row[name] = {"us": round(d * 1e6, 1), "TFLOPS": round(flop / d / 1e12, 1),
+                         "frac_mfma_bf16": round(flop / d / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            del g
+        res["%dx%d->%d" % (M, K, N)] = row
+        del packed, x, dy, y, dx, dw
+        torch.cuda.empty_cache()
+    return res
+
+
 def prefill_b1_extra(M, shapes, dev, reps=20):
     """Binary-weight prefill GEMM (bitlinear_gemm_b1) TOPS on the same shapes."""
     res = {}
@@ -643,6 +678,7 @@ def main():
             "prefill_100b_m512": prefill_extra(512, workloads.SHAPES_100B, dev),
             "prefill_b1_2b_m2048": prefill_b1_extra(2048, ((2560, 6912), (6912, 2560)), dev),
             "prefill_b1_100b_m512": prefill_b1_extra(512, workloads.SHAPES_100B, dev),
+            "train_2b_m2048": train_extra(2048, ((2560, 6912), (6912, 2560)), dev),
         }
     print(json.dumps(result), flush=True)
 

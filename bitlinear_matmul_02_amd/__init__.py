@@ -21,6 +21,9 @@ Functions carry the C names:
     bitlinear_gemm_b1(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
     bitlinear_pack_weights_b3(w, packed, w_beta, workspace)      (base-3 ternary)
     bitlinear_gemv_b3(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y)
+    bitlinear_train_forward(x, packed, w_beta, N, y)            (training, straight-through)
+    bitlinear_train_backward_input(dy, packed, w_beta, K, dx)
+    bitlinear_train_backward_weight(dy, x, dw)
 An fp32 output tensor can be passed with ``accumulate=True`` to the product
 calls, which then add their result into it (``BITLINEAR_F32_ADD``); the calls
 that quantize activations take ``rmsnorm=True`` to RMS-normalize each row
@@ -52,7 +55,8 @@ EXPORTS = (
     "bitlinear_gemv_multi", "bitlinear_forward_decode_multi", "bitlinear_gemv_glu",
     "bitlinear_forward_decode_glu", "bitlinear_packed_bytes_b1", "bitlinear_pack_weights_b1",
     "bitlinear_gemv_b1", "bitlinear_gemm_b1", "bitlinear_packed_bytes_b3", "bitlinear_pack_weights_b3",
-    "bitlinear_gemv_b3",
+    "bitlinear_gemv_b3", "bitlinear_train_forward", "bitlinear_train_backward_input",
+    "bitlinear_train_backward_weight",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -113,6 +117,12 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_pack_weights_b3.argtypes = [p, i64, i64, p, p, p, p]
     L.bitlinear_gemv_b3.restype = i32
     L.bitlinear_gemv_b3.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
+    L.bitlinear_train_forward.restype = i32
+    L.bitlinear_train_forward.argtypes = [p, i64, i64, p, p, i64, p, p]
+    L.bitlinear_train_backward_input.restype = i32
+    L.bitlinear_train_backward_input.argtypes = [p, i64, i64, p, p, i64, p, p]
+    L.bitlinear_train_backward_weight.restype = i32
+    L.bitlinear_train_backward_weight.argtypes = [p, p, i64, i64, i64, p, p]
     L.bitlinear_gemm_b1.restype = i32
     L.bitlinear_gemm_b1.argtypes = [p, p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_relu2_mul.restype = i32
@@ -226,6 +236,35 @@ def bitlinear_gemv_b3(x_q, x_ds, x_rowsum, K, packed, w_beta, N, y, stream=None,
     """y [M][N] = dequant(x_q . T^T) from base-3 packed ternary weights, M <= 64 tokens."""
     _check(lib().bitlinear_gemv_b3(_ptr(x_q), _ptr(x_ds), _ptr(x_rowsum), x_ds.shape[0], K, _ptr(packed),
                                    _ptr(w_beta), N, _ptr(y), _ydtype(y, accumulate), _stream(stream)))
+
+
+def _bf16_2d(t, name):
+    if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_contiguous():
+        raise BitLinearError(ERR_ARG, "%s must be a contiguous 2-D bf16 tensor" % name)
+
+
+def bitlinear_train_forward(x, packed, w_beta, N, y, stream=None) -> None:
+    """y [M][N] = beta * x . t^T (training forward, x bf16 unquantized, y fp32)."""
+    _bf16_2d(x, "x")
+    M, K = x.shape
+    _check(lib().bitlinear_train_forward(_ptr(x), M, K, _ptr(packed), _ptr(w_beta), N, _ptr(y), _stream(stream)))
+
+
+def bitlinear_train_backward_input(dy, packed, w_beta, K, dx, stream=None) -> None:
+    """dx [M][K] = beta * dy . t (straight-through input gradient)."""
+    _bf16_2d(dy, "dy")
+    M, N = dy.shape
+    _check(lib().bitlinear_train_backward_input(_ptr(dy), M, N, _ptr(packed), _ptr(w_beta), K, _ptr(dx),
+                                                _stream(stream)))
+
+
+def bitlinear_train_backward_weight(dy, x, dw, stream=None) -> None:
+    """dw [N][K] = dy^T . x (straight-through gradient of the latent weights)."""
+    _bf16_2d(dy, "dy")
+    _bf16_2d(x, "x")
+    M, N = dy.shape
+    K = x.shape[1]
+    _check(lib().bitlinear_train_backward_weight(_ptr(dy), _ptr(x), M, N, K, _ptr(dw), _stream(stream)))
 
 
 def _ydtype(y, accumulate: bool) -> int:

@@ -29,7 +29,7 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["abi.cpp", "quant_act.hip", "pack.hip", "gemv.hip", "gemm.hip", "glue.hip"]
+SOURCES = ["abi.cpp", "quant_act.hip", "pack.hip", "gemv.hip", "gemm.hip", "glue.hip", "train.hip"]
 
 
 def _compile(src: str) -> str:

@@ -358,6 +358,52 @@ int bitlinear_forward_decode_glu(const void* x, int x_dtype, int64_t M, int64_t 
                     fn);
 }
 
+// Shapes and pointers of the training products (M rows of activations).
+static int check_train(const char* fn, int64_t M, int64_t N, int64_t K, const void* p0, const void* p1,
+                       const void* p2, const void* out) {
+  if (M < 0 || M > BITLINEAR_MAX_M) return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld out of range", fn, (long long)M);
+  if (!n_ok(N) || !k_ok(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: N=%lld or K=%lld out of range", fn, (long long)N, (long long)K);
+  if (M == 0) return BITLINEAR_OK;
+  if (!p0 || !p1 || !p2 || !out) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(out, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: output not 4-byte aligned", fn);
+  return BITLINEAR_OK;
+}
+
+int bitlinear_train_forward(const void* x, int64_t M, int64_t K, const void* packed, const float* w_beta, int64_t N,
+                            float* y, void* stream) {
+  const char* fn = "bitlinear_train_forward";
+  int st = check_train(fn, M, N, K, x, packed, w_beta, y);
+  if (st != BITLINEAR_OK || M == 0) return st == BITLINEAR_OK ? ok() : st;
+  if (!aligned(x, 2) || !aligned(packed, 16) || !aligned(w_beta, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned input", fn);
+  return hip_status(bl::launch_train_forward(static_cast<const uint16_t*>(x), M, K, static_cast<const uint8_t*>(packed),
+                                             w_beta, N, y, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_train_backward_input(const void* dy, int64_t M, int64_t N, const void* packed, const float* w_beta,
+                                   int64_t K, float* dx, void* stream) {
+  const char* fn = "bitlinear_train_backward_input";
+  int st = check_train(fn, M, N, K, dy, packed, w_beta, dx);
+  if (st != BITLINEAR_OK || M == 0) return st == BITLINEAR_OK ? ok() : st;
+  if (!aligned(dy, 2) || !aligned(packed, 16) || !aligned(w_beta, 4)) return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned input", fn);
+  return hip_status(bl::launch_train_dx(static_cast<const uint16_t*>(dy), M, N, static_cast<const uint8_t*>(packed),
+                                        w_beta, K, dx, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int bitlinear_train_backward_weight(const void* dy, const void* x, int64_t M, int64_t N, int64_t K, float* dw,
+                                    void* stream) {
+  const char* fn = "bitlinear_train_backward_weight";
+  int st = check_train(fn, M, N, K, dy, x, x, dw);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  if (!aligned(dy, 2) || !aligned(x, 2)) return fail(BITLINEAR_ERR_ALIGN, "%s: misaligned input", fn);
+  return hip_status(bl::launch_train_dw(static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(x), M, N, K,
+                                        dw, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_relu2_mul(const float* g, const float* u, int64_t count, float* h, void* stream) {
   const char* fn = "bitlinear_relu2_mul";
   if (count < 0) return fail(BITLINEAR_ERR_SHAPE, "%s: count %lld < 0", fn, (long long)count);

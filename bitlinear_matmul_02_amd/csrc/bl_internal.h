@@ -77,6 +77,13 @@ hipError_t launch_gemv_b3(const int8_t* q, int64_t ldq, const float* ds, const i
                           int64_t K, const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype,
                           hipStream_t s);
 
+hipError_t launch_train_forward(const uint16_t* x, int64_t M, int64_t K, const uint8_t* packed, const float* beta,
+                                int64_t N, float* y, hipStream_t s);
+hipError_t launch_train_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* packed, const float* beta,
+                           int64_t K, float* dx, hipStream_t s);
+hipError_t launch_train_dw(const uint16_t* dy, const uint16_t* x, int64_t M, int64_t N, int64_t K, float* dw,
+                           hipStream_t s);
+
 hipError_t launch_relu2_mul(const float* g, const float* u, int64_t count, float* h, hipStream_t s);
 
 // ------------------------------------------------------- device helpers

@@ -227,6 +227,28 @@ int bitlinear_gemv_b3(const int8_t *x_q, const float *x_ds, const int32_t *x_row
                       int64_t K, const void *packed, const float *w_beta, int64_t N, void *y,
                       int y_dtype, void *stream);
 
+/*
+ * Training step of a BitLinear with the straight-through estimator ("BitNet /
+ * Ternary / Binary - Les LLMs 1-bit", Apercu de l'entrainement d'un
+ * BitLinear): the forward uses the quantized weights, the backward passes the
+ * gradient to the latent weights unchanged.  Activations and gradients are
+ * bf16 and not quantized; the weights enter as beta * t from
+ * bitlinear_pack_weights (packed, w_beta).  fp32 accumulation on the bf16
+ * matrix cores, fp32 outputs (row-major, 4-byte aligned):
+ *   bitlinear_train_forward:         y  [M][N] = beta * x . t^T,  x  [M][K]
+ *   bitlinear_train_backward_input:  dx [M][K] = beta * dy . t,   dy [M][N]
+ *   bitlinear_train_backward_weight: dw [N][K] = dy^T . x
+ * bf16 inputs need 2-byte alignment (16-byte rows run faster).  M, N, K in
+ * [0 or 1, the BITLINEAR_MAX_* limits]; M = 0 writes nothing.
+ * Errors: ERR_ARG (null pointer), ERR_SHAPE, ERR_ALIGN.
+ */
+int bitlinear_train_forward(const void *x, int64_t M, int64_t K, const void *packed, const float *w_beta,
+                            int64_t N, float *y, void *stream);
+int bitlinear_train_backward_input(const void *dy, int64_t M, int64_t N, const void *packed,
+                                   const float *w_beta, int64_t K, float *dx, void *stream);
+int bitlinear_train_backward_weight(const void *dy, const void *x, int64_t M, int64_t N, int64_t K,
+                                    float *dw, void *stream);
+
 /* LDS budget of the decode kernels for int8 activation rows (see below). */
 #define BITLINEAR_DECODE_MAX_ACT_BYTES 58368
 

@@ -260,3 +260,15 @@ def test_b3_sizes_and_validation():
     assert fn(FAKE, FAKE, None, 1, 320, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_ARG
     assert fn(FAKE, FAKE, FAKE, 65, 320, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.ERR_SHAPE
     assert fn(None, None, None, 0, 320, FAKE, FAKE, 16, FAKE, bl.F32, None) == bl.OK
+
+
+def test_train_validation():
+    L = bl.lib()
+    assert L.bitlinear_train_forward(None, 4, 256, FAKE, FAKE, 16, FAKE, None) == bl.ERR_ARG
+    assert L.bitlinear_train_forward(FAKE, 4, 0, FAKE, FAKE, 16, FAKE, None) == bl.ERR_SHAPE
+    assert L.bitlinear_train_forward(FAKE + 1, 4, 256, FAKE, FAKE, 16, FAKE, None) == bl.ERR_ALIGN
+    assert L.bitlinear_train_forward(FAKE, 0, 256, None, None, 16, None, None) == bl.OK
+    assert L.bitlinear_train_backward_input(FAKE, 4, 16, FAKE + 8, FAKE, 256, FAKE, None) == bl.ERR_ALIGN
+    assert L.bitlinear_train_backward_input(FAKE, -1, 16, FAKE, FAKE, 256, FAKE, None) == bl.ERR_SHAPE
+    assert L.bitlinear_train_backward_weight(FAKE, None, 4, 16, 256, FAKE, None) == bl.ERR_ARG
+    assert L.bitlinear_train_backward_weight(FAKE, FAKE, 4, 16, 256, FAKE + 2, None) == bl.ERR_ALIGN
