@@ -12,25 +12,33 @@
 // 4 waves (2 x 2) owns a 128 x 128 block of C, each wave 64 x 64 as 2 x 2
 // tiles of v_mfma_f32_32x32x16_bf16 (lane l holds A[l % 32][8 (l / 32) + j]
 // and B[8 (l / 32) + j][l % 32], j < 8).  Per 32-wide step of r both operand
-// tiles are staged in LDS as [row][r] bf16 rows (padded against bank
-// conflicts); the next step's pieces are loaded into registers while the
-// current step's MFMAs run.  The ternary operands come straight from the
-// 2-bit tiles: a piece of 8 codes (n, k .. k + 7) is the field (k % 256) / 64
-// of bytes 8 ((k % 16) / 8) .. + 7 of tile lane 16 ((k % 64) / 16) + n % 16,
-// widened to bf16 {-1, 0, +1}.  Operands that are rows of the source in the
-// contraction direction (x, dy in the forward and dx products, t in the
-// forward) go to LDS as 16-byte pieces; the others (t in dx, both in dw) are
-// written transposed, element by element.
+// tiles are staged in LDS in the orientation of their source, always as
+// 16-byte pieces, and the next step's pieces are loaded into registers while
+// the current step's MFMAs run:
+//   * sources whose rows run along the output index with r contiguous (x and
+//     dy in the forward and dx products, t in the forward) are stored as
+//     [row][r] and read with one 16-byte LDS read per operand;
+//   * sources whose rows run along r (t in dx, dy and x in dw) are stored as
+//     [r][row] and read with two transposing LDS reads (ds_read_b64_tr_b16:
+//     within 16 lanes, lane i receives element e from the 8-byte address of
+//     lane 4 e + i / 4, at offset i % 4; pointing lane j at row r0 + j / 4,
+//     column c0 + 4 (j % 4) gives lane i rows r0 .. r0 + 3 of column c0 + i).
+// The ternary operands come straight from the 2-bit tiles: a piece of 8
+// codes (n, k .. k + 7) is the field (k % 256) / 64 of bytes 8 ((k % 16) / 8)
+// .. + 7 of tile lane 16 ((k % 64) / 16) + n % 16, widened to bf16 {-1, 0, +1}.
 #include "bl_internal.h"
 
 namespace bl {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int TP = 128, TQ = 128, TR = 32;  // block of C, step of r
-constexpr int PITCH = TR + 8;               // bf16 per LDS row (80 bytes)
+constexpr int PITCH = TR + 8;               // bf16 per [row][r] LDS row (80 bytes)
+constexpr int PITCH_T = TP + 8;             // bf16 per [r][row] LDS row (272 bytes)
+constexpr int OPND = TP * PITCH > TR * PITCH_T ? TP * PITCH : TR * PITCH_T;  // bf16 per operand tile
 
 enum TrainMode { FWD = 0, DX = 1, DW = 2 };
 
@@ -83,11 +91,28 @@ __device__ inline u4 row_piece(const uint16_t* src, int ld, int rows, int cols, 
   return out;
 }
 
-__device__ inline uint16_t half_of(const u4& v, int j) { return (uint16_t)(v[j >> 1] >> (16 * (j & 1))); }
+// MFMA operand (8 bf16) of this lane from a [row][r] tile: rows row0 + l % 32,
+// r = r0 + 8 (l / 32) .. + 7.
+__device__ inline bf16x8 read_direct(const uint16_t* t, int row0, int r0, int lane) {
+  return *reinterpret_cast<const bf16x8*>(t + (row0 + (lane & 31)) * PITCH + r0 + 8 * (lane >> 5));
+}
+
+// The same operand from an [r][row] tile with two transposing reads.
+__device__ inline bf16x8 read_transposed(const uint16_t* t, int row0, int r0, int lane) {
+  const int grp = lane >> 4, i = lane & 15;
+  const int col = row0 + 16 * (grp & 1) + 4 * (i & 3);
+  const int r = r0 + 8 * (grp >> 1) + (i >> 2);
+  typedef __attribute__((address_space(3))) s16x4 lds_v4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(t + r * PITCH_T + col));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(t + (r + 4) * PITCH_T + col));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 
 template <int MODE>
 __global__ __launch_bounds__(256) void train_gemm_kernel(const TrainArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][TP * PITCH];  // [buffer][A, B][row][r]
+  // A (and B) is stored transposed, as [r][row], when its source rows run along r
+  constexpr bool AT = MODE == DW, BT = MODE != FWD;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][OPND];  // [buffer][A, B]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
@@ -116,29 +141,15 @@ __global__ __launch_bounds__(256) void train_gemm_kernel(const TrainArgs a) {
       }
     }
   };
+  // piece c of a [row][r] tile: row c / 4, r 8 (c % 4); of an [r][row] tile:
+  // r c / 16, rows 8 (c % 16) -- the same pieces the loaders fetch
+  auto slot = [](bool tr, int c) { return tr ? (c >> 4) * PITCH_T + 8 * (c & 15) : (c >> 2) * PITCH + 8 * (c & 3); };
   auto store = [&](int buf) {
-    uint16_t* A = lds[buf][0];
-    uint16_t* B = lds[buf][1];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = h * 256 + tid;
-      if constexpr (MODE == DW) {
-        const int r = c >> 4, x8 = 8 * (c & 15);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          A[(x8 + j) * PITCH + r] = half_of(pa[h], j);
-          B[(x8 + j) * PITCH + r] = half_of(pb[h], j);
-        }
-      } else {
-        *reinterpret_cast<u4*>(A + (c >> 2) * PITCH + 8 * (c & 3)) = pa[h];
-        if constexpr (MODE == FWD) {
-          *reinterpret_cast<u4*>(B + (c >> 2) * PITCH + 8 * (c & 3)) = pb[h];
-        } else {
-          const int r = c >> 4, x8 = 8 * (c & 15);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) B[(x8 + j) * PITCH + r] = half_of(pb[h], j);
-        }
-      }
+      *reinterpret_cast<u4*>(lds[buf][0] + slot(AT, c)) = pa[h];
+      *reinterpret_cast<u4*>(lds[buf][1] + slot(BT, c)) = pb[h];
     }
   };
 
@@ -164,10 +175,10 @@ __global__ __launch_bounds__(256) void train_gemm_kernel(const TrainArgs a) {
       bf16x8 av[2], bv[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        av[i] = *reinterpret_cast<const bf16x8*>(A + (wp * 64 + 32 * i + l32) * PITCH + 16 * ks + 8 * g);
+        av[i] = AT ? read_transposed(A, wp * 64 + 32 * i, 16 * ks, lane) : read_direct(A, wp * 64 + 32 * i, 16 * ks, lane);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        bv[j] = *reinterpret_cast<const bf16x8*>(B + (wq * 64 + 32 * j + l32) * PITCH + 16 * ks + 8 * g);
+        bv[j] = BT ? read_transposed(B, wq * 64 + 32 * j, 16 * ks, lane) : read_direct(B, wq * 64 + 32 * j, 16 * ks, lane);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
