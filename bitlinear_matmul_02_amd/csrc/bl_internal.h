@@ -122,6 +122,16 @@ __device__ inline v16i mfma32(v4i a, v4i b, v16i acc) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
 }
 
+// Tile index of workgroup b when T tiles are dealt round-robin to the 8 XCDs
+// (XCD x receives blocks x, x + 8, ...): XCD x gets the contiguous tiles
+// [start(x), start(x) + count(x)), so its L2 sees neighbouring tiles.
+__device__ inline int xcd_tile(int b, int T) {
+  const int x = b & 7, i = b >> 3;
+  int start = 0;
+  for (int j = 0; j < x; ++j) start += (T - j + 7) >> 3;
+  return start + i;
+}
+
 // Dequantize one accumulator (scaled by 64 by t2_field) and store it.
 __device__ inline void store_out(void* y, int y_dtype, int64_t idx, int acc64, float scale) {
   const int acc = acc64 >> 6;  // exact: every term is a multiple of 64

@@ -68,16 +68,6 @@ struct GemmTile {
   static constexpr int LDS = 2 * (SLAB_A + SLAB_B);   // double-buffered
 };
 
-// Tile index of workgroup b when T tiles are dealt round-robin to 8 XCDs:
-// XCD x receives blocks x, x+8, ...; give it the contiguous tiles
-// [start(x), start(x) + count(x)).
-__device__ inline int xcd_tile(int b, int T) {
-  const int x = b & 7, i = b >> 3;
-  int start = 0;
-  for (int j = 0; j < x; ++j) start += (T - j + 7) >> 3;
-  return start + i;
-}
-
 // Step s of a B1 chunk pair: 16 bits -> 16 bytes in {0, 1} (bit j -> byte j).
 __device__ inline v4i b1_bytes(uint32_t bits16) {
   v4i r;

@@ -11,21 +11,31 @@
 // for the three products; only the operand loaders differ.  A workgroup of
 // 4 waves (2 x 2) owns a 128 x 128 block of C, each wave 64 x 64 as 2 x 2
 // tiles of v_mfma_f32_32x32x16_bf16 (lane l holds A[l % 32][8 (l / 32) + j]
-// and B[8 (l / 32) + j][l % 32], j < 8).  Per 32-wide step of r both operand
-// tiles are staged in LDS in the orientation of their source, always as
-// 16-byte pieces, and the next step's pieces are loaded into registers while
-// the current step's MFMAs run:
+// and B[8 (l / 32) + j][l % 32], j < 8).  r advances in stages of 64:
+//   * each thread moves 4 16-byte pieces of each operand per stage; they are
+//     requested two stages ahead into a register ring and written into the
+//     free half of double-buffered LDS tiles between the MFMAs of the stage
+//     before, so the global-load latency is covered by two stages of work;
 //   * sources whose rows run along the output index with r contiguous (x and
 //     dy in the forward and dx products, t in the forward) are stored as
 //     [row][r] and read with one 16-byte LDS read per operand;
 //   * sources whose rows run along r (t in dx, dy and x in dw) are stored as
-//     [r][row] and read with two transposing LDS reads (ds_read_b64_tr_b16:
-//     within 16 lanes, lane i receives element e from the 8-byte address of
-//     lane 4 e + i / 4, at offset i % 4; pointing lane j at row r0 + j / 4,
-//     column c0 + 4 (j % 4) gives lane i rows r0 .. r0 + 3 of column c0 + i).
+//     [r][row], still as 16-byte pieces, and read with two transposing LDS
+//     reads (ds_read_b64_tr_b16: within 16 lanes, lane i receives element e
+//     from the 8-byte address of lane 4 e + i / 4, at offset i % 4; pointing
+//     lane j at row r0 + j / 4, column c0 + 4 (j % 4) gives lane i rows
+//     r0 .. r0 + 3 of column c0 + i).
+// When every bf16 row is a whole number of 16-byte pieces (row length a
+// multiple of 8, 16-byte aligned base) the loads are clamped into the matrix
+// and zeroed by a select, without branches, so the waits for a stage stay
+// partial; other shapes take an element-wise loader.
+//
 // The ternary operands come straight from the 2-bit tiles: a piece of 8
 // codes (n, k .. k + 7) is the field (k % 256) / 64 of bytes 8 ((k % 16) / 8)
-// .. + 7 of tile lane 16 ((k % 64) / 16) + n % 16, widened to bf16 {-1, 0, +1}.
+// .. + 7 of tile lane 16 ((k % 64) / 16) + n % 16; two codes at a time become
+// bf16 {-1, 0, +1} through one byte permute over constant tables.
+#include <mutex>
+
 #include "bl_internal.h"
 
 namespace bl {
@@ -35,10 +45,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int TP = 128, TQ = 128, TR = 32;  // block of C, step of r
-constexpr int PITCH = TR + 8;               // bf16 per [row][r] LDS row (80 bytes)
-constexpr int PITCH_T = TP + 8;             // bf16 per [r][row] LDS row (272 bytes)
+constexpr int TP = 128, TQ = 128, TR = 64;  // block of C, stage of r
+constexpr int NT = 256;                     // threads per workgroup
+constexpr int PITCH = TR + 8;               // bf16 per [row][r] LDS row (144 bytes)
+// bf16 per [r][row] LDS row (288 bytes = 72 banks): the four rows a
+// transposing read touches start 8 banks apart, so they do not collide
+constexpr int PITCH_T = TP + 16;
 constexpr int OPND = TP * PITCH > TR * PITCH_T ? TP * PITCH : TR * PITCH_T;  // bf16 per operand tile
+constexpr int LDS_BYTES = 2 * 2 * OPND * 2;  // [buffer][A, B]
+constexpr int NP = TP * TR / 8 / NT;         // pieces per thread, operand and stage
+static_assert(NP == TR / 16, "one piece of each operand is stored per 16-wide MFMA step");
 
 enum TrainMode { FWD = 0, DX = 1, DW = 2 };
 
@@ -54,41 +70,57 @@ struct TrainArgs {
   int tiles_q;
 };
 
-// Eight ternary codes of row n, columns k .. k + 7 (k % 8 == 0) as bf16 bits;
-// zero past the rows or tiles of t (the padding codes are 0 anyway).
-__device__ inline u4 t2_piece(const TrainArgs& a, int n, int k) {
-  if (n >= a.N || k >= a.Kt * kTileK) return u4{0u, 0u, 0u, 0u};
-  const int kb = k >> 8, c = k & 255;
-  const int i = c >> 6, L = 16 * ((c & 63) >> 4) + (n & 15), h = (c & 15) >> 3;
-  const uint2 w = *reinterpret_cast<const uint2*>(a.packed + ((int64_t)(n >> 4) * a.Kt + kb) * kTileBytes + 16 * L + 8 * h);
+// bf16 bits of the codes in bytes 0 and 2 of y (2-bit two's complement t):
+// the permute picks the low byte (0x80 unless t = 0) and the high byte (0x3F
+// or 0xBF) of each value from constant tables indexed by the code.
+__device__ inline uint32_t t2_pair(uint32_t y) {
+  const uint32_t sel = y * 0x0101u + 0x00040004u;  // bytes: c0 + 4, c0, c1 + 4, c1
+  return __builtin_amdgcn_perm(0x80008000u, 0xBF003F00u, sel);
+}
+
+// Field i of 8 packed bytes as 8 bf16 values (byte j -> value j).
+__device__ inline u4 t2_decode(const uint2 w, int i) {
   u4 out;
 #pragma unroll
   for (int d = 0; d < 2; ++d) {
-    const uint32_t word = d ? w.y : w.x;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      uint32_t pair = 0;
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const uint32_t code = (word >> (8 * (2 * p + b) + 2 * i)) & 3u;  // 01 = +1, 11 = -1, 00 = 0
-        const uint32_t v = (code & 1u) ? (0x3F80u | ((code & 2u) << 14)) : 0u;
-        pair |= v << (16 * b);
-      }
-      out[2 * d + p] = pair;
-    }
+    const uint32_t x = ((d ? w.y : w.x) >> (2 * i)) & 0x03030303u;
+    out[2 * d] = t2_pair(__builtin_amdgcn_perm(x, x, 0x0c010c00u));
+    out[2 * d + 1] = t2_pair(__builtin_amdgcn_perm(x, x, 0x0c030c02u));
   }
   return out;
 }
 
+// Eight ternary codes of row n, columns k .. k + 7 (k % 8 == 0) as bf16 bits;
+// zero past the rows or tiles of t (the padding codes are 0 anyway).  The load
+// is clamped into the tiles, so no branch is needed.
+__device__ inline u4 t2_piece(const TrainArgs& a, int n, int k) {
+  const int kmax = a.Kt * kTileK;
+  const bool in = n < a.N && k < kmax;
+  n = min(n, a.N - 1);
+  k = min(k, kmax - 8);
+  const int kb = k >> 8, c = k & 255;
+  const int i = c >> 6, L = 16 * ((c & 63) >> 4) + (n & 15), h = (c & 15) >> 3;
+  const uint2 w = *reinterpret_cast<const uint2*>(a.packed + ((int64_t)(n >> 4) * a.Kt + kb) * kTileBytes + 16 * L + 8 * h);
+  const u4 v = t2_decode(w, i);
+  return in ? v : u4{0u, 0u, 0u, 0u};
+}
+
 // Eight bf16 of row `row`, columns col .. col + 7 of a row-major source with
-// `rows` rows and `cols` columns; zero outside.
+// `rows` rows and `cols` columns (row length ld); zero outside.  ALIGNED: ld
+// == cols is a multiple of 8 and the base is 16-byte aligned.
+template <bool ALIGNED>
 __device__ inline u4 row_piece(const uint16_t* src, int ld, int rows, int cols, int row, int col) {
-  if (row >= rows || col >= cols) return u4{0u, 0u, 0u, 0u};
-  const uint16_t* p = src + (int64_t)row * ld + col;
-  if (col + 8 <= cols && (reinterpret_cast<uintptr_t>(p) & 15) == 0) return *reinterpret_cast<const u4*>(p);
-  u4 out = {0u, 0u, 0u, 0u};
-  for (int j = 0; j < 8 && col + j < cols; ++j) out[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
-  return out;
+  if constexpr (ALIGNED) {
+    const bool in = row < rows && col < cols;
+    const u4 v = *reinterpret_cast<const u4*>(src + (int64_t)min(row, rows - 1) * ld + min(col, cols - 8));
+    return in ? v : u4{0u, 0u, 0u, 0u};
+  } else {
+    if (row >= rows || col >= cols) return u4{0u, 0u, 0u, 0u};
+    const uint16_t* p = src + (int64_t)row * ld + col;
+    u4 out = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < 8 && col + j < cols; ++j) out[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
+    return out;
+  }
 }
 
 // MFMA operand (8 bf16) of this lane from a [row][r] tile: rows row0 + l % 32,
@@ -105,52 +137,63 @@ __device__ inline bf16x8 read_transposed(const uint16_t* t, int row0, int r0, in
   typedef __attribute__((address_space(3))) s16x4 lds_v4;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(t + r * PITCH_T + col));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(t + (r + 4) * PITCH_T + col));
+  // one whole-vector shuffle: rebuilding the operand element by element from
+  // the two reads has been folded into a splat of element 0 by the compiler
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void train_gemm_kernel(const TrainArgs a) {
+template <int MODE, bool ALIGNED>
+__global__ __launch_bounds__(NT) void train_gemm_kernel(const TrainArgs a) {
   // A (and B) is stored transposed, as [r][row], when its source rows run along r
   constexpr bool AT = MODE == DW, BT = MODE != FWD;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][OPND];  // [buffer][A, B]
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [buffer][A, B][OPND]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave >> 1, wq = wave & 1;
-  const int tp = blockIdx.x / a.tiles_q, tq = blockIdx.x - tp * a.tiles_q;
+  // the XCD's contiguous run of tiles, walked in groups of 4 row blocks of C
+  // along Q (they share their A rows and B columns in that XCD's L2)
+  constexpr int GM = 4;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int tiles_p = (int)(gridDim.x / a.tiles_q);
+  const int group = tile / (GM * a.tiles_q), within = tile - group * GM * a.tiles_q;
+  const int gm = min(GM, tiles_p - group * GM);
+  const int tp = group * GM + within % gm, tq = within / gm;
   const int p0 = tp * TP, q0 = tq * TQ;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // Each thread moves two 8-value pieces of each operand per step.  Pieces
-  // of a row-major source along r: piece c -> row c / 4, columns 8 (c % 4).
-  // Pieces of a source whose rows run along r (transposed into LDS): piece c
-  // -> source row (r) c / 16, columns (P or Q index) 8 (c % 16).
-  u4 pa[2], pb[2];
-  auto load = [&](int r0) {
+  // Pieces of a source row-major along r: piece c -> row c / 8, r 8 (c % 8).
+  // Pieces of a source whose rows run along r: piece c -> r c / 16, row
+  // (P or Q index) 8 (c % 16).
+  auto load = [&](u4 (&pa)[NP], u4 (&pb)[NP], int r0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = h * 256 + tid;
+    for (int h = 0; h < NP; ++h) {
+      const int c = h * NT + tid;
       if constexpr (MODE == DW) {
-        pa[h] = row_piece(a.a, a.lda, a.R, a.P, r0 + (c >> 4), p0 + 8 * (c & 15));  // dy[m][n], n along P
-        pb[h] = row_piece(a.b, a.ldb, a.R, a.Q, r0 + (c >> 4), q0 + 8 * (c & 15));  // x[m][k], k along Q
+        pa[h] = row_piece<ALIGNED>(a.a, a.lda, a.R, a.P, r0 + (c >> 4), p0 + 8 * (c & 15));  // dy[m][n], n along P
+        pb[h] = row_piece<ALIGNED>(a.b, a.ldb, a.R, a.Q, r0 + (c >> 4), q0 + 8 * (c & 15));  // x[m][k], k along Q
       } else {
-        pa[h] = row_piece(a.a, a.lda, a.P, a.R, p0 + (c >> 2), r0 + 8 * (c & 3));   // x or dy rows
+        pa[h] = row_piece<ALIGNED>(a.a, a.lda, a.P, a.R, p0 + (c >> 3), r0 + 8 * (c & 7));   // x or dy rows
         if constexpr (MODE == FWD)
-          pb[h] = t2_piece(a, q0 + (c >> 2), r0 + 8 * (c & 3));                     // t[n][k], k along r
+          pb[h] = t2_piece(a, q0 + (c >> 3), r0 + 8 * (c & 7));                              // t[n][k], k along r
         else
-          pb[h] = t2_piece(a, r0 + (c >> 4), q0 + 8 * (c & 15));                    // t[n][k], n along r
+          pb[h] = t2_piece(a, r0 + (c >> 4), q0 + 8 * (c & 15));                             // t[n][k], n along r
       }
     }
   };
-  // piece c of a [row][r] tile: row c / 4, r 8 (c % 4); of an [r][row] tile:
-  // r c / 16, rows 8 (c % 16) -- the same pieces the loaders fetch
-  auto slot = [](bool tr, int c) { return tr ? (c >> 4) * PITCH_T + 8 * (c & 15) : (c >> 2) * PITCH + 8 * (c & 3); };
-  auto store = [&](int buf) {
+  // LDS slot of piece c: the same pieces the loaders fetch
+  auto slot = [](bool tr, int c) { return tr ? (c >> 4) * PITCH_T + 8 * (c & 15) : (c >> 3) * PITCH + 8 * (c & 7); };
+  auto store_piece = [&](int buf, const u4 (&pa)[NP], const u4 (&pb)[NP], int h) {
+    const int c = h * NT + tid;
+    *reinterpret_cast<u4*>(lds + (2 * buf) * OPND + slot(AT, c)) = pa[h];
+    *reinterpret_cast<u4*>(lds + (2 * buf + 1) * OPND + slot(BT, c)) = pb[h];
+  };
+  auto read_ops = [&](bf16x8 (&av)[2], bf16x8 (&bv)[2], const uint16_t* A, const uint16_t* B, int ks) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = h * 256 + tid;
-      *reinterpret_cast<u4*>(lds[buf][0] + slot(AT, c)) = pa[h];
-      *reinterpret_cast<u4*>(lds[buf][1] + slot(BT, c)) = pb[h];
-    }
+    for (int i = 0; i < 2; ++i)
+      av[i] = AT ? read_transposed(A, wp * 64 + 32 * i, 16 * ks, lane) : read_direct(A, wp * 64 + 32 * i, 16 * ks, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      bv[j] = BT ? read_transposed(B, wq * 64 + 32 * j, 16 * ks, lane) : read_direct(B, wq * 64 + 32 * j, 16 * ks, lane);
   };
 
   f32x16 acc[2][2];
@@ -161,32 +204,46 @@ __global__ __launch_bounds__(256) void train_gemm_kernel(const TrainArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int steps = (a.R + TR - 1) / TR;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < steps) load((s + 1) * TR);  // in flight during the MFMAs
-    const uint16_t* A = lds[buf][0];
-    const uint16_t* B = lds[buf][1];
+  // One stage from LDS half buf; the pieces (na, nb) of a later stage go to
+  // the other half, one of each per 16-wide step, between the MFMAs.
+  auto compute = [&](int buf, const u4 (&na)[NP], const u4 (&nb)[NP]) {
+    const uint16_t* A = lds + (2 * buf) * OPND;
+    const uint16_t* B = lds + (2 * buf + 1) * OPND;
+    bf16x8 av[2][2], bv[2][2];
+    read_ops(av[0], bv[0], A, B, 0);
 #pragma unroll
     for (int ks = 0; ks < TR / 16; ++ks) {
-      bf16x8 av[2], bv[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        av[i] = AT ? read_transposed(A, wp * 64 + 32 * i, 16 * ks, lane) : read_direct(A, wp * 64 + 32 * i, 16 * ks, lane);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bv[j] = BT ? read_transposed(B, wq * 64 + 32 * j, 16 * ks, lane) : read_direct(B, wq * 64 + 32 * j, 16 * ks, lane);
+      const int cur = ks & 1;
+      if (ks + 1 < TR / 16) read_ops(av[cur ^ 1], bv[cur ^ 1], A, B, ks + 1);
+      store_piece(buf ^ 1, na, nb, ks);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < steps) store(buf ^ 1);
+  };
+
+  // ring of two stages in registers; requests past the last stage re-read it
+  // (in bounds) and their pieces are never read from LDS
+  const int steps = (a.R + TR - 1) / TR;
+  auto rs = [&](int s) { return min(s, steps - 1) * TR; };
+  u4 ra0[NP], rb0[NP], ra1[NP], rb1[NP];
+  load(ra0, rb0, rs(0));
+  load(ra1, rb1, rs(1));
+#pragma unroll
+  for (int h = 0; h < NP; ++h) store_piece(0, ra0, rb0, h);
+  __syncthreads();
+  int s = 0;
+  for (; s + 2 <= steps; s += 2) {
+    load(ra0, rb0, rs(s + 2));  // stage s went to LDS half 0 before
+    compute(0, ra1, rb1);       // stage s; stage s + 1 into half 1
+    __syncthreads();
+    load(ra1, rb1, rs(s + 3));
+    compute(1, ra0, rb0);       // stage s + 1; stage s + 2 into half 0
     __syncthreads();
   }
+  if (s < steps) compute(0, ra1, rb1);  // the last stage (its copy into half 1 is never read)
 
   const float scale = MODE == DW ? 1.0f : *a.beta;
 #pragma unroll
@@ -203,12 +260,28 @@ __global__ __launch_bounds__(256) void train_gemm_kernel(const TrainArgs a) {
     }
 }
 
-template <int MODE>
-hipError_t launch(const TrainArgs& a, hipStream_t s) {
+template <int MODE, bool ALIGNED>
+hipError_t launch_aligned(const TrainArgs& a, hipStream_t s) {
+  static std::once_flag once;
+  static hipError_t attr = hipSuccess;
+  std::call_once(once, [] {
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&train_gemm_kernel<MODE, ALIGNED>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+  });
+  if (attr != hipSuccess) return attr;
   const int tiles_p = (a.P + TP - 1) / TP;
-  hipLaunchKernelGGL((train_gemm_kernel<MODE>), dim3((unsigned)(tiles_p * a.tiles_q)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((train_gemm_kernel<MODE, ALIGNED>), dim3((unsigned)(tiles_p * a.tiles_q)), dim3(NT), LDS_BYTES,
+                     s, a);
   return hipGetLastError();
 }
+
+template <int MODE>
+hipError_t launch(const TrainArgs& a, bool aligned, hipStream_t s) {
+  return aligned ? launch_aligned<MODE, true>(a, s) : launch_aligned<MODE, false>(a, s);
+}
+
+// bf16 rows of `len` values starting at p are whole, aligned 16-byte pieces
+bool pieces(const void* p, int64_t len) { return len % 8 == 0 && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 }  // namespace
 
@@ -223,7 +296,7 @@ hipError_t launch_train_forward(const uint16_t* x, int64_t M, int64_t K, const u
   a.lda = (int)K;
   a.Kt = (int)ceil_div(K, kTileK), a.N = (int)N;
   a.tiles_q = (int)ceil_div(N, TQ);
-  return launch<FWD>(a, s);
+  return launch<FWD>(a, pieces(x, K), s);
 }
 
 hipError_t launch_train_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8_t* packed, const float* beta,
@@ -237,7 +310,7 @@ hipError_t launch_train_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8
   a.lda = (int)N;
   a.Kt = (int)ceil_div(K, kTileK), a.N = (int)N;
   a.tiles_q = (int)ceil_div(K, TQ);
-  return launch<DX>(a, s);
+  return launch<DX>(a, pieces(dy, N), s);
 }
 
 hipError_t launch_train_dw(const uint16_t* dy, const uint16_t* x, int64_t M, int64_t N, int64_t K, float* dw,
@@ -249,7 +322,7 @@ hipError_t launch_train_dw(const uint16_t* dy, const uint16_t* x, int64_t M, int
   a.P = (int)N, a.Q = (int)K, a.R = (int)M;
   a.lda = (int)N, a.ldb = (int)K;
   a.tiles_q = (int)ceil_div(K, TQ);
-  return launch<DW>(a, s);
+  return launch<DW>(a, pieces(dy, N) && pieces(x, K), s);
 }
 
 }  // namespace bl
