@@ -45,6 +45,12 @@
 // Workgroups are numbered so that each of the 8 XCDs (blocks are dealt to
 // them round-robin) works on a contiguous run of output tiles, walked in
 // groups of 4 token blocks along N, which share both operands in its L2.
+//
+// Up to 64 tokens (decode with a batch) the blocks are 64 x 128, and when
+// that leaves fewer workgroups than compute units the k-steps are split
+// across S workgroups per block: each writes its int32 sums to a workspace
+// slice [S][M][N] and a second kernel adds the S slices and dequantizes.
+// Integer sums are exact in any order, so the result equals the unsplit one.
 #include <mutex>
 #include <type_traits>
 
@@ -76,14 +82,14 @@ __device__ inline v4i b1_bytes(uint32_t bits16) {
   return r;
 }
 
-template <int BM, int BN, int D, int FMT>
+template <int BM, int BN, int D, int FMT, bool SPLIT>
 __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__ q, int64_t ldq,
                                                       const float* __restrict__ ds,
                                                       const int32_t* __restrict__ rowsum, int M,
                                                       const uint8_t* __restrict__ packed,
                                                       const float* __restrict__ beta, int N, int Nt,
                                                       int Kt, int KtW, int tiles_n, void* __restrict__ y,
-                                                      int y_dtype) {
+                                                      int y_dtype, int splits, int32_t* __restrict__ part) {
   using G = GemmTile<BM, BN, FMT>;
   using BT = typename std::conditional<FMT != 0, uint2, u4>::type;  // one weight piece
   constexpr int MB = G::MB, NB = G::NB;
@@ -97,8 +103,16 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
   const int wm = wave / G::WGN, wn = wave % G::WGN;
   // within an XCD's run of tiles, walk groups of GM token blocks along N
   constexpr int GM = 4;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int tiles_m = (int)(gridDim.x / tiles_n);
+  // SPLIT: the XCD's run covers consecutive tiles of one split (one k-range),
+  // which share the activation columns of that range
+  const int lin = xcd_tile(blockIdx.x, gridDim.x);
+  const int ntiles = SPLIT ? (int)(gridDim.x / splits) : (int)gridDim.x;
+  const int split = SPLIT ? lin / ntiles : 0;
+  const int tile = lin - split * ntiles;
+  const int per = SPLIT ? (Kt + splits - 1) / splits : Kt;
+  const int kt0 = split * per;                // first k-step of this workgroup
+  const int nk = min(per, Kt - kt0);          // k-steps (>= 1: the host sizes the splits)
+  const int tiles_m = ntiles / tiles_n;
   const int group = tile / (GM * tiles_n), within = tile - group * GM * tiles_n;
   const int gm = min(GM, tiles_m - group * GM);  // token blocks in this group
   const int tm = group * GM + within % gm, tn = within / gm;
@@ -212,18 +226,18 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
   // prologue: k-steps 0 .. D-1 requested (indices past the end re-read the
   // last k-step, in bounds, never used); k-step 0 into LDS half 0
 #pragma unroll
-  for (int u = 0; u < D; ++u) load(u, min(u, Kt - 1));
+  for (int u = 0; u < D; ++u) load(u, kt0 + min(u, nk - 1));
 #pragma unroll
   for (int i = 0; i < G::PA + G::PB; ++i) stage_piece(0, 0, i);
   __syncthreads();
 
   // full rounds of the ring, free of branches so the waits stay partial
   int k0 = 0;
-  for (; k0 + D < Kt; k0 += D) {
+  for (; k0 + D < nk; k0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       const int kt = k0 + u;
-      load(u, min(kt + D, Kt - 1));  // slot u (k-step kt) went to LDS during the previous k-step
+      load(u, kt0 + min(kt + D, nk - 1));  // slot u (k-step kt) went to LDS during the previous k-step
       compute(kt & 1, true, (u + 1) % D);
       __syncthreads();
     }
@@ -232,14 +246,31 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
 #pragma unroll
   for (int u = 0; u < D; ++u) {
     const int kt = k0 + u;
-    if (kt < Kt) {  // uniform
-      compute(kt & 1, kt + 1 < Kt, (u + 1) % D);
+    if (kt < nk) {  // uniform
+      compute(kt & 1, kt + 1 < nk, (u + 1) % D);
       __syncthreads();
     }
   }
 
-  const float bt = *beta;
   const int n_wave = nt0 * kTileN + wn * G::WN;
+  if constexpr (SPLIT) {
+    // raw sums of this k-range into slice `split` of the workspace
+    int32_t* slice = part + (int64_t)split * M * N;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * G::WM + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int n = n_wave + 32 * j + r32;
+          if (n < N) slice[(int64_t)m * N + n] = acc[mb][j][e];
+        }
+      }
+    return;
+  }
+  const float bt = *beta;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -258,28 +289,82 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
     }
 }
 
-template <int BM, int BN, int D, int FMT>
+// Sum of the S workspace slices and the dequantization of the unsplit
+// epilogue (the same expressions), one output element per thread; the slices
+// are zeroed again, so the workspace leaves the call as it came in.
+template <int FMT>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(int32_t* __restrict__ part, int S, int M, int N,
+                                                          const float* __restrict__ ds,
+                                                          const int32_t* __restrict__ rowsum,
+                                                          const float* __restrict__ beta, void* __restrict__ y,
+                                                          int y_dtype) {
+  const int64_t mn = (int64_t)M * N;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= mn) return;
+  int acc = 0;
+  for (int sp = 0; sp < S; ++sp) {
+    int32_t* p = part + sp * mn + i;
+    acc += *p;
+    *p = 0;
+  }
+  const int m = (int)(i / N);
+  const float scale = ds[m] * *beta;
+  const int v = FMT ? (2 * acc - rowsum[m]) * 64 : acc;
+  store_out(y, y_dtype, i, v, scale);
+}
+
+template <int BM, int BN, int D, int FMT, bool SPLIT = false>
 hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
-                       const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+                       const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
+                       int splits = 1, int32_t* part = nullptr) {
   using G = GemmTile<BM, BN, FMT>;
   static std::once_flag once;
   static hipError_t attr = hipSuccess;
   std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT>),
+    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT, SPLIT>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
   });
   if (attr != hipSuccess) return attr;
   const int Nt = (int)ceil_div(N, kTileN), Kt = (int)ceil_div(K, kTileK);
   const int KtW = (int)ceil_div(K, FMT ? kTileKB1 : kTileK);
   const int tiles_n = (int)ceil_div(N, BN), tiles_m = (int)ceil_div(M, BM);
-  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D, FMT>), dim3((unsigned)(tiles_m * tiles_n)), dim3(G::NT), G::LDS, s,
-                     q, ldq, ds, rowsum, (int)M, packed, beta, (int)N, Nt, Kt, KtW, tiles_n, y, y_dtype);
+  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D, FMT, SPLIT>), dim3((unsigned)(tiles_m * tiles_n * splits)),
+                     dim3(G::NT), G::LDS, s, q, ldq, ds, rowsum, (int)M, packed, beta, (int)N, Nt, Kt, KtW, tiles_n,
+                     y, y_dtype, splits, part);
+  if (!SPLIT) return hipGetLastError();
+  hipLaunchKernelGGL((gemm_reduce_kernel<FMT>), dim3((unsigned)ceil_div(M * N, 256)), dim3(256), 0, s, part, splits,
+                     (int)M, (int)N, ds, rowsum, beta, y, y_dtype);
   return hipGetLastError();
+}
+
+// Up to 64 tokens: 64 x 128 blocks, and k split across workgroups while the
+// blocks alone leave at least half of the compute units idle (S whole
+// multiples of the block count up to one workgroup per unit, each split
+// keeping at least 4 k-steps).  Returns the number of splits; every split is
+// non-empty.
+constexpr int kMidM = 64, kMidN = 128, kMidGrid = 256, kMidMinSteps = 4;
+int mid_splits(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ceil_div(M, kMidM) * ceil_div(N, kMidN), Kt = ceil_div(K, kTileK);
+  int64_t S = kMidGrid / tiles;
+  if (S > Kt / kMidMinSteps) S = Kt / kMidMinSteps;
+  if (S < 2) return 1;
+  const int64_t per = ceil_div(Kt, S);
+  return (int)ceil_div(Kt, per);
 }
 
 template <int FMT>
 hipError_t launch_fmt(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
-                      const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
+                      const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
+                      void* ws = nullptr) {
+  if constexpr (FMT == 0) {
+    if (M <= kMidM) {
+      const int S = mid_splits(M, N, K);
+      if (S > 1)
+        return launch_tile<kMidM, kMidN, 2, FMT, true>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, S,
+                                                        static_cast<int32_t*>(ws));
+      return launch_tile<kMidM, kMidN, 2, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s);
+    }
+  }
   // 128 x 256 blocks when that still gives a few hundred workgroups,
   // 128 x 128 otherwise
   const int64_t big = ceil_div(M, 128) * ceil_div(N, 256);
@@ -289,12 +374,16 @@ hipError_t launch_fmt(const int8_t* q, int64_t ldq, const float* ds, const int32
 
 }  // namespace
 
-int64_t gemm_ws_bytes(int64_t, int64_t, int64_t) { return 0; }
+int64_t gemm_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M > kMidM) return 0;
+  const int S = mid_splits(M, N, K);
+  return S > 1 ? (int64_t)S * M * N * 4 : 0;
+}
 
 hipError_t launch_gemm_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
-                          int y_dtype, void*, hipStream_t s) {
-  return launch_fmt<0>(q, ldq, ds, nullptr, M, K, packed, beta, N, y, y_dtype, s);
+                          int y_dtype, void* ws, hipStream_t s) {
+  return launch_fmt<0>(q, ldq, ds, nullptr, M, K, packed, beta, N, y, y_dtype, s, ws);
 }
 
 hipError_t launch_gemm_b1(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,

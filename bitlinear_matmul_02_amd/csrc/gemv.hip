@@ -970,7 +970,18 @@ hipError_t launch_gemv_b3(const int8_t* q, int64_t ldq, const float* ds, const i
   return dispatch_mb_nb<AGLOBAL, false, 2>(p, a, s);
 }
 
-int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) { return make_plan(M, N, K, false).ws_bytes; }
+// Token counts for which the 64-row matrix-core path of the prefill product
+// (bitlinear_gemm's, bit-identical results) beats this kernel: from 49
+// tokens; from 33 on matrices of 2^24 weights or more; from 24 on 2^27 or
+// more (measured on the 2B- and 100B-class shapes).
+bool gemv_prefers_gemm(int64_t M, int64_t N, int64_t K) {
+  const int64_t w = N * K;
+  return M > 48 || (M > 32 && w >= (int64_t(1) << 24)) || (M >= 24 && w >= (int64_t(1) << 27));
+}
+
+int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return gemv_prefers_gemm(M, N, K) ? gemm_ws_bytes(M, N, K) : make_plan(M, N, K, false).ws_bytes;
+}
 
 bool decode_fused_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= BITLINEAR_GEMV_MAX_M && M * lds_row(K) <= kDecodeLdsBytes;
@@ -979,6 +990,7 @@ bool decode_fused_fits(int64_t M, int64_t K) {
 hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K,
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s) {
+  if (gemv_prefers_gemm(M, N, K)) return launch_gemm_t2(q, ldq, ds, M, K, packed, beta, N, y, y_dtype, ws, s);
   const GemvPlan p = make_plan(M, N, K, false, true, M * (ldq / 16));
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, ws);
   a.q = q;

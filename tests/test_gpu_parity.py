@@ -207,6 +207,37 @@ def test_gemm_parity(M, N, K):
     check_product(xb, w, use_gemm=True)
 
 
+# ----------------------------------- up to 64 tokens on the int8 matrix cores
+@pytest.mark.parametrize("M,N,K,split", [(1, 1000, 4096, True), (37, 333, 6925, True), (64, 6912, 2560, True),
+                                         (24, 130, 2048, True), (17, 2560, 6912, True), (64, 64, 512, False),
+                                         (64, 28672, 1024, False)])
+def test_gemm_small_batch_parity(M, N, K, split):
+    """64-row blocks; with few blocks the k-steps are split across workgroups
+    (int32 partial sums in the workspace, added and dequantized by a second
+    kernel, which zeroes them again)."""
+    need = bl.gemm_workspace_bytes(M, N, K)
+    assert (need > 0) == split
+    w = workloads.gen_weights(N, K, seed=7000 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=8000 + M, outliers=True)
+    ref = oracle.bitlinear_forward(xb, w, threads=8)
+    for _ in range(2):  # the same cached workspace twice
+        check_product(xb, w, use_gemm=True, ref=ref)
+    if need > 0:
+        ws = bl.workspace(need, DEV)
+        torch.cuda.synchronize()
+        assert not ws[:need].any().item()
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 16384, 8192), (33, 4096, 4096), (49, 300, 1000), (32, 2560, 2560),
+                                   (23, 16384, 8192)])
+def test_gemv_large_batches(M, N, K):
+    """bitlinear_gemv hands larger batches to the 64-row matrix-core path (from
+    24 tokens on 2^27 weights, 33 on 2^24, 49 on any); results are the same."""
+    w = workloads.gen_weights(N, K, seed=9000 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=9500 + M)
+    check_product(xb, w, use_gemm=False, dtypes=("i32", "f32"))
+
+
 def test_gemv_split_k_workspace_left_zero():
     # a long K with few outputs makes the plan split K across workgroups
     M, N, K = 3, 48, 40000
