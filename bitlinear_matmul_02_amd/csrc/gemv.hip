@@ -131,9 +131,11 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   if (p.NB > nb_cap) p.NB = nb_cap;
   p.Ng = (int)ceil_div(p.Nt, p.NB);
   const int maxw = max_waves(p.MB);
-  // one token block with operands from global memory and many output groups
-  // (e.g. 8 tokens, K = 8192): one wave streams the whole k-range
-  const int target = p.MB == 1 ? (p.amode == AGLOBAL && p.Ng >= 512 ? 32 : (p.Kt >= 32 ? 16 : 8)) : 5;
+  // one token block with operands from global memory, many output groups and
+  // 32 or more k-tiles (e.g. 8 tokens, K = 8192 at 2 bits): one wave streams
+  // 32 k-tiles
+  const int target =
+      p.MB == 1 ? (p.Kt >= 32 ? (p.amode == AGLOBAL && p.Ng >= 512 ? 32 : 16) : 8) : 5;
   int waves = (int)ceil_div(p.Kt, target);
   if (p.MB == 1 && p.Ng < 512) {
     // about one workgroup per CU: keep all four SIMDs busy with whole

@@ -104,8 +104,12 @@ int64_t bitlinear_pack_workspace_bytes(int64_t N, int64_t K);
 
 /*
  * Workspace bytes bitlinear_gemv / bitlinear_gemm need for this shape (may be
- * 0).  A workspace must be filled with zeros once before its first use; every
- * call that returns BITLINEAR_OK leaves it filled with zeros again.
+ * 0): int32 partial sums when the k-range of a product is split across
+ * workgroups (few output columns with a long K for bitlinear_gemv; up to 64
+ * tokens with few output blocks for bitlinear_gemm, which bitlinear_gemv also
+ * uses for its larger batches).  A workspace must be filled with zeros once
+ * before its first use; every call that returns BITLINEAR_OK leaves it filled
+ * with zeros again.  Calls that share a workspace must not run concurrently.
  */
 int64_t bitlinear_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
