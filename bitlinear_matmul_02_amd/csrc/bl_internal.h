@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "bitlinear.h"
 
 namespace bl {
@@ -120,6 +123,26 @@ __device__ inline v4i mfma16(v4i a, v4i b, v4i acc) {
 // output element e of lane l is D[8 * (e / 4) + 4 * (l / 32) + e % 4][l % 32].
 __device__ inline v16i mfma32(v4i a, v4i b, v16i acc) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
+}
+
+// Raises a kernel's dynamic LDS limit on the current device, once per device
+// (the attribute belongs to the device that is current when it is set).
+struct LdsLimit {
+  std::atomic<uint64_t> done{0};  // bit d: raised on device d
+  std::mutex mu;
+};
+inline hipError_t ensure_lds_limit(LdsLimit& l, const void* func, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  const uint64_t bit = uint64_t(1) << dev;
+  if (l.done.load(std::memory_order_acquire) & bit) return hipSuccess;
+  std::lock_guard<std::mutex> g(l.mu);
+  if (l.done.load(std::memory_order_relaxed) & bit) return hipSuccess;
+  e = hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) l.done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 // Tile index of workgroup b when T tiles are dealt round-robin to the 8 XCDs

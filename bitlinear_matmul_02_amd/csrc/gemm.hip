@@ -51,7 +51,6 @@
 // across S workgroups per block: each writes its int32 sums to a workspace
 // slice [S][M][N] and a second kernel adds the S slices and dequantizes.
 // Integer sums are exact in any order, so the result equals the unsplit one.
-#include <mutex>
 #include <type_traits>
 
 #include "bl_internal.h"
@@ -318,12 +317,9 @@ hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, const int3
                        const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
                        int splits = 1, int32_t* part = nullptr) {
   using G = GemmTile<BM, BN, FMT>;
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT, SPLIT>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-  });
+  static LdsLimit lim;
+  const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT, SPLIT>),
+                                           G::LDS);
   if (attr != hipSuccess) return attr;
   const int Nt = (int)ceil_div(N, kTileN), Kt = (int)ceil_div(K, kTileK);
   const int KtW = (int)ceil_div(K, FMT ? kTileKB1 : kTileK);

@@ -63,8 +63,6 @@
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
 // workspace again.
-#include <mutex>
-
 #include "bl_internal.h"
 
 namespace bl {
@@ -820,13 +818,10 @@ template <int MB, int NB, int AM, bool NORM, int FMT = 0>
 hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   if constexpr (AM != AGLOBAL) {
     // static LDS plus the largest activation rows can pass the default 64 KB
-    // per workgroup: raise the limit once
-    static std::once_flag once;
-    static hipError_t attr = hipSuccess;
-    std::call_once(once, [] {
-      attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT>),
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDecodeLdsBytes);
-    });
+    // per workgroup: raise the limit (once per device)
+    static LdsLimit lim;
+    const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT>),
+                                             (int)kDecodeLdsBytes);
     if (attr != hipSuccess) return attr;
   }
   hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM, FMT>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),

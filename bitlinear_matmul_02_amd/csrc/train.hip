@@ -34,8 +34,6 @@
 // codes (n, k .. k + 7) is the field (k % 256) / 64 of bytes 8 ((k % 16) / 8)
 // .. + 7 of tile lane 16 ((k % 64) / 16) + n % 16; two codes at a time become
 // bf16 {-1, 0, +1} through one byte permute over constant tables.
-#include <mutex>
-
 #include "bl_internal.h"
 
 namespace bl {
@@ -262,12 +260,9 @@ __global__ __launch_bounds__(NT) void train_gemm_kernel(const TrainArgs a) {
 
 template <int MODE, bool ALIGNED>
 hipError_t launch_aligned(const TrainArgs& a, hipStream_t s) {
-  static std::once_flag once;
-  static hipError_t attr = hipSuccess;
-  std::call_once(once, [] {
-    attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&train_gemm_kernel<MODE, ALIGNED>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-  });
+  static LdsLimit lim;
+  const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&train_gemm_kernel<MODE, ALIGNED>),
+                                           LDS_BYTES);
   if (attr != hipSuccess) return attr;
   const int tiles_p = (a.P + TP - 1) / TP;
   hipLaunchKernelGGL((train_gemm_kernel<MODE, ALIGNED>), dim3((unsigned)(tiles_p * a.tiles_q)), dim3(NT), LDS_BYTES,
