@@ -75,6 +75,15 @@ def parse():
                     help="launch the headline kernels and a calibration copy for rocprofv3 --pmc, then exit")
     ap.add_argument("--counter-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two rocprofv3 --pmc CSV files, then exit")
+    ap.add_argument("--extras", default=None,
+                    help="comma-separated secondary workloads to run beside the headline (default: all; "
+                         "names as in the 'also' object)")
+    ap.add_argument("--trace-summary", nargs="+", metavar=("DB", "REGEX"),
+                    help="per-kernel table of a rocprofv3 --kernel-trace database (kernels whose name matches "
+                         "REGEX), then exit")
+    ap.add_argument("--pmc-table", nargs="+", metavar=("CSV", "REGEX"),
+                    help="per-kernel means of the counters in a rocprofv3 --pmc CSV file (kernels whose name "
+                         "matches REGEX), then exit")
     return ap.parse_args()
 
 
@@ -285,6 +294,61 @@ def _counter_rows(path, counter):
             if r["Counter_Name"] == counter:
                 rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
     return sorted(rows)
+
+
+def _short_kernel(name):
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "").replace("bl::", "")
+    depth = 0
+    for i, ch in enumerate(name):  # cut the argument list after the template arguments
+        depth += ch == "<"
+        depth -= ch == ">"
+        if ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def trace_summary(db, regex=None):
+    """Markdown table of per-kernel dispatch durations from a rocprofv3 kernel trace."""
+    import re
+    import sqlite3
+    pat = re.compile(regex) if regex else None
+    con = sqlite3.connect(db)
+    groups = {}
+    for name, gx, wx, dur, lds, vgpr in con.execute(
+            "select name, grid_x, workgroup_x, duration, lds_size, vgpr_count from kernels"):
+        if pat and not pat.search(name):
+            continue
+        key = (_short_kernel(name), gx // max(wx, 1), wx, lds, vgpr)
+        groups.setdefault(key, []).append(dur)
+    print("| kernel | workgroups x threads | LDS B | VGPRs | dispatches | mean us | median us | min us |")
+    print("|---|---|---|---|---|---|---|---|")
+    for key, v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        v = sorted(v)
+        print("| `%s` | %d x %d | %d | %d | %d | %.2f | %.2f | %.2f |"
+              % (key[0][:70], key[1], key[2], key[3], key[4], len(v), sum(v) / len(v) / 1e3, v[len(v) // 2] / 1e3,
+                 v[0] / 1e3))
+
+
+def pmc_table(path, regex=None):
+    """Markdown table of per-kernel counter means (one row per kernel and grid)."""
+    import re
+    pat = re.compile(regex) if regex else None
+    csv.field_size_limit(1 << 30)
+    groups, counters = {}, []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if pat and not pat.search(r["Kernel_Name"]):
+                continue
+            key = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]) // max(int(r["Workgroup_Size"]), 1))
+            c = r["Counter_Name"]
+            if c not in counters:
+                counters.append(c)
+            groups.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    print("| kernel | workgroups | " + " | ".join(counters) + " |")
+    print("|---|---|" + "---|" * len(counters))
+    for key, d in groups.items():
+        vals = ["%.4g" % (sum(d[c]) / len(d[c])) if c in d else "" for c in counters]
+        print("| `%s` | %d | %s |" % (key[0][:70], key[1], " | ".join(vals)))
 
 
 COUNTER_LAUNCHES = 16  # dispatches per headline shape in counters_run, in workload order
@@ -628,6 +692,12 @@ def main():
     if args.counter_summary:
         counter_summary(*args.counter_summary)
         return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary[:2])
+        return
+    if args.pmc_table:
+        pmc_table(*args.pmc_table[:2])
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on one GPU only (the path has no sharding or collectives); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -666,20 +736,30 @@ def main():
     }
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(host, wl)
-    if not args.quick:
-        result["also"] = {
-            "decode_step_2b_30l": decode_step(workloads.DECODE_STEP_BATCHES, dev),
-            "decode_100b": decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
-            "decode_b1_2b": decode_fmt_extra("b1", [(l.K, l.N) for l in workloads.DECODE_2B.linears], (1, 8), dev),
-            "decode_b1_100b": decode_fmt_extra("b1", workloads.SHAPES_100B, (1, 8), dev),
-            "decode_b3_2b": decode_fmt_extra("b3", [(l.K, l.N) for l in workloads.DECODE_2B.linears], (1, 8), dev),
-            "decode_b3_100b": decode_fmt_extra("b3", workloads.SHAPES_100B, (1, 8), dev),
-            "prefill_2b_m2048": prefill_extra(2048, ((2560, 6912), (6912, 2560)), dev),
-            "prefill_100b_m512": prefill_extra(512, workloads.SHAPES_100B, dev),
-            "prefill_b1_2b_m2048": prefill_b1_extra(2048, ((2560, 6912), (6912, 2560)), dev),
-            "prefill_b1_100b_m512": prefill_b1_extra(512, workloads.SHAPES_100B, dev),
-            "train_2b_m2048": train_extra(2048, ((2560, 6912), (6912, 2560)), dev),
-        }
+    shapes_2b = [(l.K, l.N) for l in workloads.DECODE_2B.linears]
+    extras = {
+        "decode_step_2b_30l": lambda: decode_step(workloads.DECODE_STEP_BATCHES, dev),
+        "decode_100b": lambda: decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
+        "decode_b1_2b": lambda: decode_fmt_extra("b1", shapes_2b, (1, 8), dev),
+        "decode_b1_100b": lambda: decode_fmt_extra("b1", workloads.SHAPES_100B, (1, 8), dev),
+        "decode_b3_2b": lambda: decode_fmt_extra("b3", shapes_2b, (1, 8), dev),
+        "decode_b3_100b": lambda: decode_fmt_extra("b3", workloads.SHAPES_100B, (1, 8), dev),
+        "prefill_2b_m2048": lambda: prefill_extra(2048, ((2560, 6912), (6912, 2560)), dev),
+        "prefill_100b_m512": lambda: prefill_extra(512, workloads.SHAPES_100B, dev),
+        "prefill_b1_2b_m2048": lambda: prefill_b1_extra(2048, ((2560, 6912), (6912, 2560)), dev),
+        "prefill_b1_100b_m512": lambda: prefill_b1_extra(512, workloads.SHAPES_100B, dev),
+        "train_2b_m2048": lambda: train_extra(2048, ((2560, 6912), (6912, 2560)), dev),
+    }
+    if args.extras is not None:
+        chosen = [e for e in args.extras.split(",") if e]
+        unknown = [e for e in chosen if e not in extras]
+        if unknown:
+            print("bench.py: unknown --extras %s (known: %s)" % (",".join(unknown), ",".join(extras)), file=sys.stderr)
+            sys.exit(2)
+    else:
+        chosen = [] if args.quick else list(extras)
+    if chosen:
+        result["also"] = {name: extras[name]() for name in chosen}
     print(json.dumps(result), flush=True)
 
 

@@ -46,9 +46,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int TP = 128, TQ = 128, TR = 64;  // block of C, stage of r
 constexpr int NT = 256;                     // threads per workgroup
 constexpr int PITCH = TR + 8;               // bf16 per [row][r] LDS row (144 bytes)
-// bf16 per [r][row] LDS row (288 bytes = 72 banks): the four rows a
-// transposing read touches start 8 banks apart, so they do not collide
-constexpr int PITCH_T = TP + 16;
+// bf16 per [r][row] LDS row: 320 bytes, 80 banks, i.e. 16 mod 64.  A
+// transposing read serves 32 lanes per LDS cycle: two groups of 16 lanes,
+// 8 banks apart, each reading 8 banks in each of 4 consecutive rows; with a
+// row stride of 16 banks (mod 64) the 2 x 4 pieces fill the 64 banks once.
+constexpr int PITCH_T = TP + 32;
 constexpr int OPND = TP * PITCH > TR * PITCH_T ? TP * PITCH : TR * PITCH_T;  // bf16 per operand tile
 constexpr int LDS_BYTES = 2 * 2 * OPND * 2;  // [buffer][A, B]
 constexpr int NP = TP * TR / 8 / NT;         // pieces per thread, operand and stage
