@@ -8,10 +8,13 @@
 //   weight    dw[N][K] = dy^T . x
 //
 // One bf16 matrix-core kernel computes C[P][Q] = scale * sum_r A(p, r) B(q, r)
-// for the three products; only the operand loaders differ.  A workgroup of
-// 4 waves (2 x 2) owns a 128 x 128 block of C, each wave 64 x 64 as 2 x 2
-// tiles of v_mfma_f32_32x32x16_bf16 (lane l holds A[l % 32][8 (l / 32) + j]
-// and B[8 (l / 32) + j][l % 32], j < 8).  r advances in stages of 64:
+// for the three products; only the operand loaders differ.  A workgroup owns
+// a T x T block of C: T = 256 with 8 waves (2 x 4, each 128 x 64) when the
+// grid still covers most compute units, else T = 128 with 4 waves (2 x 2,
+// each 64 x 64); waves compute 32 x 32 tiles with v_mfma_f32_32x32x16_bf16
+// (lane l holds A[l % 32][8 (l / 32) + j] and B[8 (l / 32) + j][l % 32],
+// j < 8).  The larger block halves the operand bytes per MFMA through L1 and
+// LDS writes.  r advances in stages of 64:
 //   * each thread moves 4 16-byte pieces of each operand per stage; they are
 //     requested two stages ahead into a register ring and written into the
 //     free half of double-buffered LDS tiles between the MFMAs of the stage
@@ -43,18 +46,27 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int TP = 128, TQ = 128, TR = 64;  // block of C, stage of r
-constexpr int NT = 256;                     // threads per workgroup
-constexpr int PITCH = TR + 8;               // bf16 per [row][r] LDS row (144 bytes)
-// bf16 per [r][row] LDS row: 320 bytes, 80 banks, i.e. 16 mod 64.  A
-// transposing read serves 32 lanes per LDS cycle: two groups of 16 lanes,
-// 8 banks apart, each reading 8 banks in each of 4 consecutive rows; with a
-// row stride of 16 banks (mod 64) the 2 x 4 pieces fill the 64 banks once.
-constexpr int PITCH_T = TP + 32;
-constexpr int OPND = TP * PITCH > TR * PITCH_T ? TP * PITCH : TR * PITCH_T;  // bf16 per operand tile
-constexpr int LDS_BYTES = 2 * 2 * OPND * 2;  // [buffer][A, B]
-constexpr int NP = TP * TR / 8 / NT;         // pieces per thread, operand and stage
-static_assert(NP == TR / 16, "one piece of each operand is stored per 16-wide MFMA step");
+template <bool BIG>
+struct TrainTile {
+  static constexpr int T = BIG ? 256 : 128;        // block of C is T x T
+  static constexpr int TR = BIG ? 32 : 64;         // stage of r (16 MFMAs per wave either way)
+  static constexpr int PITCH = TR + 8;             // bf16 per [row][r] LDS row
+  static constexpr int NT = BIG ? 512 : 256;       // threads per workgroup
+  static constexpr int WQN = NT / 128;             // waves along Q (2 along P)
+  static constexpr int WP = T / 2, WQ = T / WQN;   // per-wave block
+  static constexpr int MI = WP / 32, NJ = WQ / 32; // 32 x 32 tiles per wave
+  static constexpr int PPD = TR / 8;               // 16-byte pieces per [row][r] row
+  static constexpr int PPR = T / 8;                // 16-byte pieces per [r][row] row
+  // bf16 per [r][row] LDS row: T + 32, i.e. 16 banks mod 64.  A transposing
+  // read serves 32 lanes per LDS cycle: two groups of 16 lanes, 8 banks
+  // apart, each reading 8 banks in each of 4 consecutive rows; with a row
+  // stride of 16 banks (mod 64) the 2 x 4 pieces fill the 64 banks once.
+  static constexpr int PITCH_T = T + 32;
+  static constexpr int OPND = T * PITCH > TR * PITCH_T ? T * PITCH : TR * PITCH_T;  // bf16 per operand tile
+  static constexpr int LDS = 2 * 2 * OPND * 2;     // [buffer][A, B]
+  static constexpr int NP = T * TR / 8 / NT;       // pieces per thread, operand and stage
+  static_assert(NP == TR / 16, "one piece of each operand is stored per 16-wide MFMA step");
+};
 
 enum TrainMode { FWD = 0, DX = 1, DW = 2 };
 
@@ -125,11 +137,13 @@ __device__ inline u4 row_piece(const uint16_t* src, int ld, int rows, int cols, 
 
 // MFMA operand (8 bf16) of this lane from a [row][r] tile: rows row0 + l % 32,
 // r = r0 + 8 (l / 32) .. + 7.
+template <int PITCH>
 __device__ inline bf16x8 read_direct(const uint16_t* t, int row0, int r0, int lane) {
   return *reinterpret_cast<const bf16x8*>(t + (row0 + (lane & 31)) * PITCH + r0 + 8 * (lane >> 5));
 }
 
 // The same operand from an [r][row] tile with two transposing reads.
+template <int PITCH_T>
 __device__ inline bf16x8 read_transposed(const uint16_t* t, int row0, int r0, int lane) {
   const int grp = lane >> 4, i = lane & 15;
   const int col = row0 + 16 * (grp & 1) + 4 * (i & 3);
@@ -142,14 +156,17 @@ __device__ inline bf16x8 read_transposed(const uint16_t* t, int row0, int r0, in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int MODE, bool ALIGNED>
-__global__ __launch_bounds__(NT) void train_gemm_kernel(const TrainArgs a) {
+template <int MODE, bool ALIGNED, bool BIG>
+__global__ __launch_bounds__(TrainTile<BIG>::NT) void train_gemm_kernel(const TrainArgs a) {
+  using G = TrainTile<BIG>;
+  constexpr int T = G::T, NT = G::NT, NP = G::NP, OPND = G::OPND, PPR = G::PPR, MI = G::MI, NJ = G::NJ;
+  constexpr int TR = G::TR, PITCH = G::PITCH, PPD = G::PPD;
   // A (and B) is stored transposed, as [r][row], when its source rows run along r
   constexpr bool AT = MODE == DW, BT = MODE != FWD;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [buffer][A, B][OPND]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wp = wave >> 1, wq = wave & 1;
+  const int wp = wave / G::WQN, wq = wave % G::WQN;
   // the XCD's contiguous run of tiles, walked in groups of 4 row blocks of C
   // along Q (they share their A rows and B columns in that XCD's L2)
   constexpr int GM = 4;
@@ -158,49 +175,51 @@ __global__ __launch_bounds__(NT) void train_gemm_kernel(const TrainArgs a) {
   const int group = tile / (GM * a.tiles_q), within = tile - group * GM * a.tiles_q;
   const int gm = min(GM, tiles_p - group * GM);
   const int tp = group * GM + within % gm, tq = within / gm;
-  const int p0 = tp * TP, q0 = tq * TQ;
+  const int p0 = tp * T, q0 = tq * T;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // Pieces of a source row-major along r: piece c -> row c / 8, r 8 (c % 8).
-  // Pieces of a source whose rows run along r: piece c -> r c / 16, row
-  // (P or Q index) 8 (c % 16).
+  // Pieces of a source row-major along r: piece c -> row c / PPD, r 8 (c % PPD).
+  // Pieces of a source whose rows run along r: piece c -> r c / PPR, row
+  // (P or Q index) 8 (c % PPR).
   auto load = [&](u4 (&pa)[NP], u4 (&pb)[NP], int r0) {
 #pragma unroll
     for (int h = 0; h < NP; ++h) {
       const int c = h * NT + tid;
       if constexpr (MODE == DW) {
-        pa[h] = row_piece<ALIGNED>(a.a, a.lda, a.R, a.P, r0 + (c >> 4), p0 + 8 * (c & 15));  // dy[m][n], n along P
-        pb[h] = row_piece<ALIGNED>(a.b, a.ldb, a.R, a.Q, r0 + (c >> 4), q0 + 8 * (c & 15));  // x[m][k], k along Q
+        pa[h] = row_piece<ALIGNED>(a.a, a.lda, a.R, a.P, r0 + c / PPR, p0 + 8 * (c % PPR));  // dy[m][n], n along P
+        pb[h] = row_piece<ALIGNED>(a.b, a.ldb, a.R, a.Q, r0 + c / PPR, q0 + 8 * (c % PPR));  // x[m][k], k along Q
       } else {
-        pa[h] = row_piece<ALIGNED>(a.a, a.lda, a.P, a.R, p0 + (c >> 3), r0 + 8 * (c & 7));   // x or dy rows
+        pa[h] = row_piece<ALIGNED>(a.a, a.lda, a.P, a.R, p0 + c / PPD, r0 + 8 * (c % PPD));   // x or dy rows
         if constexpr (MODE == FWD)
-          pb[h] = t2_piece(a, q0 + (c >> 3), r0 + 8 * (c & 7));                              // t[n][k], k along r
+          pb[h] = t2_piece(a, q0 + c / PPD, r0 + 8 * (c % PPD));                              // t[n][k], k along r
         else
-          pb[h] = t2_piece(a, r0 + (c >> 4), q0 + 8 * (c & 15));                             // t[n][k], n along r
+          pb[h] = t2_piece(a, r0 + c / PPR, q0 + 8 * (c % PPR));                             // t[n][k], n along r
       }
     }
   };
   // LDS slot of piece c: the same pieces the loaders fetch
-  auto slot = [](bool tr, int c) { return tr ? (c >> 4) * PITCH_T + 8 * (c & 15) : (c >> 3) * PITCH + 8 * (c & 7); };
+  auto slot = [](bool tr, int c) { return tr ? (c / PPR) * G::PITCH_T + 8 * (c % PPR) : (c / PPD) * PITCH + 8 * (c % PPD); };
   auto store_piece = [&](int buf, const u4 (&pa)[NP], const u4 (&pb)[NP], int h) {
     const int c = h * NT + tid;
     *reinterpret_cast<u4*>(lds + (2 * buf) * OPND + slot(AT, c)) = pa[h];
     *reinterpret_cast<u4*>(lds + (2 * buf + 1) * OPND + slot(BT, c)) = pb[h];
   };
-  auto read_ops = [&](bf16x8 (&av)[2], bf16x8 (&bv)[2], const uint16_t* A, const uint16_t* B, int ks) {
+  auto read_ops = [&](bf16x8 (&av)[MI], bf16x8 (&bv)[NJ], const uint16_t* A, const uint16_t* B, int ks) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      av[i] = AT ? read_transposed(A, wp * 64 + 32 * i, 16 * ks, lane) : read_direct(A, wp * 64 + 32 * i, 16 * ks, lane);
+    for (int i = 0; i < MI; ++i)
+      av[i] = AT ? read_transposed<G::PITCH_T>(A, wp * G::WP + 32 * i, 16 * ks, lane)
+                 : read_direct<PITCH>(A, wp * G::WP + 32 * i, 16 * ks, lane);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      bv[j] = BT ? read_transposed(B, wq * 64 + 32 * j, 16 * ks, lane) : read_direct(B, wq * 64 + 32 * j, 16 * ks, lane);
+    for (int j = 0; j < NJ; ++j)
+      bv[j] = BT ? read_transposed<G::PITCH_T>(B, wq * G::WQ + 32 * j, 16 * ks, lane)
+                 : read_direct<PITCH>(B, wq * G::WQ + 32 * j, 16 * ks, lane);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -209,17 +228,21 @@ __global__ __launch_bounds__(NT) void train_gemm_kernel(const TrainArgs a) {
   auto compute = [&](int buf, const u4 (&na)[NP], const u4 (&nb)[NP]) {
     const uint16_t* A = lds + (2 * buf) * OPND;
     const uint16_t* B = lds + (2 * buf + 1) * OPND;
-    bf16x8 av[2][2], bv[2][2];
+    // the small block reads the next step's operands during the current
+    // step's MFMAs; the large one has no registers to spare for that
+    constexpr int OB = BIG ? 1 : 2;
+    bf16x8 av[OB][MI], bv[OB][NJ];
     read_ops(av[0], bv[0], A, B, 0);
 #pragma unroll
     for (int ks = 0; ks < TR / 16; ++ks) {
-      const int cur = ks & 1;
-      if (ks + 1 < TR / 16) read_ops(av[cur ^ 1], bv[cur ^ 1], A, B, ks + 1);
+      const int cur = OB == 2 ? (ks & 1) : 0;
+      if (OB == 2 && ks + 1 < TR / 16) read_ops(av[(ks + 1) % OB], bv[(ks + 1) % OB], A, B, ks + 1);
+      if (OB == 1 && ks > 0) read_ops(av[0], bv[0], A, B, ks);
       store_piece(buf ^ 1, na, nb, ks);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][j], acc[i][j], 0, 0, 0);
     }
   };
@@ -247,34 +270,46 @@ __global__ __launch_bounds__(NT) void train_gemm_kernel(const TrainArgs a) {
 
   const float scale = MODE == DW ? 1.0f : *a.beta;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int p = p0 + wp * 64 + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
+      const int p = p0 + wp * G::WP + 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);
       if (p >= a.P) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int q = q0 + wq * 64 + 32 * j + l32;
+      for (int j = 0; j < NJ; ++j) {
+        const int q = q0 + wq * G::WQ + 32 * j + l32;
         if (q < a.Q) a.c[(int64_t)p * a.Q + q] = __fmul_rn(acc[i][j][e], scale);
       }
     }
 }
 
-template <int MODE, bool ALIGNED>
-hipError_t launch_aligned(const TrainArgs& a, hipStream_t s) {
+template <int MODE, bool ALIGNED, bool BIG>
+hipError_t launch_tile(TrainArgs a, hipStream_t s) {
+  using G = TrainTile<BIG>;
   static LdsLimit lim;
-  const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&train_gemm_kernel<MODE, ALIGNED>),
-                                           LDS_BYTES);
+  const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&train_gemm_kernel<MODE, ALIGNED, BIG>),
+                                           G::LDS);
   if (attr != hipSuccess) return attr;
-  const int tiles_p = (a.P + TP - 1) / TP;
-  hipLaunchKernelGGL((train_gemm_kernel<MODE, ALIGNED>), dim3((unsigned)(tiles_p * a.tiles_q)), dim3(NT), LDS_BYTES,
-                     s, a);
+  a.tiles_q = (a.Q + G::T - 1) / G::T;
+  const int tiles_p = (a.P + G::T - 1) / G::T;
+  hipLaunchKernelGGL((train_gemm_kernel<MODE, ALIGNED, BIG>), dim3((unsigned)(tiles_p * a.tiles_q)), dim3(G::NT),
+                     G::LDS, s, a);
   return hipGetLastError();
 }
 
+// Block size for aligned operands, from rounds over the 256 compute units:
+// one 256 x 256 block per unit and round, or two 128 x 128 blocks per unit
+// and round; a 256-block does the work of four 128-blocks about 1.25 times
+// as efficiently (measured), so it wins when 4 / 1.25 * rounds(256) < 2 *
+// rounds(128).  Unaligned operands take the 128 x 128 kernel.
+constexpr int64_t kCUs = 256;
 template <int MODE>
 hipError_t launch(const TrainArgs& a, bool aligned, hipStream_t s) {
-  return aligned ? launch_aligned<MODE, true>(a, s) : launch_aligned<MODE, false>(a, s);
+  if (!aligned) return launch_tile<MODE, false, false>(a, s);
+  const int64_t r256 = ceil_div(ceil_div(a.P, 256) * ceil_div(a.Q, 256), kCUs);
+  const int64_t r128 = ceil_div(ceil_div(a.P, 128) * ceil_div(a.Q, 128), 2 * kCUs);
+  if (16 * r256 < 10 * r128) return launch_tile<MODE, true, true>(a, s);
+  return launch_tile<MODE, true, false>(a, s);
 }
 
 // bf16 rows of `len` values starting at p are whole, aligned 16-byte pieces
@@ -292,7 +327,6 @@ hipError_t launch_train_forward(const uint16_t* x, int64_t M, int64_t K, const u
   a.P = (int)M, a.Q = (int)N, a.R = (int)K;
   a.lda = (int)K;
   a.Kt = (int)ceil_div(K, kTileK), a.N = (int)N;
-  a.tiles_q = (int)ceil_div(N, TQ);
   return launch<FWD>(a, pieces(x, K), s);
 }
 
@@ -306,7 +340,6 @@ hipError_t launch_train_dx(const uint16_t* dy, int64_t M, int64_t N, const uint8
   a.P = (int)M, a.Q = (int)K, a.R = (int)N;
   a.lda = (int)N;
   a.Kt = (int)ceil_div(K, kTileK), a.N = (int)N;
-  a.tiles_q = (int)ceil_div(K, TQ);
   return launch<DX>(a, pieces(dy, N), s);
 }
 
@@ -318,7 +351,6 @@ hipError_t launch_train_dw(const uint16_t* dy, const uint16_t* x, int64_t M, int
   a.c = dw;
   a.P = (int)N, a.Q = (int)K, a.R = (int)M;
   a.lda = (int)N, a.ldb = (int)K;
-  a.tiles_q = (int)ceil_div(K, TQ);
   return launch<DW>(a, pieces(dy, N) && pieces(x, K), s);
 }
 

@@ -83,3 +83,44 @@ def test_train_exact_small_integers():
     np.testing.assert_array_equal(y.cpu().numpy(), oracle.train_forward(bf16_bits(xd), t, b))
     np.testing.assert_array_equal(dx.cpu().numpy(), oracle.train_dx(bf16_bits(dyd), t, b))
     np.testing.assert_array_equal(dw.cpu().numpy(), oracle.train_dw(bf16_bits(dyd), bf16_bits(xd)))
+
+
+@pytest.mark.parametrize("product,M,K,N", [("forward", 2048, 512, 6144), ("input", 2048, 6144, 512),
+                                           ("weight", 512, 6144, 2048)])
+def test_train_products_large_blocks(product, M, K, N):
+    """Grids of at least 192 blocks of 256 x 256 outputs take the 8-wave kernel
+    with 32-wide stages; the oracle checks 64 sampled output rows (the first and
+    last 8 and 48 drawn ones), every column."""
+    rng = np.random.default_rng({"forward": 1, "input": 2, "weight": 3}[product])
+    w = workloads.gen_weights(N, K, seed=K + N + 1)
+    x = torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    dy = torch.from_numpy(rng.standard_normal((M, N)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    packed, beta = bl.pack_weights(torch.from_numpy(w).to(DEV))
+    b = oracle.absmean(w)
+    t = oracle.ternarize(w, b)
+    xb, dyb = bf16_bits(x), bf16_bits(dy)
+    P = N if product == "weight" else M
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(P - 8, P), rng.choice(P, 48, replace=False)]))
+    ta = np.abs(t).astype(np.float64)
+    if product == "forward":
+        out = torch.full((M, N), 7.0, device=DEV)
+        bl.bitlinear_train_forward(x, packed, beta, N, out)
+        ref = oracle.train_forward(xb[rows], t, b, threads=8)
+        terms = float(b) * (np.abs(workloads.bf16_bits_to_f32(xb[rows]).astype(np.float64)) @ ta.T)
+        L = K
+    elif product == "input":
+        out = torch.full((M, K), 7.0, device=DEV)
+        bl.bitlinear_train_backward_input(dy, packed, beta, K, out)
+        ref = oracle.train_dx(dyb[rows], t, b, threads=8)
+        terms = float(b) * (np.abs(workloads.bf16_bits_to_f32(dyb[rows]).astype(np.float64)) @ ta)
+        L = N
+    else:
+        out = torch.full((N, K), 7.0, device=DEV)
+        bl.bitlinear_train_backward_weight(dy, x, out)
+        dys = np.ascontiguousarray(dyb[:, rows])
+        ref = oracle.train_dw(dys, xb, threads=8)
+        terms = (np.abs(workloads.bf16_bits_to_f32(dys).astype(np.float64)).T
+                 @ np.abs(workloads.bf16_bits_to_f32(xb).astype(np.float64)))
+        L = M
+    torch.cuda.synchronize()
+    check(out.cpu().numpy()[rows], ref, terms, L)
