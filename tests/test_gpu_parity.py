@@ -240,8 +240,9 @@ def test_gemv_large_batches(M, N, K):
 
 def test_gemv_split_k_workspace_left_zero():
     # a long K with few outputs makes the plan split K across workgroups
-    M, N, K = 3, 48, 40000
+    M, N, K = 3, 48, 70000
     need = bl.gemv_workspace_bytes(M, N, K)
+    assert need > 0
     w = workloads.gen_weights(N, K, seed=5)
     xb = workloads.gen_acts_bf16(M, K, seed=6)
     ref = oracle.bitlinear_forward(xb, w, threads=8)
@@ -251,6 +252,30 @@ def test_gemv_split_k_workspace_left_zero():
         ws = bl.workspace(need, DEV)
         torch.cuda.synchronize()
         assert not ws[:need].any().item()
+
+
+def test_workspace_shared_by_split_products():
+    """One workspace serves the GEMV split across workgroups (needs zeros on
+    entry) and the small-batch GEMM split (fills and re-zeroes its slices),
+    alternately; every result stays exact and the buffer ends zero."""
+    cases = [(3, 48, 70000), (32, 640, 6912)]  # (M, N, K): GEMV split-K, GEMM split
+    need = max(max(bl.gemv_workspace_bytes(*c), bl.gemm_workspace_bytes(*c)) for c in cases)
+    assert bl.gemv_workspace_bytes(*cases[0]) > 0 and bl.gemm_workspace_bytes(*cases[1]) > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    data = []
+    for i, (M, N, K) in enumerate(cases):
+        w = workloads.gen_weights(N, K, seed=60 + i)
+        xb = workloads.gen_acts_bf16(M, K, seed=70 + i)
+        packed, beta = gpu_pack(w)
+        x_q, x_ds = bl.quant_act(to_dev_bf16(xb))
+        data.append((x_q, x_ds, K, packed, beta, N, oracle.bitlinear_forward(xb, w, threads=8)["acc"]))
+    for _ in range(3):
+        for fn, (x_q, x_ds, K, packed, beta, N, acc) in zip((bl.bitlinear_gemv, bl.bitlinear_gemm), data):
+            y = torch.empty((x_q.shape[0], N), dtype=torch.int32, device=DEV)
+            fn(x_q, x_ds, K, packed, beta, N, y, ws)
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(y.cpu().numpy(), acc)
+    assert not ws.any().item()
 
 
 def test_max_magnitude_accumulators():
