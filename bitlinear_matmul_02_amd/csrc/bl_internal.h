@@ -171,4 +171,22 @@ __device__ inline void store_out(void* y, int y_dtype, int64_t idx, int acc64, f
   }
 }
 
+// store_out with the output type fixed at compile time (epilogues that
+// dispatch on the type once, outside their loops).
+template <int YD>
+__device__ inline void store_out_t(void* y, int64_t idx, int acc64, float scale) {
+  const int acc = acc64 >> 6;  // exact: every term is a multiple of 64
+  if constexpr (YD == BITLINEAR_I32) {
+    static_cast<int32_t*>(y)[idx] = acc;
+  } else {
+    const float v = (float)acc * scale;
+    if constexpr (YD == BITLINEAR_F32)
+      static_cast<float*>(y)[idx] = v;
+    else if constexpr (YD == BITLINEAR_F32_ADD)
+      static_cast<float*>(y)[idx] = __fadd_rn(static_cast<const float*>(y)[idx], v);
+    else
+      static_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
+  }
+}
+
 }  // namespace bl

@@ -269,23 +269,53 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
       }
     return;
   }
+  // The per-row scales of the block go through LDS (the slabs are free: the
+  // last k-step ended with a barrier), loaded once before any output store:
+  // a global load between the stores would wait for every store issued
+  // before it (vmcnt retires in order).
+  float* s_ds = reinterpret_cast<float*>(lds);
+  int* s_rs = reinterpret_cast<int*>(lds + BM * 4);
   const float bt = *beta;
+  if (tid < BM) {
+    s_ds[tid] = ds[min(m0 + tid, M - 1)];
+    if constexpr (FMT != 0) s_rs[tid] = rowsum[min(m0 + tid, M - 1)];
+  }
+  __syncthreads();
+  // this lane's row scales, all read before the first store
+  float scale[MB][16];
+  int rsv[MB][16];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int m = m0 + wm * G::WM + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
-      if (m >= M) continue;
-      const float scale = ds[m] * bt;
-      const int rs = FMT ? rowsum[m] : 0;
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = n_wave + 32 * j + r32;
-        // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum, scaled like the T2 sums (64 t)
-        const int v = FMT ? (2 * acc[mb][j][e] - rs) * 64 : acc[mb][j][e];
-        if (n < N) store_out(y, y_dtype, (int64_t)m * N + n, v, scale);
-      }
+      const int r = wm * G::WM + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+      scale[mb][e] = s_ds[r] * bt;
+      rsv[mb][e] = FMT ? s_rs[r] : 0;
     }
+  // the output type is dispatched once, outside the store loops
+  auto emit = [&](auto ytype) {
+    constexpr int YD = decltype(ytype)::value;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wm * G::WM + mb * 32 + 8 * (e >> 2) + 4 * g2 + (e & 3);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int n = n_wave + 32 * j + r32;
+          // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum, scaled like the T2 sums (64 t)
+          const int v = FMT ? (2 * acc[mb][j][e] - rsv[mb][e]) * 64 : acc[mb][j][e];
+          if (n < N) store_out_t<YD>(y, (int64_t)m * N + n, v, scale[mb][e]);
+        }
+      }
+  };
+  switch (y_dtype) {
+    case BITLINEAR_I32: emit(std::integral_constant<int, BITLINEAR_I32>{}); break;
+    case BITLINEAR_F32: emit(std::integral_constant<int, BITLINEAR_F32>{}); break;
+    case BITLINEAR_F32_ADD: emit(std::integral_constant<int, BITLINEAR_F32_ADD>{}); break;
+    default: emit(std::integral_constant<int, BITLINEAR_BF16>{}); break;
+  }
 }
 
 // Sum of the S workspace slices and the dequantization of the unsplit
