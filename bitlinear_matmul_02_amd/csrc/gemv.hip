@@ -63,6 +63,8 @@
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
 // workspace again.
+#include <type_traits>
+
 #include "bl_internal.h"
 
 namespace bl {
@@ -793,25 +795,67 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     return;
   }
   const float bt = *sg.beta;
+  if constexpr (FUSED) {
+    // the row scales are in LDS: no global load between the stores
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mb * 16 + 4 * g4 + r;
-      if (m >= M) continue;
-      const float dsm = FUSED ? row_g[m] / 127.0f : a.ds[m];  // g of the normalized row with a.norm
-      const float scale = dsm * bt;
-      const int rs = FMT ? a.rowsum[m] : 0;
+      for (int r = 0; r < 4; ++r) {
+        const int m = mb * 16 + 4 * g4 + r;
+        if (m >= M) continue;
+        const float scale = (row_g[m] / 127.0f) * bt;  // g of the normalized row with a.norm
+        const int rs = FMT ? a.rowsum[m] : 0;
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = (nb0 + j) * kTileN + r16;
-        // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum; B3: sum q * (c - 1) =
-        // sum q * c - rowsum; both scaled as the T2 sums (64 t)
-        const int v = FMT == 1 ? (2 * acc[mb][j][r] - rs) * 64
-                               : (FMT == 2 ? (acc[mb][j][r] - rs) * 64 : acc[mb][j][r]);
-        if (n < sg.N) store_out(sg.y, a.y_dtype, (int64_t)m * sg.N + n, v, scale);
+        for (int j = 0; j < NB; ++j) {
+          const int n = (nb0 + j) * kTileN + r16;
+          const int v = FMT == 1 ? (2 * acc[mb][j][r] - rs) * 64
+                                 : (FMT == 2 ? (acc[mb][j][r] - rs) * 64 : acc[mb][j][r]);
+          if (n < sg.N) store_out(sg.y, a.y_dtype, (int64_t)m * sg.N + n, v, scale);
+        }
       }
+  } else {
+    // Every row scale is read before the first store (a global load between
+    // stores would wait for all of them: vmcnt retires in order), and the
+    // output type is dispatched once, outside the store loops.
+    float scale[MB][4];
+    int rsv[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = mb * 16 + 4 * g4 + r;
+        scale[mb][r] = 0.0f, rsv[mb][r] = 0;
+        if (m < M) {
+          scale[mb][r] = a.ds[m] * bt;
+          rsv[mb][r] = FMT ? a.rowsum[m] : 0;
+        }
+      }
+    auto emit = [&](auto ytype) {
+      constexpr int YD = decltype(ytype)::value;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mb * 16 + 4 * g4 + r;
+          if (m >= M) continue;
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int n = (nb0 + j) * kTileN + r16;
+            // B1: sum q * (2 b - 1) = 2 sum q * b - rowsum; B3: sum q * (c - 1) =
+            // sum q * c - rowsum; both scaled as the T2 sums (64 t)
+            const int v = FMT == 1 ? (2 * acc[mb][j][r] - rsv[mb][r]) * 64
+                                   : (FMT == 2 ? (acc[mb][j][r] - rsv[mb][r]) * 64 : acc[mb][j][r]);
+            if (n < sg.N) store_out_t<YD>(sg.y, (int64_t)m * sg.N + n, v, scale[mb][r]);
+          }
+        }
+    };
+    switch (a.y_dtype) {
+      case BITLINEAR_I32: emit(std::integral_constant<int, BITLINEAR_I32>{}); break;
+      case BITLINEAR_F32: emit(std::integral_constant<int, BITLINEAR_F32>{}); break;
+      case BITLINEAR_F32_ADD: emit(std::integral_constant<int, BITLINEAR_F32_ADD>{}); break;
+      default: emit(std::integral_constant<int, BITLINEAR_BF16>{}); break;
     }
+  }
 }
 
 template <int MB, int NB, int AM, bool NORM, int FMT = 0>
