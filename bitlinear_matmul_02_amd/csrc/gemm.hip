@@ -60,7 +60,8 @@ namespace {
 
 template <int BM, int BN, int FMT = 0>
 struct GemmTile {
-  static constexpr int WGM = 2, WGN = 4;              // waves along M x along N
+  static constexpr int WGM = BM >= 64 ? 2 : 1;         // waves along M
+  static constexpr int WGN = 8 / WGM;                  // waves along N
   static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave block
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA tiles per wave
@@ -368,14 +369,28 @@ hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, const int3
 // multiples of the block count up to one workgroup per unit, each split
 // keeping at least 4 k-steps).  Returns the number of splits; every split is
 // non-empty.
-constexpr int kMidM = 64, kMidN = 128, kMidGrid = 256, kMidMinSteps = 4;
-int mid_splits(int64_t M, int64_t N, int64_t K) {
-  const int64_t tiles = ceil_div(M, kMidM) * ceil_div(N, kMidN), Kt = ceil_div(K, kTileK);
+constexpr int kMidM = 64, kMidN = 128, kSmallM = 32, kSmallN = 256, kMidGrid = 256, kMidMinSteps = 4;
+int mid_splits(int64_t M, int64_t N, int64_t K, int bm, int bn) {
+  const int64_t tiles = ceil_div(M, bm) * ceil_div(N, bn), Kt = ceil_div(K, kTileK);
   int64_t S = kMidGrid / tiles;
   if (S > Kt / kMidMinSteps) S = Kt / kMidMinSteps;
   if (S < 2) return 1;
   const int64_t per = ceil_div(Kt, S);
   return (int)ceil_div(Kt, per);
+}
+int mid_splits(int64_t M, int64_t N, int64_t K) {
+  return M <= kSmallM ? mid_splits(M, N, K, kSmallM, kSmallN) : mid_splits(M, N, K, kMidM, kMidN);
+}
+
+template <int BM, int BN, int FMT>
+hipError_t launch_mid(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
+                      const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
+                      void* ws) {
+  const int S = mid_splits(M, N, K, BM, BN);
+  if (S > 1)
+    return launch_tile<BM, BN, 3, FMT, true>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, S,
+                                             static_cast<int32_t*>(ws));
+  return launch_tile<BM, BN, 3, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s);
 }
 
 template <int FMT>
@@ -383,13 +398,9 @@ hipError_t launch_fmt(const int8_t* q, int64_t ldq, const float* ds, const int32
                       const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
                       void* ws = nullptr) {
   if constexpr (FMT == 0) {
-    if (M <= kMidM) {
-      const int S = mid_splits(M, N, K);
-      if (S > 1)
-        return launch_tile<kMidM, kMidN, 2, FMT, true>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, S,
-                                                        static_cast<int32_t*>(ws));
-      return launch_tile<kMidM, kMidN, 2, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s);
-    }
+    if (M <= kSmallM)
+      return launch_mid<kSmallM, kSmallN, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, ws);
+    if (M <= kMidM) return launch_mid<kMidM, kMidN, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, ws);
   }
   // 128 x 256 blocks when that still gives a few hundred workgroups,
   // 128 x 128 otherwise

@@ -1011,13 +1011,13 @@ hipError_t launch_gemv_b3(const int8_t* q, int64_t ldq, const float* ds, const i
   return dispatch_mb_nb<AGLOBAL, false, 2>(p, a, s);
 }
 
-// Token counts for which the 64-row matrix-core path of the prefill product
-// (bitlinear_gemm's, bit-identical results) beats this kernel: from 49
-// tokens; from 33 on matrices of 2^24 weights or more; from 24 on 2^27 or
-// more (measured on the 2B- and 100B-class shapes).
+// Token counts for which the small-batch matrix-core path of the prefill
+// product (bitlinear_gemm's 32- and 64-row blocks, bit-identical results)
+// beats this kernel: from 49 tokens; from 33 on matrices of 2^24 weights or
+// more; from 12 on 2^27 or more (measured on the 2B- and 100B-class shapes).
 bool gemv_prefers_gemm(int64_t M, int64_t N, int64_t K) {
   const int64_t w = N * K;
-  return M > 48 || (M > 32 && w >= (int64_t(1) << 24)) || (M >= 24 && w >= (int64_t(1) << 27));
+  return M > 48 || (M > 32 && w >= (int64_t(1) << 24)) || (M >= 12 && w >= (int64_t(1) << 27));
 }
 
 int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {

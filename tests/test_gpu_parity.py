@@ -210,11 +210,13 @@ def test_gemm_parity(M, N, K):
 # ----------------------------------- up to 64 tokens on the int8 matrix cores
 @pytest.mark.parametrize("M,N,K,split", [(1, 1000, 4096, True), (37, 333, 6925, True), (64, 6912, 2560, True),
                                          (24, 130, 2048, True), (17, 2560, 6912, True), (64, 64, 512, False),
-                                         (64, 28672, 1024, False)])
+                                         (64, 28672, 1024, False), (32, 8192, 28672, True), (33, 8192, 4096, True),
+                                         (32, 65536, 512, False), (9, 300, 700, False)])
 def test_gemm_small_batch_parity(M, N, K, split):
-    """64-row blocks; with few blocks the k-steps are split across workgroups
-    (int32 partial sums in the workspace, added and dequantized by a second
-    kernel, which zeroes them again)."""
+    """32-row blocks up to 32 tokens, 64-row blocks up to 64; with few blocks
+    the k-steps are split across workgroups (int32 partial sums in the
+    workspace, added and dequantized by a second kernel, which zeroes them
+    again)."""
     need = bl.gemm_workspace_bytes(M, N, K)
     assert (need > 0) == split
     w = workloads.gen_weights(N, K, seed=7000 + N)
@@ -228,11 +230,12 @@ def test_gemm_small_batch_parity(M, N, K, split):
         assert not ws[:need].any().item()
 
 
-@pytest.mark.parametrize("M,N,K", [(24, 16384, 8192), (33, 4096, 4096), (49, 300, 1000), (32, 2560, 2560),
-                                   (23, 16384, 8192)])
+@pytest.mark.parametrize("M,N,K", [(12, 16384, 8192), (24, 16384, 8192), (33, 4096, 4096), (49, 300, 1000),
+                                   (32, 2560, 2560), (11, 16384, 8192)])
 def test_gemv_large_batches(M, N, K):
-    """bitlinear_gemv hands larger batches to the 64-row matrix-core path (from
-    24 tokens on 2^27 weights, 33 on 2^24, 49 on any); results are the same."""
+    """bitlinear_gemv hands larger batches to the small-batch matrix-core path
+    (from 12 tokens on 2^27 weights, 33 on 2^24, 49 on any); results are the
+    same."""
     w = workloads.gen_weights(N, K, seed=9000 + N)
     xb = workloads.gen_acts_bf16(M, K, seed=9500 + M)
     check_product(xb, w, use_gemm=False, dtypes=("i32", "f32"))
