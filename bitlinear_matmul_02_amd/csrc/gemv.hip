@@ -75,6 +75,9 @@ constexpr float kEpsX = 1e-5f;
 // weight prefetch and holds in registers until the weight loads are in flight.
 constexpr int kXReg = 8;
 constexpr int kLdsPad = 16;  // bytes added to each LDS activation row
+// Residency of the LDS-staged plans: compute units, LDS per unit, and a bound
+// on the kernel's static LDS (reduction buffer and row scales).
+constexpr int64_t kResidentCUs = 256, kLdsPerCU = 160 * 1024, kGemvStaticLds = 4608;
 enum AMode { AGLOBAL = 0, ALDS_Q = 1, ALDS_X = 2, ALDS_XS = 3 };
 
 // k-tiles in flight per wave, chosen to keep the prefetch ring within the
@@ -130,6 +133,15 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   const int nb_cap = p.amode == AGLOBAL ? (p.MB > 2 ? 2 : 4) : (p.MB >= 3 ? 1 : 4 / p.MB);
   if (p.NB > nb_cap) p.NB = nb_cap;
   p.Ng = (int)ceil_div(p.Nt, p.NB);
+  if (p.amode == ALDS_Q && p.Ng > kResidentCUs * (kLdsPerCU / (lds + kGemvStaticLds))) {
+    // the staged rows would leave too few workgroups resident for one
+    // round: read the operands from global memory instead (measured:
+    // 6 x 8192 -> 28672 in 16.4 us against 21.2 us)
+    p.amode = AGLOBAL;
+    p.lds_bytes = 0;
+    p.NB = p.NB > (p.MB > 2 ? 2 : 4) ? (p.MB > 2 ? 2 : 4) : p.NB;
+    p.Ng = (int)ceil_div(p.Nt, p.NB);
+  }
   const int maxw = max_waves(p.MB);
   // one token block with operands from global memory, many output groups and
   // 32 or more k-tiles (e.g. 8 tokens, K = 8192 at 2 bits): one wave streams
