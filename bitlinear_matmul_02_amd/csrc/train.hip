@@ -50,13 +50,7 @@ template <bool BIG>
 struct TrainTile {
   static constexpr int T = BIG ? 256 : 128;        // block of C is T x T
   static constexpr int TR = BIG ? 32 : 64;         // stage of r (16 MFMAs per wave either way)
-  // bf16 per [row][r] LDS row.  A 16-byte LDS read or write serves 8 lanes
-  // per cycle, lanes 4k..4k+3 with 32+4k..32+4k+3: the operand reads take
-  // 4 rows at two 16-byte offsets, the piece stores 8 rows apart.  TR + 8
-  // (36 banks) keeps both on distinct banks for TR = 64; for TR = 32 it
-  // takes TR + 24 (28 banks): TR + 8 (20 banks) puts a read's fourth row on
-  // its first row's banks, TR + 16 (24 banks) a store's two rows.
-  static constexpr int PITCH = BIG ? TR + 24 : TR + 8;
+  static constexpr int PITCH = TR + 8;             // bf16 per [row][r] LDS row
   static constexpr int NT = BIG ? 512 : 256;       // threads per workgroup
   static constexpr int WQN = NT / 128;             // waves along Q (2 along P)
   static constexpr int WP = T / 2, WQ = T / WQN;   // per-wave block
