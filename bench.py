@@ -36,7 +36,9 @@ Also printed on the same JSON line:
                 (b3) decode on the 2B and 100B shapes (M = 1, 8); prefill GEMMs (2B M=2048,
                 100B M=512), ternary and binary, in int8 TOPS; the training
                 products (straight-through forward, input and weight
-                gradients, 2B shapes, 2048 tokens) in bf16 TFLOP/s.
+                gradients, 2B shapes, 2048 tokens) in bf16 TFLOP/s;
+  clocks        the shader and memory clock levels the driver reported while
+                the timed graphs ran (min / median / max of 1 ms samples).
 """
 from __future__ import annotations
 
@@ -174,15 +176,75 @@ def capture_steps(linears, nsteps):
     return capture(one, nsteps)
 
 
+class ClockSampler:
+    """The GPU's current shader (sclk) and memory (mclk) clock levels, read
+    from the driver's pp_dpm_* files by a background thread every `period`
+    seconds, kept only while a timed graph replay is in flight."""
+
+    def __init__(self, period=0.001):
+        import glob
+        import threading
+        self.files = {}
+        for key in ("sclk", "mclk"):
+            found = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_" + key))
+            if found:
+                self.files[key] = found[0]
+        self.samples = {k: [] for k in self.files}
+        self.busy = False
+        self.period = period
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True) if self.files else None
+        if self._thread:
+            self._thread.start()
+
+    @staticmethod
+    def _current(path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":")[1].strip().split("Mhz")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.wait(self.period):
+            if not self.busy:
+                continue
+            for k, path in self.files.items():
+                v = self._current(path)
+                if v is not None and self.busy:
+                    self.samples[k].append(v)
+
+    def summary(self):
+        self._stop.set()
+        out = {}
+        for k, v in self.samples.items():
+            if v:
+                out[k + "_mhz"] = {"min": min(v), "median": float(np.median(v)), "max": max(v), "samples": len(v)}
+        if not out:
+            return None
+        out["source"] = "current pp_dpm_sclk / pp_dpm_mclk level, polled every 1 ms during the timed graph replays"
+        return out
+
+
+CLOCKS = None
+
+
 def time_graph(g, reps=1):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if CLOCKS:
+        CLOCKS.busy = True
     a.record()
     for _ in range(reps):
         g.replay()
     b.record()
     torch.cuda.synchronize()
+    if CLOCKS:
+        CLOCKS.busy = False
     return a.elapsed_time(b) / 1e3, time.perf_counter() - t0
 
 
@@ -712,6 +774,8 @@ def main():
         counters_run(dev)
         return
 
+    global CLOCKS
+    CLOCKS = ClockSampler()
     head, host, wl = headline(args, dev)
     result = {
         "metric": "ternary GEMV HBM GB/s + decode tok/s; prefill int8 TOPS; % of roofline",
@@ -758,6 +822,7 @@ def main():
         chosen = [] if args.quick else list(extras)
     if chosen:
         result["also"] = {name: extras[name]() for name in chosen}
+    result["clocks"] = CLOCKS.summary()
     # The oracle runs last: its host threads can keep the cores busy for a
     # while after it returns, which would delay the graph launches between
     # the timing events of the GPU measurements.
