@@ -378,8 +378,7 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
         if (norm) s2 += piece_sumsq(v[r], bf16);
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+    amax = wave_max_u32(amax);
     if (lane == 0) slots[wave * M + m] = amax;
     if (norm) {
 #pragma unroll
@@ -443,8 +442,7 @@ __device__ void stage_store_x1(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* 
       if (NORM) s2 += piece_sumsq(v[r], bf16);
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, o, 64));
+  amax = wave_max_u32(amax);
   if (NORM) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);

@@ -112,8 +112,7 @@ __device__ inline u4 scale_f32_piece(const u4 v, float r) {
 // Block-wide max of non-negative float bit patterns / sum of ints via LDS.
 template <int NT>
 __device__ inline uint32_t block_max(uint32_t v, uint32_t* slots) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  v = wave_max_u32(v);
   if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t r = slots[0];
@@ -124,8 +123,7 @@ __device__ inline uint32_t block_max(uint32_t v, uint32_t* slots) {
 
 template <int NT>
 __device__ inline int block_sum(int v, int* slots) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_i32(v);
   if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
   __syncthreads();
   int r = 0;
