@@ -5,8 +5,8 @@
 // One workgroup per token row.  Each thread loads its 16-byte pieces of the
 // row (8 bf16 or 4 fp32 values) once and keeps up to kHold of them in
 // registers: the row maximum of |x| is taken on the sign-cleared bit patterns
-// (packed 16-bit integer max for bf16), reduced across the wave with
-// butterfly shuffles and across waves through LDS; then every held piece is
+// (packed 16-bit integer max for bf16), reduced across the wave with DPP
+// moves and across waves through LDS; then every held piece is
 // quantized, q = rint(x * (127 / g)), g = max(gamma, 1e-5), and stored as
 // int8 (zero padding up to the row stride).  Rows that are not whole 16-byte
 // pieces (unaligned x, or K not a multiple of the piece) take an element
