@@ -20,7 +20,8 @@ Also printed on the same JSON line:
                 launch duration (HIP events on the launch stream around a
                 graph of back-to-back launches), against the 8 TB/s HBM peak;
   cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) running the same
-                step on the host cores, on a bounded number of repetitions;
+                step on the host cores, on a bounded number of repetitions, and
+                on one thread (value_1thread);
   roofline.traffic  measured HBM bytes per launch of the same kernel, from two
                 rocprofv3 --pmc runs of `bench.py --counters` (FETCH_SIZE, then
                 WRITE_SIZE, KiB per dispatch), each scaled by the factor that
@@ -492,19 +493,26 @@ def cpu_baseline(host, wl, budget_s=10.0):
         beta = oracle.absmean(w)
         prepared.append((oracle.ternarize(w, beta), beta, xb))
     per_step = sum(l.N * l.K // 4 for l in wl.linears)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for t, beta, xb in prepared:
-            q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
-            acc = oracle.matmul_i32(q, t, threads=threads)
-            oracle.dequant(acc, ds, beta)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
+
+    def run(nthreads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            for t, beta, xb in prepared:
+                q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
+                acc = oracle.matmul_i32(q, t, threads=nthreads)
+                oracle.dequant(acc, ds, beta)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    reps, el = run(threads, budget_s)
+    reps1, el1 = run(1, budget_s / 3)
     return {"value": round(per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "%d decode steps (quantize + int32 product + dequant, both 2B shapes, M=1) in %.1f s"
-                      % (reps, el)}
+                      % (reps, el),
+            "value_1thread": round(per_step * reps1 / el1 / 1e9, 3),
+            "sample_1thread": "%d steps on one thread in %.1f s" % (reps1, el1)}
 
 
 # ------------------------------------------------------------------- extras
