@@ -207,6 +207,23 @@ struct GemvArgs {
   uint32_t* ws_cnt;
 };
 
+// a.seg[si] for a uniform si, field by field through selects over the fixed
+// offsets of every segment
+__device__ inline GemvSeg seg_select(const GemvArgs& a, int si) {
+  GemvSeg s = a.seg[0];
+#pragma unroll
+  for (int i = 1; i < kGemvMaxSeg; ++i) {
+    const bool t = si == i;
+    s.packed = t ? a.seg[i].packed : s.packed;
+    s.beta = t ? a.seg[i].beta : s.beta;
+    s.y = t ? a.seg[i].y : s.y;
+    s.N = t ? a.seg[i].N : s.N;
+    s.Nt = t ? a.seg[i].Nt : s.Nt;
+    s.g0 = t ? a.seg[i].g0 : s.g0;
+  }
+  return s;
+}
+
 __device__ inline float x_at(const void* x, int dt, int64_t i) {
   return dt == BITLINEAR_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(x)[i])
                               : static_cast<const float*>(x)[i];
@@ -592,9 +609,14 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   const int split = sb * waves + wave;
   const int k0 = split * a.tps;
   const int k1 = min(k0 + a.tps, a.Kt);
-  int si = 0;  // segment of this workgroup (uniform)
-  for (int i = 1; i < a.nseg; ++i) si = grp >= a.seg[i].g0 ? i : si;
-  const GemvSeg sg = a.seg[si];
+  // Segment of this workgroup (uniform).  The segment fields come from fixed
+  // argument offsets and a select on the index, so no argument load waits
+  // for the index (each such wait is one more round trip before the first
+  // weight load).
+  int si = 0;
+#pragma unroll
+  for (int i = 1; i < kGemvMaxSeg; ++i) si = i < a.nseg && grp >= a.seg[i].g0 ? i : si;
+  const GemvSeg sg = seg_select(a, si);
   const int lg = grp - sg.g0;                // output group within the segment
   const int nb0 = a.glu ? lg : lg * NB;      // first 16-row output block
   const int r16 = lane & 15, g4 = lane >> 4;
