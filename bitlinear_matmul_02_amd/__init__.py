@@ -56,7 +56,7 @@ EXPORTS = (
     "bitlinear_forward_decode_glu", "bitlinear_packed_bytes_b1", "bitlinear_pack_weights_b1",
     "bitlinear_gemv_b1", "bitlinear_gemm_b1", "bitlinear_packed_bytes_b3", "bitlinear_pack_weights_b3",
     "bitlinear_gemv_b3", "bitlinear_train_forward", "bitlinear_train_backward_input",
-    "bitlinear_train_backward_weight",
+    "bitlinear_train_backward_weight", "bitlinear_gemv_read_extent",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -135,6 +135,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_gemv_glu.argtypes = [p, p, i64, i64, p, p, p, p, i64, p, p]
     L.bitlinear_forward_decode_glu.restype = i32
     L.bitlinear_forward_decode_glu.argtypes = [p, i32, i64, i64, p, p, p, p, i64, p, p]
+    L.bitlinear_gemv_read_extent.restype = i32
+    L.bitlinear_gemv_read_extent.argtypes = [i64, i64, i64, i32, p, p]
     _lib = L
     return L
 
@@ -185,6 +187,13 @@ def gemv_workspace_bytes(M: int, N: int, K: int) -> int:
 
 def gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(lib().bitlinear_gemm_workspace_bytes(M, N, K))
+
+
+def gemv_read_extent(M: int, N: int, K: int, fmt: int = 0) -> tuple[int, int]:
+    """(activation, weight) read extents in bytes of the decode kernel's plan (host model)."""
+    a, w = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().bitlinear_gemv_read_extent(M, N, K, fmt, ctypes.byref(a), ctypes.byref(w)))
+    return a.value, w.value
 
 
 # --------------------------------------------------------------- the C calls

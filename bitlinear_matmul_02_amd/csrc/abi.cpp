@@ -113,6 +113,17 @@ int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return M == 0 ? 0 : bl::gemm_ws_bytes(M, N, K);
 }
 
+int bitlinear_gemv_read_extent(int64_t M, int64_t N, int64_t K, int format, int64_t* act_end, int64_t* w_end) {
+  const char* fn = "bitlinear_gemv_read_extent";
+  if (M < 1 || M > BITLINEAR_GEMV_MAX_M || !n_ok(N) || !k_ok(K))
+    return fail(BITLINEAR_ERR_SHAPE, "%s: M=%lld, N=%lld, K=%lld out of range", fn, (long long)M, (long long)N,
+                (long long)K);
+  if (format < 0 || format > 2) return fail(BITLINEAR_ERR_ARG, "%s: unknown format %d", fn, format);
+  if (!act_end || !w_end) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  bl::gemv_read_extent(M, N, K, format, act_stride(K), act_end, w_end);
+  return ok();
+}
+
 int bitlinear_quant_act(const void* x, int x_dtype, int64_t M, int64_t K, int8_t* x_q, float* x_ds,
                         int32_t* x_rowsum, void* stream) {
   const char* fn = "bitlinear_quant_act";

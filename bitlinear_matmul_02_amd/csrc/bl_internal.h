@@ -47,6 +47,10 @@ hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s);
 
+// Host model of the decode kernel's global read extents (fmt 0 ternary 2-bit,
+// 1 binary, 2 base-3; int8 rows of ldq bytes).
+void gemv_read_extent(int64_t M, int64_t N, int64_t K, int fmt, int64_t ldq, int64_t* act_end, int64_t* w_end);
+
 // Fused decode: per-token quantization of x inside the product kernel.
 bool decode_fused_fits(int64_t M, int64_t K);
 hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,

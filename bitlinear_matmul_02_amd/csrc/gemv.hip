@@ -63,6 +63,7 @@
 // their sums meet in an int32 workspace through device-scope atomics and the
 // last workgroup to arrive (a counter) dequantizes, stores y and zeroes the
 // workspace again.
+#include <algorithm>
 #include <type_traits>
 
 #include "bl_internal.h"
@@ -590,6 +591,19 @@ __device__ inline void b3_digits(uint32_t dw, uint32_t (&d)[5]) {
   for (int s = 0; s < 5; ++s) d[s] = __builtin_bit_cast(uint32_t, de[s]) | (__builtin_bit_cast(uint32_t, dd[s]) << 8);
 }
 
+// Byte offset within a token row of the 16 activation bytes that lanes
+// 16 g4 .. 16 g4 + 15 use in MFMA step i of k-tile kt (KT columns per tile).
+// Rows read from global memory are act_stride(K) bytes, which can be shorter
+// than the k-tiles of a base-3 matrix (320 columns): those reads are clamped
+// to the row's last 16 bytes.  Every column they stand for is past K (the row
+// length and the offsets are multiples of 16), where the weight codes are 0
+// (base 3: c = 0), so the bytes read there add nothing, and the rowsum
+// correction covers the real columns only.
+__host__ __device__ inline int64_t act_col(int kt, int i, int g4, int KT, int64_t row_bytes, bool clamp) {
+  const int64_t c = (int64_t)kt * KT + 64 * i + 16 * g4;
+  return clamp && c > row_bytes - 16 ? row_bytes - 16 : c;
+}
+
 template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT)>
 __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int KT = tile_cols(FMT), NS = KT / 64;  // columns and MFMA steps per k-tile
@@ -640,8 +654,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // their accumulators are never stored, so the loads need no branch.
   int64_t aoff[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-    aoff[mb] = (int64_t)min(mb * 16 + r16, M - 1) * (AM == AGLOBAL ? a.ldq : a.ldl) + 16 * g4;
+  for (int mb = 0; mb < MB; ++mb) aoff[mb] = (int64_t)min(mb * 16 + r16, M - 1) * (AM == AGLOBAL ? a.ldq : a.ldl);
 
   u4 wbuf[kU][NB];
   v4i abuf[UA][MB][NS];
@@ -655,7 +668,8 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int i = 0; i < NS; ++i)
-        abuf[slot][mb][i] = *reinterpret_cast<const v4i*>(base + aoff[mb] + (int64_t)kt * KT + 64 * i);
+        abuf[slot][mb][i] = *reinterpret_cast<const v4i*>(
+            base + aoff[mb] + act_col(kt, i, g4, KT, a.ldq, AM == AGLOBAL && FMT == 2));
   };
   auto mma_tile = [&](int slot, int kt) {
     const int as = AM == AGLOBAL ? slot : 0;
@@ -1054,6 +1068,38 @@ bool gemv_prefers_gemm(int64_t M, int64_t N, int64_t K) {
 
 int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
   return gemv_prefers_gemm(M, N, K) ? gemm_ws_bytes(M, N, K) : make_plan(M, N, K, false).ws_bytes;
+}
+
+// Host model of the decode kernel's global reads for bitlinear_gemv(_b1,_b3)
+// at these sizes (int8 rows of ldq bytes): walks every workgroup, wave and
+// k-tile of the kernel's plan, including the ring's clamped re-loads, with the
+// kernel's own offset function, and returns one past the last byte any lane
+// reads of the activations and of the packed weights.
+void gemv_read_extent(int64_t M, int64_t N, int64_t K, int fmt, int64_t ldq, int64_t* act_end, int64_t* w_end) {
+  const GemvPlan p = make_plan(M, N, K, false, fmt == 0, M * (ldq / 16), fmt);
+  const int KT = tile_cols(fmt), NS = KT / 64;
+  int64_t ae = 0, we = 0;
+  for (int grp = 0; grp < p.Ng; ++grp)
+    for (int sb = 0; sb < p.SB; ++sb)
+      for (int wave = 0; wave < p.waves; ++wave) {
+        const int k0 = (sb * p.waves + wave) * p.tps, k1 = std::min(k0 + p.tps, p.Kt);
+        // the prologue's unconditional ring loads read [kfirst, klast]; the
+        // loop's re-loads are clamped to k1 - 1
+        const int kf = k0 < k1 ? k0 : 0, kl = k0 < k1 ? k1 - 1 : 0;
+        for (int j = 0; j < p.NB; ++j) {
+          const int64_t nb = std::min(grp * p.NB + j, p.Nt - 1);
+          we = std::max(we, (nb * p.Kt + kl) * kTileBytes + kTileBytes);
+        }
+        if (p.amode != AGLOBAL || k0 >= k1) continue;
+        const int64_t row = std::min<int64_t>(p.MB * 16 - 1, M - 1) * ldq;
+        for (int kt = kf; kt <= kl; ++kt)
+          for (int i = 0; i < NS; ++i)
+            for (int g4 = 0; g4 < 4; ++g4)
+              ae = std::max(ae, row + act_col(kt, i, g4, KT, ldq, fmt == 2) + 16);
+      }
+  if (p.amode != AGLOBAL) ae = M * ldq;  // rows staged whole: pieces < M * ldq / 16
+  *act_end = ae;
+  *w_end = we;
 }
 
 bool decode_fused_fits(int64_t M, int64_t K) {

@@ -115,6 +115,22 @@ int64_t bitlinear_gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int64_t bitlinear_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
+ * Introspection for tests (no GPU needed, computes nothing on a device): the
+ * read extents of the decode product kernel that bitlinear_gemv (format 0),
+ * bitlinear_gemv_b1 (1) or bitlinear_gemv_b3 (2) launches for M tokens, K
+ * inputs and N outputs, modelled on the host from the kernel's own plan and
+ * offset arithmetic.  *act_end is one past the last byte of x_q (rows of
+ * bitlinear_act_stride(K) bytes) any lane reads, *w_end one past the last
+ * byte of the packed weights.  Both must stay within M * act_stride(K) and
+ * the packed size.  (For format 0, bitlinear_gemv hands larger batches to
+ * the prefill kernel; the model describes the decode kernel's plan.)
+ * Returns BITLINEAR_ERR_SHAPE for M outside [1, BITLINEAR_GEMV_MAX_M] or N, K
+ * out of range, BITLINEAR_ERR_ARG for an unknown format or a null pointer.
+ */
+int bitlinear_gemv_read_extent(int64_t M, int64_t N, int64_t K, int format, int64_t *act_end,
+                               int64_t *w_end);
+
+/*
  * Per-token absmax activation quantization.
  *   x        [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32,
  *            optionally | BITLINEAR_X_RMSNORM;

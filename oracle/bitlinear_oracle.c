@@ -408,22 +408,6 @@ void oracle_unpack_b3(const uint8_t *packed, int64_t N, int64_t K, int8_t *t)
         }
 }
 
-/* --------------------------------------------------------- whole forward */
-
-/* y = dequant(Q(x) . T(w)^T): the BitLinear forward for bf16 activations
- * x[M][K] and latent weights w[N][K].  Writes the intermediate values too
- * (any of q, ds, rowsum, t, acc may be used by the caller for checks). */
-void oracle_bitlinear_forward(const uint16_t *xb, int64_t M, int64_t K, const float *w, int64_t N,
-                              int8_t *q, float *ds, int32_t *rowsum, int8_t *t, float *beta,
-                              int32_t *acc, float *y, int threads)
-{
-    *beta = oracle_absmean(w, N * K);
-    oracle_ternarize(w, N * K, *beta, t);
-    oracle_quant_act_bf16(xb, M, K, q, ds, rowsum);
-    oracle_matmul_i32(q, t, M, N, K, acc, threads);
-    oracle_dequant_f32(acc, ds, *beta, M, N, y);
-}
-
 /* ------------------------------------------------------- decoder glue */
 
 /* h = ReLU(g)^2 * u elementwise: r = g if g > 0 else +0, then (r * r) * u,

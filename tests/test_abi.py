@@ -272,3 +272,29 @@ def test_train_validation():
     assert L.bitlinear_train_backward_input(FAKE, -1, 16, FAKE, FAKE, 256, FAKE, None) == bl.ERR_SHAPE
     assert L.bitlinear_train_backward_weight(FAKE, None, 4, 16, 256, FAKE, None) == bl.ERR_ARG
     assert L.bitlinear_train_backward_weight(FAKE, FAKE, 4, 16, 256, FAKE + 2, None) == bl.ERR_ALIGN
+
+
+# The decode kernel's global reads stay inside the caller's buffers: a host
+# model of every workgroup's, wave's and k-tile's loads (the kernel's own plan
+# and offset function) for the three weight formats.  Base-3 tiles span 320
+# columns while int8 rows are padded to 512, so their last k-tile's operand
+# reads are clamped into the row (K = 512, 2048, 8192, 28672, 131072 and
+# ragged K would otherwise read past the last row).
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("M", [1, 2, 8, 16, 17, 33, 64])
+@pytest.mark.parametrize("N,K", [(16, 256), (40, 700), (512, 512), (100, 3000), (256, 2048), (2560, 6912),
+                                 (28672, 8192), (8192, 28672), (16, 131072), (300, 7), (64, 1000)])
+def test_gemv_reads_stay_in_bounds(fmt, M, N, K):
+    size = {0: bl.packed_bytes, 1: bl.packed_bytes_b1, 2: bl.packed_bytes_b3}[fmt]
+    act_end, w_end = bl.gemv_read_extent(M, N, K, fmt)
+    assert 0 < act_end <= M * bl.act_stride(K)
+    assert 0 < w_end <= size(N, K)
+
+
+def test_gemv_read_extent_validation():
+    a, w = ctypes.c_int64(0), ctypes.c_int64(0)
+    L = bl.lib()
+    assert L.bitlinear_gemv_read_extent(0, 16, 256, 0, ctypes.byref(a), ctypes.byref(w)) == bl.ERR_SHAPE
+    assert L.bitlinear_gemv_read_extent(65, 16, 256, 0, ctypes.byref(a), ctypes.byref(w)) == bl.ERR_SHAPE
+    assert L.bitlinear_gemv_read_extent(1, 16, 256, 3, ctypes.byref(a), ctypes.byref(w)) == bl.ERR_ARG
+    assert L.bitlinear_gemv_read_extent(1, 16, 256, 0, None, ctypes.byref(w)) == bl.ERR_ARG

@@ -264,14 +264,19 @@ def two_layers():
     return stack_inputs(2)
 
 
+@pytest.fixture(scope="module")
+def four_layers():
+    return stack_inputs(4)
+
+
 @pytest.mark.parametrize("M", list(workloads.DECODE_STEP_BATCHES) + [3, 64, 80])
-def test_decode_step_layers_match_oracle(two_layers, M):
+def test_decode_step_layers_match_oracle(four_layers, M):
     x0 = workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, workloads.D_MODEL, seed=workloads.DECODER_X0_SEED))
-    stack = gpu_stack(two_layers, M)
+    stack = gpu_stack(four_layers, M)
     assert stack.fused == (M <= 4)
     x = torch.from_numpy(x0).to(DEV)
     xr = x0
-    for l, L in enumerate(two_layers):
+    for l, L in enumerate(four_layers):
         stack.layer(l, x)
         torch.cuda.synchronize()
         xr, parts = oracle_layer(xr, L, {})

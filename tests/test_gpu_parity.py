@@ -207,6 +207,29 @@ def test_gemm_parity(M, N, K):
     check_product(xb, w, use_gemm=True)
 
 
+# 128 x 256 blocks: bitlinear_gemm takes them while ceil(M/128) * ceil(N/256)
+# >= 384 (each case below is at or above that), with ragged token, output
+# and k tails
+@pytest.mark.parametrize("M,N,K", [(2048, 6144, 512), (1999, 6100, 1000), (3000, 4100, 700)])
+def test_gemm_big_tile_parity(M, N, K):
+    assert -(-M // 128) * -(-N // 256) >= 384
+    w = workloads.gen_weights(N, K, seed=3100 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=4100 + M)
+    check_product(xb, w, use_gemm=True, ref=oracle.bitlinear_forward(xb, w, threads=16))
+
+
+# Decode plans with many output groups and long k-runs per wave: one token
+# block, 2-block workgroups, >= 512 groups and >= 32 k-tiles (8 tokens with
+# operands from global memory; one token fused with rows staged in LDS)
+@pytest.mark.parametrize("M,N,K,mode", [(8, 16400, 8192, "gemv"), (1, 16400, 8192, "fused"),
+                                        (1, 16400, 8200, "gemv"), (2, 8200, 28700, "fused")])
+def test_gemv_large_plans_parity(M, N, K, mode):
+    w = workloads.gen_weights(N, K, seed=3200 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=4200 + M, outliers=True)
+    check_product(xb, w, use_gemm=mode if mode == "fused" else False, dtypes=("i32", "f32"),
+                  ref=oracle.bitlinear_forward(xb, w, threads=16))
+
+
 # ----------------------------------- up to 64 tokens on the int8 matrix cores
 @pytest.mark.parametrize("M,N,K,split", [(1, 1000, 4096, True), (37, 333, 6925, True), (64, 6912, 2560, True),
                                          (24, 130, 2048, True), (17, 2560, 6912, True), (64, 64, 512, False),
