@@ -45,6 +45,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libbitlinear.so")
 OK, ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4, -5
 F32, BF16, I32, F32_ADD = 0, 1, 2, 3
 X_RMSNORM = 16  # flag OR-ed into an activation dtype: RMS-normalize rows before quantizing
+NOALLOC_SCRATCH_BYTES = 8 << 20  # device array behind bitlinear_gemv_noalloc
 MAX_K, MAX_N, MAX_M, GEMV_MAX_M = 131072, 1 << 20, 1 << 20, 64
 
 EXPORTS = (
@@ -56,7 +57,7 @@ EXPORTS = (
     "bitlinear_forward_decode_glu", "bitlinear_packed_bytes_b1", "bitlinear_pack_weights_b1",
     "bitlinear_gemv_b1", "bitlinear_gemm_b1", "bitlinear_packed_bytes_b3", "bitlinear_pack_weights_b3",
     "bitlinear_gemv_b3", "bitlinear_train_forward", "bitlinear_train_backward_input",
-    "bitlinear_train_backward_weight", "bitlinear_gemv_read_extent",
+    "bitlinear_train_backward_weight", "bitlinear_gemv_read_extent", "bitlinear_gemv_noalloc",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -135,6 +136,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_gemv_glu.argtypes = [p, p, i64, i64, p, p, p, p, i64, p, p]
     L.bitlinear_forward_decode_glu.restype = i32
     L.bitlinear_forward_decode_glu.argtypes = [p, i32, i64, i64, p, p, p, p, i64, p, p]
+    L.bitlinear_gemv_noalloc.restype = i32
+    L.bitlinear_gemv_noalloc.argtypes = [p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_gemv_read_extent.restype = i32
     L.bitlinear_gemv_read_extent.argtypes = [i64, i64, i64, i32, p, p]
     _lib = L
@@ -296,6 +299,13 @@ def bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=No
     with ``accumulate`` y += the fp32 result)."""
     _product(lib().bitlinear_gemv, x_q, x_ds, x_ds.shape[0], K, packed, w_beta, N, y, workspace,
              stream, accumulate)
+
+
+def bitlinear_gemv_noalloc(x_q, x_ds, K, packed, w_beta, N, y, stream=None, accumulate: bool = False) -> None:
+    """bitlinear_gemv without a workspace: split-k partial sums live in the library's
+    device-resident scratch array (no allocation; calls on one GPU must not overlap)."""
+    _check(lib().bitlinear_gemv_noalloc(_ptr(x_q), _ptr(x_ds), x_ds.shape[0], K, _ptr(packed), _ptr(w_beta), N,
+                                        _ptr(y), _ydtype(y, accumulate), _stream(stream)))
 
 
 def bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, workspace=None, stream=None,

@@ -194,6 +194,27 @@ int bitlinear_gemv(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, c
                     fn);
 }
 
+int bitlinear_gemv_noalloc(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed,
+                           const float* w_beta, int64_t N, void* y, int y_dtype, void* stream) {
+  const char* fn = "bitlinear_gemv_noalloc";
+  int st = check_product(fn, x_q, x_ds, M, BITLINEAR_GEMV_MAX_M, K, packed, w_beta, N, y, y_dtype, nullptr, 0, 0);
+  if (st != BITLINEAR_OK || M == 0) return st == BITLINEAR_OK ? ok() : st;
+  const int64_t need = bl::gemv_ws_bytes(M, N, K);
+  if (need > BITLINEAR_NOALLOC_SCRATCH_BYTES)
+    return fail(BITLINEAR_ERR_UNSUPPORTED, "%s: this shape needs %lld bytes of scratch, more than the %d-byte device "
+                "array; use bitlinear_gemv with a workspace", fn, (long long)need, BITLINEAR_NOALLOC_SCRATCH_BYTES);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = bl::noalloc_scratch(s, &ws);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  const hipError_t e = bl::launch_gemv_t2(x_q, act_stride(K), x_ds, M, K, static_cast<const uint8_t*>(packed), w_beta,
+                                          N, y, y_dtype, ws, s);
+  if (e != hipSuccess && need > 0) bl::noalloc_mark_dirty();
+  return hip_status(e, fn);
+}
+
 int bitlinear_gemm(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed,
                    const float* w_beta, int64_t N, void* y, int y_dtype, void* workspace,
                    size_t workspace_bytes, void* stream) {

@@ -51,6 +51,12 @@ hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t
 // 1 binary, 2 base-3; int8 rows of ldq bytes).
 void gemv_read_extent(int64_t M, int64_t N, int64_t K, int fmt, int64_t ldq, int64_t* act_end, int64_t* w_end);
 
+// The device array behind bitlinear_gemv_noalloc (zero on return, or an
+// error): its address on the current device, cleared first when needed.
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
+// After a failed launch that used the array: clear it before its next use.
+void noalloc_mark_dirty();
+
 // Fused decode: per-token quantization of x inside the product kernel.
 bool decode_fused_fits(int64_t M, int64_t K);
 hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,

@@ -347,6 +347,30 @@ int bitlinear_forward_decode_glu(const void *x, int x_dtype, int64_t M, int64_t 
  */
 int bitlinear_relu2_mul(const float *g, const float *u, int64_t count, float *h, void *stream);
 
+/* Bytes of the device array bitlinear_gemv_noalloc uses as scratch. */
+#define BITLINEAR_NOALLOC_SCRATCH_BYTES (8 << 20)
+
+/*
+ * bitlinear_gemv for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same product, arguments and results as bitlinear_gemv, but the split-k
+ * partial sums some shapes need live in a fixed array of
+ * BITLINEAR_NOALLOC_SCRATCH_BYTES in device memory that each GPU holds until
+ * the process ends, instead of a caller-provided workspace.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine);
+ * the caller still passes inputs and outputs.  Every shape bitlinear_gemv
+ * accepts needs at most 8 MiB (bitlinear_gemv_workspace_bytes); a shape
+ * needing more would return BITLINEAR_ERR_UNSUPPORTED.  The array is shared
+ * by every call on the same GPU and keeps the last call's contents (zero
+ * after each successful call; cleared by a kernel on first use and after a
+ * failed launch): calls that overlap on one GPU race and must be serialized,
+ * e.g. on one stream.
+ * Errors: as bitlinear_gemv.
+ */
+int bitlinear_gemv_noalloc(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K,
+                           const void *packed, const float *w_beta, int64_t N, void *y, int y_dtype,
+                           void *stream);
+
 #ifdef __cplusplus
 }
 #endif

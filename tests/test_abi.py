@@ -44,6 +44,8 @@ def test_header_constants_match_binding():
     assert int(consts["BITLINEAR_MAX_K"]) == bl.MAX_K
     assert int(consts["BITLINEAR_GEMV_MAX_M"]) == bl.GEMV_MAX_M
     assert int(consts["BITLINEAR_DECODE_MAX_ACT_BYTES"]) == bl.DECODE_MAX_ACT_BYTES
+    assert eval(re.search(r"#define BITLINEAR_NOALLOC_SCRATCH_BYTES \(([^)]*)\)", text).group(1)) == \
+        bl.NOALLOC_SCRATCH_BYTES
 
 
 def test_size_helpers():
@@ -298,3 +300,31 @@ def test_gemv_read_extent_validation():
     assert L.bitlinear_gemv_read_extent(65, 16, 256, 0, ctypes.byref(a), ctypes.byref(w)) == bl.ERR_SHAPE
     assert L.bitlinear_gemv_read_extent(1, 16, 256, 3, ctypes.byref(a), ctypes.byref(w)) == bl.ERR_ARG
     assert L.bitlinear_gemv_read_extent(1, 16, 256, 0, None, ctypes.byref(w)) == bl.ERR_ARG
+
+
+# bitlinear_gemv_noalloc's device array covers every shape bitlinear_gemv accepts:
+# the small-batch split keeps S * ceil(M/bm) * ceil(N/bn) <= 256 workgroups, so
+# S * M * N * 4 <= 8 MiB; the decode kernel's own split needs at most 1 MiB.
+@pytest.mark.parametrize("M", [1, 2, 5, 8, 11, 12, 16, 17, 24, 31, 32, 33, 40, 48, 49, 63, 64])
+def test_noalloc_scratch_covers_every_gemv_shape(M):
+    for N in (1, 16, 100, 255, 256, 257, 640, 1000, 2560, 4096, 6912, 8192, 16384, 28672, 65536, 1 << 20):
+        for K in (1, 256, 1000, 4096, 6912, 8192, 28672, 65536, 131072):
+            assert bl.gemv_workspace_bytes(M, N, K) <= bl.NOALLOC_SCRATCH_BYTES, (M, N, K)
+
+
+def test_noalloc_validation():
+    L = bl.lib()
+    p = ctypes.c_void_p(1 << 20)
+    args = [p, p, 1, 256, p, p, 16, p, bl.F32, None]
+    bad = list(args)
+    bad[2] = 65
+    assert L.bitlinear_gemv_noalloc(*bad) == bl.ERR_SHAPE
+    bad = list(args)
+    bad[8] = 9
+    assert L.bitlinear_gemv_noalloc(*bad) == bl.ERR_ARG
+    bad = list(args)
+    bad[4] = ctypes.c_void_p((1 << 20) + 1)
+    assert L.bitlinear_gemv_noalloc(*bad) == bl.ERR_ALIGN
+    bad = list(args)
+    bad[2] = 0
+    assert L.bitlinear_gemv_noalloc(*bad) == bl.OK  # empty batch: nothing enqueued

@@ -49,7 +49,8 @@ def test_abi_validation_under_asan_ubsan(tmp_path):
              "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     srcs = [os.path.join(CSRC, f) for f in
-            ("abi.cpp", "gemv.hip", "gemm.hip", "quant_act.hip", "pack.hip", "glue.hip", "train.hip")]
+            ("abi.cpp", "gemv.hip", "gemm.hip", "quant_act.hip", "pack.hip", "glue.hip", "train.hip",
+             "noalloc.hip")]
     srcs.append(os.path.join(SAN, "abi_driver.cpp"))
 
     def compile_one(src):
