@@ -4,40 +4,47 @@
     python bench.py --counters            (run under rocprofv3 --pmc, see below)
     python bench.py --counter-summary FETCH_CSV WRITE_CSV
 
-Headline workload: decode GEMV at batch 1 on the 2B-class shapes, K=2560 ->
-N=6912 and K=6912 -> N=2560, bf16 activations with 1% x20 outliers.  One step
-is the whole inference hot path for one token through both BitLinears:
-per-token int8 quantization then the ternary product with fused dequant
-(weights are packed once, before timing).  Inputs are resident in HBM; the
-packed weights rotate over enough distinct copies (> 2x the 256 MB Infinity
-Cache) that every step streams them from HBM.  The K timed steps are one HIP
-graph replay (no host launch overhead inside the timed region).
+Headline workload: decode GEMV at batch 1 on the 100B-class shapes, the
+largest configuration that fits one GPU: K=8192 -> N=28672 and K=28672 ->
+N=8192, bf16 activations N(0, 1).  One step is the whole inference hot path
+for one token through both BitLinears: per-token absmax int8 quantization,
+the ternary product and the dequantization (fp32 out), one fused launch per
+BitLinear (weights packed once, before timing).  Inputs are resident in HBM.
+Every BitLinear cycles through its own R distinct copies of its packed
+weights, R * (its bytes) >= 2x the 256 MB Infinity Cache, and its copy
+counter runs on across every graph (warm-up, timed), so a copy is read again
+only after at least twice the cache's capacity of its other copies: every
+step streams its weights from HBM.  The W warm-up steps and the K timed steps
+are two HIP graphs, each replayed once (no host launch cost inside).
 
 value = packed weight bytes of the step x K / elapsed time, in GB/s.
 
 Also printed on the same JSON line:
-  roofline      the decode kernel: algorithmic bytes per launch / its average
-                launch duration (HIP events on the launch stream around a
-                graph of back-to-back launches), against the 8 TB/s HBM peak;
-  cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) running the same
-                step on the host cores, on a bounded number of repetitions, and
-                on one thread (value_1thread);
+  roofline      the decode kernel, against the 8 TB/s HBM peak: achieved =
+                the algorithmic bytes of the step's launches (packed weights,
+                bf16 x, fp32 y of both BitLinears) / the timed step (HIP events
+                on the launch stream around the timed graph, whose steps hold
+                only these launches);
   roofline.traffic  measured HBM bytes per launch of the same kernel, from two
                 rocprofv3 --pmc runs of `bench.py --counters` (FETCH_SIZE, then
                 WRITE_SIZE, KiB per dispatch), each scaled by the factor that
                 makes the same counter read the known size of a 64 MiB device
                 copy in the same run; `--counter-summary` turns the two CSV
-                files into profiles/traffic_gemv_fused_decode_2b_m1.txt, which
+                files into profiles/traffic_gemv_decode_100b_m1.txt, which
                 records a hash of the kernel sources; the field is null when
                 the sources have changed since;
-  also          the other workloads: one decode step over the 30-layer 2B-class
-                stack (210 BitLinears + glue, batch 1 and 8) in tokens/s,
-                checked bit for bit against the oracle's chain; 100B-class
-                decode (M = 1, 8, 32) in GB/s; binary-weight (b1) and base-3
-                (b3) decode on the 2B and 100B shapes (M = 1, 8); prefill GEMMs (2B M=2048,
-                100B M=512), ternary and binary, in int8 TOPS; the training
-                products (straight-through forward, input and weight
-                gradients, 2B shapes, 2048 tokens) in bf16 TFLOP/s;
+  cpu_baseline  the CPU oracle (plain C, OpenMP over outputs) on the host cores,
+                on bounded samples: the headline step on all cores and on one
+                thread, and every other configuration (see cpu_baseline());
+  also          the other workloads: the 2B-class decode GEMV at batch 1; one
+                decode step over the 30-layer 2B-class stack (210 BitLinears +
+                glue, batch 1 and 8) in tokens/s, checked bit for bit against
+                the oracle's chain; 100B-class decode (M = 1, 8, 32) in GB/s;
+                binary-weight (b1) and base-3 (b3) decode on the 2B and 100B
+                shapes (M = 1, 8); prefill GEMMs (2B M=2048, 100B M=512),
+                ternary and binary, in int8 TOPS; the training products
+                (straight-through forward, input and weight gradients, 2B
+                shapes, 2048 tokens) in bf16 TFLOP/s;
   clocks        the shader and memory clock levels the driver reported while
                 the timed graphs ran (min / median / max of 1 ms samples).
 """
@@ -58,20 +65,22 @@ import bitlinear_matmul_02_amd as bl
 import workloads
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_fused_decode_2b_m1.txt")
+HEADLINE = workloads.DECODE_100B
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_decode_100b_m1.txt")
 KERNEL_SOURCES = ("bitlinear_matmul_02_amd/csrc/gemv.hip", "bitlinear_matmul_02_amd/csrc/bl_internal.h")
 CAL_BYTES = 64 << 20  # calibration copy
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
 MALL_BYTES = 256 << 20
+THREADS = max(1, min(16, os.cpu_count() or 1))  # host threads of the oracle
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--counters", action="store_true",
@@ -91,11 +100,20 @@ def parse():
 
 
 # ------------------------------------------------------------------ helpers
+def rotation(weight_bytes):
+    """Distinct copies of one matrix such that R copies span at least twice
+    the Infinity Cache: a copy is read again only after >= 2x its capacity of
+    other copies of the same matrix."""
+    return int(max(2, min(512, -(-2 * MALL_BYTES // max(weight_bytes, 1)) + 1)))
+
+
 class Linear:
     """Device buffers of one BitLinear used in a timed step.
 
     mode "fused": one launch (bitlinear_forward_decode);
-    mode "gemv" / "gemm": bitlinear_quant_act then the product call."""
+    mode "gemv" / "gemm": bitlinear_quant_act then the product call.
+    Each product call uses the next of the R weight copies (a counter that
+    runs on across graphs)."""
 
     def __init__(self, M, K, N, packed_copies, beta, x, y_dtype=torch.float32, mode=None):
         dev = x.device
@@ -103,6 +121,7 @@ class Linear:
         self.packed = packed_copies
         self.beta = beta
         self.x = x
+        self.r = 0
         if mode is None:
             # the fused decode kernel wins while the quantization it repeats per
             # workgroup is small (measured: M <= 4); the GEMV otherwise
@@ -123,27 +142,28 @@ class Linear:
     def traffic_bytes(self):
         """Algorithmic HBM bytes of the timed kernel: packed weights once, its
         activation input once (bf16 x when fused, int8 rows otherwise), y once."""
-        act = self.M * self.K * self.x.element_size() if self.mode == "fused" else self.M * bl.act_stride(self.K)
-        return self.weight_bytes() + act + self.M * self.N * self.y.element_size()
+        return algorithmic_bytes(self.M, self.K, self.N, self.mode, self.x.element_size(), self.y.element_size())
 
     def quant(self):
         if self.mode != "fused":
             bl.bitlinear_quant_act(self.x, self.x_q, self.x_ds)
 
-    def run_product(self, r):
-        packed = self.packed[r % len(self.packed)]
+    def run_product(self):
+        packed = self.packed[self.r % len(self.packed)]
+        self.r += 1
         if self.mode == "fused":
             bl.bitlinear_forward_decode(self.x, packed, self.beta, self.N, self.y)
         else:
             self.product(self.x_q, self.x_ds, self.K, packed, self.beta, self.N, self.y, self.ws)
 
-    def step(self, r):
+    def step(self):
         self.quant()
-        self.run_product(r)
+        self.run_product()
 
 
-def rotation(per_step_bytes):
-    return int(max(1, min(256, -(-2 * MALL_BYTES // max(per_step_bytes, 1)) + 1)))
+def algorithmic_bytes(M, K, N, mode, x_bytes=2, y_bytes=4):
+    act = M * K * x_bytes if mode == "fused" else M * bl.act_stride(K)
+    return N * K // 4 + act + M * N * y_bytes
 
 
 def pack_from_host(w_np, dev):
@@ -155,26 +175,19 @@ def copies_of(packed, n):
 
 
 def capture(fn, nsteps):
-    """One HIP graph holding fn(0) ... fn(nsteps - 1)."""
+    """One HIP graph holding nsteps calls of fn."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn(0)  # one eager call first (loads code objects)
+        fn()  # one eager call first (loads code objects)
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
-            for i in range(nsteps):
-                fn(i)
+            for _ in range(nsteps):
+                fn()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     return g
-
-
-def capture_steps(linears, nsteps):
-    def one(i):
-        for lin in linears:
-            lin.step(i)
-    return capture(one, nsteps)
 
 
 class ClockSampler:
@@ -233,15 +246,15 @@ class ClockSampler:
 CLOCKS = None
 
 
-def time_graph(g, reps=1):
+def time_graph(g):
+    """Replay g once; HIP events on the current stream around it."""
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if CLOCKS:
         CLOCKS.busy = True
     a.record()
-    for _ in range(reps):
-        g.replay()
+    g.replay()
     b.record()
     torch.cuda.synchronize()
     if CLOCKS:
@@ -249,66 +262,96 @@ def time_graph(g, reps=1):
     return a.elapsed_time(b) / 1e3, time.perf_counter() - t0
 
 
+def timed(fn, nsteps, warm):
+    """Seconds for nsteps calls of fn: a graph of `warm` calls, then a graph of
+    nsteps calls, each replayed once, in the order captured (so that weight
+    copy counters run on without repeats); returns (elapsed, wall)."""
+    g_warm = capture(fn, max(warm, 1))
+    g_main = capture(fn, nsteps)
+    time_graph(g_warm)
+    out = time_graph(g_main)
+    del g_warm, g_main
+    return out
+
+
 def kernel_duration(lin, launches=200):
-    """Average duration of the product kernel: HIP events on the launch stream
-    around a graph of `launches` back-to-back launches (weight copies rotate)."""
+    """Average duration of the product kernel alone: HIP events on the launch
+    stream around a graph of `launches` back-to-back launches (its weight
+    copies rotate)."""
     lin.quant()
-    g = capture(lambda i: lin.run_product(i), launches)
-    time_graph(g)
-    el, _ = time_graph(g)
+    el, _ = timed(lin.run_product, launches, launches // 4)
     return el / launches
 
 
 # --------------------------------------------------------------- headline
-def headline(args, dev):
-    wl = workloads.DECODE_2B
-    host = []
-    for i, lin in enumerate(wl.linears):
-        w = workloads.gen_weights(lin.N, lin.K, seed=2 * i)
-        xb = workloads.gen_acts_bf16(lin.M, lin.K, seed=2 * i + 1, outliers=lin.outliers)
-        host.append((w, xb))
-    per_step = sum(l.N * l.K // 4 for l in wl.linears)
-    R = rotation(per_step)
+def build_linears(wl, dev, host=None):
+    """Device buffers of the workload's BitLinears from host-drawn inputs
+    (tensor i: weights seed 2i, activations seed 2i + 1); returns (linears, host)."""
+    if host is None:
+        host = []
+        for i, lin in enumerate(wl.linears):
+            w = workloads.gen_weights(lin.N, lin.K, seed=2 * i)
+            xb = workloads.gen_acts_bf16(lin.M, lin.K, seed=2 * i + 1, outliers=lin.outliers)
+            host.append((w, xb))
     linears = []
     for (w, xb), lin in zip(host, wl.linears):
         packed, beta = pack_from_host(w, dev)
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-        linears.append(Linear(lin.M, lin.K, lin.N, copies_of(packed, R), beta, x))
+        linears.append(Linear(lin.M, lin.K, lin.N, copies_of(packed, rotation(lin.N * lin.K // 4)), beta, x))
+    return linears, host
 
-    # sanity: the timed path reproduces the oracle on this input
+
+def decode_workload(wl, args, dev, roofline=True):
+    """Time a decode workload (one step = each BitLinear once) and check the
+    timed path against the oracle on the whole output first."""
     import oracle
+    linears, host = build_linears(wl, dev)
+    prepared = []
     for (w, xb), L in zip(host, linears):
         L.quant()
-        L.run_product(0)
+        L.run_product()
         torch.cuda.synchronize()
-        ref = oracle.bitlinear_forward(xb, w, threads=8)
-        if not np.array_equal(L.y.cpu().numpy(), ref["y"]):
-            raise SystemExit("bench: GPU output differs from the oracle on the headline workload")
+        beta = oracle.absmean(w)
+        t = oracle.ternarize(w, beta)
+        q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
+        if not np.array_equal(L.y.cpu().numpy(), oracle.dequant(oracle.matmul_i32(q, t, threads=THREADS), ds, beta)):
+            raise SystemExit("bench: GPU output differs from the oracle on %s" % wl.name)
+        prepared.append((t, beta, xb))
+    del host
 
-    g_warm = capture_steps(linears, max(args.warmup, 1))
-    g_main = capture_steps(linears, args.steps)
-    time_graph(g_warm)
-    elapsed, wall = time_graph(g_main)
-    value = per_step * args.steps / elapsed / 1e9
-
+    def step():
+        for L in linears:
+            L.step()
+    elapsed, wall = timed(step, args.steps, args.warmup)
+    per_w = sum(L.weight_bytes() for L in linears)
+    per_alg = sum(L.traffic_bytes() for L in linears)
     durs = [kernel_duration(L) for L in linears]
-    bytes_per = [L.traffic_bytes() for L in linears]
     # the same step with the standalone quantizer (two launches per BitLinear)
     split = [Linear(L.M, L.K, L.N, L.packed, L.beta, L.x, mode="gemv") for L in linears]
-    g_split = capture_steps(split, args.steps)
-    time_graph(g_split)
-    el_split, _ = time_graph(g_split)
-    achieved = sum(bytes_per) / sum(durs) / 1e9
+    el_split, _ = timed(lambda: [L.step() for L in split], args.steps, args.warmup)
+    achieved = per_alg * args.steps / elapsed / 1e9
     out = {
-        "value": value, "ms_per_step": elapsed / args.steps * 1e3, "wall_s": wall,
-        "rotation_copies": R,
+        "value": per_w * args.steps / elapsed / 1e9, "ms_per_step": elapsed / args.steps * 1e3, "wall_s": wall,
+        "rotation_copies": [len(L.packed) for L in linears],
+        "rotation_bytes_per_shape": [len(L.packed) * L.weight_bytes() for L in linears],
         "unfused_us_per_step": round(el_split / args.steps * 1e6, 2),
         "kernel_us": {"%dx%d->%d" % (L.M, L.K, L.N): round(d * 1e6, 3) for L, d in zip(linears, durs)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "gemv_t2_kernel (fused quantization)", "bytes_per_launch": bytes_per},
+        "mode": linears[0].mode,
     }
-    return out, host, wl
+    if roofline:
+        out["roofline"] = {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+            "kernel": "gemv_t2_kernel (%s)" % ("fused quantization" if linears[0].mode == "fused" else linears[0].mode),
+            "bytes_per_launch": [L.traffic_bytes() for L in linears],
+            "duration_us_per_launch": round(elapsed / args.steps / len(linears) * 1e6, 3),
+            "timing": "HIP events on the launch stream around the timed graph; its steps hold only these launches",
+        }
+    else:
+        out["frac_hbm"] = round(achieved / HBM_PEAK_GBS, 4)
+    del linears, split
+    torch.cuda.empty_cache()
+    return out, prepared
 
 
 # ------------------------------------------------------- HBM traffic counters
@@ -320,32 +363,27 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def headline_linears(dev, R):
-    wl = workloads.DECODE_2B
-    out = []
-    for i, lin in enumerate(wl.linears):
-        w = workloads.gen_weights(lin.N, lin.K, seed=2 * i)
-        xb = workloads.gen_acts_bf16(lin.M, lin.K, seed=2 * i + 1, outliers=lin.outliers)
-        packed, beta = pack_from_host(w, dev)
-        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-        out.append(Linear(lin.M, lin.K, lin.N, copies_of(packed, R), beta, x))
-    return out
-
-
 def counters_run(dev):
     """Dispatches for counter collection: a 64 MiB device copy (calibration),
-    then each headline kernel COUNTER_LAUNCHES times over rotating weight copies."""
+    then each headline kernel COUNTER_LAUNCHES times over its rotating weight copies."""
     launches = COUNTER_LAUNCHES
-    src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
+    # three copies of 64 MiB, each from a source no cache holds: a 1 GiB fill
+    # (4x the Infinity Cache) runs before each, so the copy's reads all leave L2
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
     for _ in range(3):
+        src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        flush.fill_(1)
+        torch.cuda.synchronize()
         dst.copy_(src)
-    torch.cuda.synchronize()
-    linears = headline_linears(dev, rotation(sum(l.N * l.K // 4 for l in workloads.DECODE_2B.linears)))
+        torch.cuda.synchronize()
+        del src, dst
+    del flush
+    linears, _ = build_linears(HEADLINE, dev)
     for L in linears:
-        for i in range(launches):
-            L.run_product(i)
+        L.quant()
+        for _ in range(launches):
+            L.run_product()
     torch.cuda.synchronize()
     print(json.dumps({"counters_run": [L.traffic_bytes() for L in linears]}), flush=True)
 
@@ -420,9 +458,10 @@ COUNTER_LAUNCHES = 16  # dispatches per headline shape in counters_run, in workl
 def counter_summary(fetch_csv, write_csv):
     """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by the calibration copy
     and write the per-launch HBM traffic of the headline kernels."""
-    lins = workloads.DECODE_2B.linears
+    lins = HEADLINE.linears
     labels = ["%dx%d->%d" % (l.M, l.K, l.N) for l in lins]
-    algo = [l.N * l.K // 4 + l.M * l.K * 2 + l.M * l.N * 4 for l in lins]  # packed + bf16 x + fp32 y
+    modes = ["fused" if (l.M <= 4 and bl.decode_fits(l.M, l.K)) else "gemv" for l in lins]
+    algo = [algorithmic_bytes(l.M, l.K, l.N, m) for l, m in zip(lins, modes)]  # packed + x + fp32 y
     factors, med, names = {}, {}, {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
@@ -449,7 +488,7 @@ def counter_summary(fetch_csv, write_csv):
                      % ("", rd, wr, rd + wr, algo[i], (rd + wr) / algo[i]))
     mean = sum(traffic) / len(traffic)
     text = [
-        "HBM traffic of the fused decode kernel (gemv_t2_kernel, fused quantization), 2B-class shapes, batch 1",
+        "HBM traffic of the decode kernel (gemv_t2_kernel, %s), 100B-class shapes, batch 1" % modes[0],
         "",
         "commands (run from the repository root on one MI355X):",
         "  rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o run -- python bench.py --counters",
@@ -457,7 +496,12 @@ def counter_summary(fetch_csv, write_csv):
         "  python bench.py --counter-summary gpurun_out/pmc_fetch/run_counter_collection.csv "
         "gpurun_out/pmc_write/run_counter_collection.csv",
         "",
-        "calibration: a 64 MiB device copy (__amd_rocclr_copyBuffer) in the same run;",
+        "FETCH_SIZE counts the bytes the L2 caches fetch from the memory fabric; an Infinity Cache (MALL) hit",
+        "is such a fetch too, so it measures L2 misses, not HBM reads alone (each weight copy is re-read only",
+        "after >= 2x the MALL's capacity of other copies, so the weight fetches miss the MALL as well).",
+        "",
+        "calibration: 64 MiB device copies (__amd_rocclr_copyBuffer) in the same run, each after a 1 GiB fill",
+        "  so that no cache holds its source;",
         "  FETCH_SIZE factor %.5f (the counter reads %.0f KiB for 65536 KiB moved)" % (factors["FETCH_SIZE"], 65536 / factors["FETCH_SIZE"]),
         "  WRITE_SIZE factor %.5f" % factors["WRITE_SIZE"],
         "",
@@ -485,34 +529,137 @@ def measured_traffic():
     return round(float(kv["traffic_bytes_per_launch_mean"]))
 
 
-def cpu_baseline(host, wl, budget_s=10.0):
+def host_cpu():
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "model": model, "threads_used": THREADS}
+
+
+def time_reps(fn, budget, min_reps=1):
+    """(reps, seconds) of repeated fn() calls until `budget` seconds have passed."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if reps >= min_reps and el >= budget:
+            return reps, el
+
+
+def oracle_decode(prepared, threads):
+    """One oracle step over BitLinears: quantize, int32 product, dequant."""
     import oracle
-    threads = min(16, os.cpu_count() or 1)
-    prepared = []
-    for (w, xb), lin in zip(host, wl.linears):
-        beta = oracle.absmean(w)
-        prepared.append((oracle.ternarize(w, beta), beta, xb))
-    per_step = sum(l.N * l.K // 4 for l in wl.linears)
 
-    def run(nthreads, budget):
-        reps, t0 = 0, time.perf_counter()
-        while True:
-            for t, beta, xb in prepared:
-                q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
-                acc = oracle.matmul_i32(q, t, threads=nthreads)
-                oracle.dequant(acc, ds, beta)
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= budget:
-                return reps, el
+    def run():
+        for t, beta, xb in prepared:
+            q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
+            oracle.dequant(oracle.matmul_i32(q, t, threads=threads), ds, beta)
+    return run
 
-    reps, el = run(threads, budget_s)
-    reps1, el1 = run(1, budget_s / 3)
-    return {"value": round(per_step * reps / el / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d decode steps (quantize + int32 product + dequant, both 2B shapes, M=1) in %.1f s"
-                      % (reps, el),
-            "value_1thread": round(per_step * reps1 / el1 / 1e9, 3),
-            "sample_1thread": "%d steps on one thread in %.1f s" % (reps1, el1)}
+
+def oracle_chain(terns, x, threads):
+    """The oracle's decode step over the decoder stack (terns: per layer, name ->
+    (beta, codes)) from the fp32 residual stream x; returns the new stream."""
+    import oracle
+
+    def lin(inp, b_t):
+        q, ds, _ = oracle.quant_act(inp)
+        return oracle.dequant(oracle.matmul_i32(q, b_t[1], threads=threads), ds, b_t[0])
+    for tern in terns:
+        xn = oracle.rmsnorm(x)
+        q = lin(xn, tern["q"])
+        lin(xn, tern["k"])
+        lin(xn, tern["v"])
+        x = oracle.add_f32(x, lin(q, tern["o"]))
+        xn = oracle.rmsnorm(x)
+        x = oracle.add_f32(x, lin(oracle.relu2_mul(lin(xn, tern["gate"]), lin(xn, tern["up"])), tern["down"]))
+    return x
+
+
+def host_codes(shapes, seed0):
+    """Ternary codes and beta of host-drawn weights (oracle) for (K, N) shapes."""
+    import oracle
+    out = []
+    for i, (K, N) in enumerate(shapes):
+        w = workloads.gen_weights(N, K, seed=seed0 + i)
+        b = oracle.absmean(w)
+        out.append((oracle.ternarize(w, b), b))
+        del w
+    return out
+
+
+def cpu_baseline(head_prepared, stash):
+    """The CPU oracle as it stands, timed on the host cores on bounded samples of
+    each configuration (all cores = THREADS OpenMP threads over outputs; one
+    thread where the sample is small): decode in GB/s of packed weights, the
+    decoder step in tokens/s, prefill in int8 TOPS (2 M N K per product)."""
+    per_w = sum(t.size // 4 for t, _, _ in head_prepared)
+    reps, el = time_reps(oracle_decode(head_prepared, THREADS), 6.0)
+    reps1, el1 = time_reps(oracle_decode(head_prepared, 1), 3.0)
+    res = {"value": round(per_w * reps / el / 1e9, 3), "unit": "GB/s", "cores": THREADS, "kind": "oracle",
+           "sample": "%d decode steps (quantize + int32 product + dequant, both 100B shapes, M=1) in %.1f s"
+                     % (reps, el),
+           "value_1thread": round(per_w * reps1 / el1 / 1e9, 3),
+           "sample_1thread": "%d steps on one thread in %.1f s" % (reps1, el1),
+           "host": host_cpu()}
+    cfg = {}
+
+    def decode_cfg(name, shapes, M, seed, outliers=False, one_thread=False, budget=1.5, codes=None):
+        codes = codes or host_codes(shapes, seed)
+        prep = [(t, b, workloads.gen_acts_bf16(M, K, seed=seed + 50 + i, outliers=outliers))
+                for i, ((t, b), (K, N)) in enumerate(zip(codes, shapes))]
+        wbytes = sum(N * K // 4 for K, N in shapes)
+        r, e = time_reps(oracle_decode(prep, THREADS), budget)
+        row = {"GB_s": round(wbytes * r / e / 1e9, 3), "us_per_step": round(e / r * 1e6, 1),
+               "sample": "%d steps of M=%d in %.2f s" % (r, M, e)}
+        if one_thread:
+            r1, e1 = time_reps(oracle_decode(prep, 1), budget)
+            row["GB_s_1thread"] = round(wbytes * r1 / e1 / 1e9, 3)
+            row["us_per_step_1thread"] = round(e1 / r1 * 1e6, 1)
+        cfg[name] = row
+
+    def prefill_cfg(name, shapes, M, sample_m, seed, codes=None):
+        import oracle
+        codes = codes or host_codes(shapes, seed)
+        ops, secs = 0.0, 0.0
+        for i, ((t, b), (K, N)) in enumerate(zip(codes, shapes)):
+            xb = workloads.gen_acts_bf16(sample_m, K, seed=seed + 50 + i)
+            t0 = time.perf_counter()
+            q, ds, _ = oracle.quant_act(xb, bf16_bits=True)
+            oracle.dequant(oracle.matmul_i32(q, t, threads=THREADS), ds, b)
+            secs += time.perf_counter() - t0
+            ops += 2.0 * sample_m * N * K
+        cfg[name] = {"TOPS": round(ops / secs / 1e12, 4), "seconds": round(secs, 2),
+                     "sample": "%d of the %d tokens of each shape (whole output rows), one pass" % (sample_m, M)}
+
+    decode_cfg("single_4x512x512", ((512, 512),), 4, 9000, one_thread=True, budget=0.5)
+    shapes_2b = [(l.K, l.N) for l in workloads.DECODE_2B.linears]
+    decode_cfg("decode_gemv_2b_m1", shapes_2b, 1, 9100, outliers=True, one_thread=True)
+    if "terns" in stash:
+        x0s = stash["x0"]
+        for M, one in ((1, True), (8, False)):
+            r, e = time_reps(lambda: oracle_chain(stash["terns"], x0s[M], THREADS), 1.0)
+            row = {"tok_s": round(M * r / e, 2), "us_per_step": round(e / r * 1e6, 1),
+                   "sample": "%d steps of the %d-layer chain, M=%d, in %.2f s" % (r, len(stash["terns"]), M, e)}
+            if one:
+                r1, e1 = time_reps(lambda: oracle_chain(stash["terns"], x0s[M], 1), 1.0)
+                row["tok_s_1thread"] = round(M * r1 / e1, 3)
+                row["us_per_step_1thread"] = round(e1 / r1 * 1e6, 1)
+            cfg["decode_step_2b_30l_m%d" % M] = row
+    prefill_cfg("prefill_2b_m2048", shapes_2b, 2048, 256, 9200)
+    codes_100b = [(t, b) for t, b, _ in head_prepared]
+    for M in (8, 32):
+        decode_cfg("decode_100b_m%d" % M, workloads.SHAPES_100B, M, 9300, codes=codes_100b)
+    prefill_cfg("prefill_100b_m512", workloads.SHAPES_100B, 512, 64, 9400, codes=codes_100b)
+    res["configs"] = cfg
+    return res
 
 
 # ------------------------------------------------------------------- extras
@@ -533,26 +680,24 @@ def decode_extra(shapes, Ms, dev, steps=100):
     res = {}
     packs = [gpu_weights(N, K, 100 + i, dev) for i, (K, N) in enumerate(shapes)]
     per_step = sum(N * K // 4 for K, N in shapes)
-    R = rotation(per_step)
-    copies = [copies_of(p, R) for p, _ in packs]
+    copies = [copies_of(p, rotation(N * K // 4)) for (p, _), (K, N) in zip(packs, shapes)]
     for M in Ms:
         lins = [Linear(M, K, N, copies[i], packs[i][1], gpu_acts(M, K, 200 + i, dev))
                 for i, (K, N) in enumerate(shapes)]
-        g = capture_steps(lins, steps)
-        time_graph(g)
-        el, _ = time_graph(g)
+        el, _ = timed(lambda: [L.step() for L in lins], steps, steps // 4)
         durs = [kernel_duration(L, 100) for L in lins]
         res["M%d" % M] = {"mode": lins[0].mode, "GB_s": round(per_step * steps / el / 1e9, 1),
                           "gemv_GB_s": round(sum(L.traffic_bytes() for L in lins) / sum(durs) / 1e9, 1),
                           "us_per_step": round(el / steps * 1e6, 2),
+                          "kernel_us": [round(d * 1e6, 2) for d in durs],
                           "frac_hbm": round(sum(L.traffic_bytes() for L in lins) / sum(durs) / 1e9 / HBM_PEAK_GBS, 4)}
-        del lins, g
+        del lins
     del copies, packs
     torch.cuda.empty_cache()
     return res
 
 
-def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
+def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS, stash=None):
     """One decode step over all BitLinears of the 30-layer stack, for each batch in Ms.
 
     Latent weights are drawn on the device (torch generator, one seed per
@@ -560,14 +705,15 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
     chain layer by layer from the same bf16 input tokens; after one eager step
     the GPU's residual stream must equal the oracle's bit for bit.  A timed
     step restarts from the input tokens (a 10 KB device copy) and runs the
-    210 BitLinears with their glue; `steps` of them form one HIP graph."""
+    210 BitLinears with their glue; `steps` of them form one HIP graph.  The
+    oracle's codes and input tokens are left in `stash` for its timing."""
     import oracle
     from bitlinear_matmul_02_amd.decoder import DecoderStack, PackedLinear
     threads = min(16, os.cpu_count() or 1)
     x0 = {M: workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, workloads.D_MODEL, workloads.DECODER_X0_SEED))
           for M in Ms}
     xr = dict(x0)
-    layers, wbytes = [], 0
+    layers, wbytes, terns = [], 0, []
     for l in range(n_layers):
         L, lat = {}, {}
         for j, (name, K, N) in enumerate(workloads.LAYER_SHAPES):
@@ -596,7 +742,10 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
             x = oracle.add_f32(x, lin(oracle.relu2_mul(lin(xn, "gate"), lin(xn, "up")), "down"))
             xr[M] = x
         layers.append(L)
-        del tern
+        terns.append(tern)
+    if stash is not None:
+        stash["terns"], stash["x0"] = terns, x0
+    del terns
     res = {"layers": n_layers, "bitlinears": 7 * n_layers, "weight_bytes": wbytes}
     for M in Ms:
         stack = DecoderStack(layers, M, dev)
@@ -610,19 +759,17 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS):
         if not np.all(np.isfinite(xr[M])) or not (exact or rel <= 1e-3):
             raise RuntimeError("decode step M=%d differs from the oracle (max rel %.3g)" % (M, rel))
 
-        def one(i):
+        def one():
             x.copy_(src)
             stack.step(x)
-        g = capture(one, steps)
-        time_graph(g)
-        el, _ = time_graph(g)
+        el, _ = timed(one, steps, max(steps // 5, 1))
         t = el / steps
         res["M%d" % M] = {"tok_s": round(M / t, 1), "us_per_step": round(t * 1e6, 1),
                           "weight_GB_s": round(wbytes / t / 1e9, 1),
                           "frac_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
                           "path": "fused" if stack.fused else "quant_act + gemv",
                           "oracle_match": "bit-exact" if exact else "rel %.2g" % rel}
-        del g, stack, x, src
+        del stack, x, src
     del layers
     torch.cuda.empty_cache()
     return res
@@ -645,8 +792,8 @@ def decode_fmt_extra(fmt, shapes, Ms, dev, steps=100):
         del w
     per_step = sum(p.numel() for p, _ in packs)
     weights = sum(N * K for K, N in shapes)
-    R = rotation(per_step)
-    copies = [copies_of(p, R) for p, _ in packs]
+    copies = [copies_of(p, rotation(p.numel())) for p, _ in packs]
+    ctr = [0] * len(shapes)  # per-matrix copy counters, running on across graphs
     for M in Ms:
         bufs = []
         for i, (K, N) in enumerate(shapes):
@@ -656,24 +803,20 @@ def decode_fmt_extra(fmt, shapes, Ms, dev, steps=100):
                          torch.empty((M,), dtype=torch.int32, device=dev),
                          torch.empty((M, N), dtype=torch.float32, device=dev)))
 
-        def step(r, quant=True):
-            for (K, N), (x, xq, xds, rs, y), c, (_, beta) in zip(shapes, bufs, copies, packs):
+        def step(quant=True):
+            for i, ((K, N), (x, xq, xds, rs, y), c, (_, beta)) in enumerate(zip(shapes, bufs, copies, packs)):
                 if quant:
                     bl.bitlinear_quant_act(x, xq, xds, rs)
-                gemv_fn(xq, xds, rs, K, c[r % R], beta, N, y)
-        g = capture(step, steps)
-        time_graph(g)
-        el, _ = time_graph(g)
-        step(0)
-        gk = capture(lambda r: step(r, quant=False), steps)
-        time_graph(gk)
-        elk, _ = time_graph(gk)
+                gemv_fn(xq, xds, rs, K, c[ctr[i] % len(c)], beta, N, y)
+                ctr[i] += 1
+        el, _ = timed(step, steps, steps // 4)
+        elk, _ = timed(lambda: step(quant=False), steps, steps // 4)
         res["M%d" % M] = {"GB_s": round(per_step * steps / el / 1e9, 1),
                           "gemv_GB_s": round(per_step * steps / elk / 1e9, 1),
                           "us_per_step": round(el / steps * 1e6, 2),
                           "weights_per_s_T": round(weights * steps / el / 1e12, 3),
                           "frac_hbm_gemv": round(per_step * steps / elk / 1e9 / HBM_PEAK_GBS, 4)}
-        del g, gk, bufs
+        del bufs
     del copies, packs
     torch.cuda.empty_cache()
     return res
@@ -692,19 +835,16 @@ def train_extra(M, shapes, dev, reps=10):
         y = torch.empty((M, N), device=dev)
         dx = torch.empty((M, K), device=dev)
         dw = torch.empty((N, K), device=dev)
-        ops = {"forward": lambda r: bl.bitlinear_train_forward(x, packed, beta, N, y),
-               "backward_input": lambda r: bl.bitlinear_train_backward_input(dy, packed, beta, K, dx),
-               "backward_weight": lambda r: bl.bitlinear_train_backward_weight(dy, x, dw)}
+        ops = {"forward": lambda: bl.bitlinear_train_forward(x, packed, beta, N, y),
+               "backward_input": lambda: bl.bitlinear_train_backward_input(dy, packed, beta, K, dx),
+               "backward_weight": lambda: bl.bitlinear_train_backward_weight(dy, x, dw)}
         flop = 2.0 * M * N * K
         row = {}
         for name, fn in ops.items():
-            g = capture(fn, reps)
-            time_graph(g)
-            el, _ = time_graph(g)
+            el, _ = timed(fn, reps, reps)
             d = el / reps
             row[name] = {"us": round(d * 1e6, 1), "TFLOPS": round(flop / d / 1e12, 1),
                          "frac_mfma_bf16": round(flop / d / 1e12 / BF16_PEAK_TFLOPS, 4)}
-            del g
         res["%dx%d->%d" % (M, K, N)] = row
         del packed, x, dy, y, dx, dw
         torch.cuda.empty_cache()
@@ -721,14 +861,12 @@ def prefill_b1_extra(M, shapes, dev, reps=20):
         del w
         x_q, x_ds, rs = bl.quant_act(gpu_acts(M, K, 800 + i, dev), with_rowsum=True)
         y = torch.empty((M, N), dtype=torch.float32, device=dev)
-        g2 = capture(lambda r: bl.bitlinear_gemm_b1(x_q, x_ds, rs, K, packed, beta, N, y), reps)
-        time_graph(g2)
-        el, _ = time_graph(g2)
+        el, _ = timed(lambda: bl.bitlinear_gemm_b1(x_q, x_ds, rs, K, packed, beta, N, y), reps, reps)
         d = el / reps
         tops = 2.0 * M * N * K / d / 1e12
         res["%dx%d->%d" % (M, K, N)] = {"gemm_us": round(d * 1e6, 1), "TOPS": round(tops, 1),
                                         "frac_mfma": round(tops / INT8_PEAK_TOPS, 4)}
-        del packed, x_q, y, g2
+        del packed, x_q, y
         torch.cuda.empty_cache()
     return res
 
@@ -739,20 +877,17 @@ def prefill_extra(M, shapes, dev, reps=20):
         packed, beta = gpu_weights(N, K, 300 + i, dev)
         L = Linear(M, K, N, [packed], beta, gpu_acts(M, K, 400 + i, dev))
         L.quant()
-        L.run_product(0)
+        L.run_product()
         torch.cuda.synchronize()
         d = kernel_duration(L, reps)
         # the quantizer alone, as a graph of back-to-back launches (no host
         # launch cost inside the timing)
         nq = 100
-        gq = capture(lambda i: L.quant(), nq)
-        time_graph(gq)
-        elq, _ = time_graph(gq)
+        elq, _ = timed(L.quant, nq, nq // 4)
         tops = 2.0 * M * N * K / d / 1e12
         res["%dx%d->%d" % (M, K, N)] = {"gemm_us": round(d * 1e6, 1), "TOPS": round(tops, 1),
                                         "frac_mfma": round(tops / INT8_PEAK_TOPS, 4),
                                         "quant_us": round(elq / nq * 1e6, 2)}
-        del gq
         del L, packed
         torch.cuda.empty_cache()
     return res
@@ -785,7 +920,8 @@ def main():
 
     global CLOCKS
     CLOCKS = ClockSampler()
-    head, host, wl = headline(args, dev)
+    wl = HEADLINE
+    head, head_prepared = decode_workload(wl, args, dev)
     result = {
         "metric": "ternary GEMV HBM GB/s + decode tok/s; prefill int8 TOPS; % of roofline",
         "value": round(head["value"], 2),
@@ -799,17 +935,22 @@ def main():
         "vs_baseline": None,
         "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": wl.name, "shapes": ["1x2560->6912", "1x6912->2560"],
+        "config": {"workload": wl.name,
+                   "shapes": ["%dx%d->%d" % (l.M, l.K, l.N) for l in wl.linears],
                    "step": "per BitLinear: absmax int8 quantization + ternary product + dequant (fp32 out), "
-                           "one fused launch",
-                   "rotation_copies": head["rotation_copies"], "parallelism": "none (1 GPU)"},
+                           + ("one fused launch" if head["mode"] == "fused" else "quantizer + product launches"),
+                   "rotation_copies": head["rotation_copies"],
+                   "rotation_bytes_per_shape": head["rotation_bytes_per_shape"],
+                   "parallelism": "none (1 GPU)"},
         "roofline": head["roofline"],
         "kernel_us": head["kernel_us"],
         "unfused_us_per_step": head["unfused_us_per_step"],
     }
     shapes_2b = [(l.K, l.N) for l in workloads.DECODE_2B.linears]
+    stash = {}
     extras = {
-        "decode_step_2b_30l": lambda: decode_step(workloads.DECODE_STEP_BATCHES, dev),
+        "decode_gemv_2b_m1": lambda: decode_workload(workloads.DECODE_2B, args, dev, roofline=False)[0],
+        "decode_step_2b_30l": lambda: decode_step(workloads.DECODE_STEP_BATCHES, dev, stash=stash),
         "decode_100b": lambda: decode_extra(workloads.SHAPES_100B, (1, 8, 32), dev),
         "decode_b1_2b": lambda: decode_fmt_extra("b1", shapes_2b, (1, 8), dev),
         "decode_b1_100b": lambda: decode_fmt_extra("b1", workloads.SHAPES_100B, (1, 8), dev),
@@ -830,13 +971,16 @@ def main():
     else:
         chosen = [] if args.quick else list(extras)
     if chosen:
-        result["also"] = {name: extras[name]() for name in chosen}
+        result["also"] = {}
+        for name in chosen:
+            result["also"][name] = extras[name]()
+            print("bench: %s done" % name, file=sys.stderr, flush=True)
     result["clocks"] = CLOCKS.summary()
     # The oracle runs last: its host threads can keep the cores busy for a
     # while after it returns, which would delay the graph launches between
     # the timing events of the GPU measurements.
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(host, wl)
+        result["cpu_baseline"] = cpu_baseline(head_prepared, stash)
     print(json.dumps(result), flush=True)
 
 

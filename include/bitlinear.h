@@ -131,7 +131,10 @@ int bitlinear_gemv_read_extent(int64_t M, int64_t N, int64_t K, int format, int6
                                int64_t *w_end);
 
 /*
- * Per-token absmax activation quantization.
+ * Per-token absmax activation quantization ("Key Technologies Enabling the
+ * BitNET Family", Advanced Quantization Methodologies: 8-bit activations,
+ * absmax, per token; Hacker News Reader item 39537919: activations are int8 at
+ * inference).
  *   x        [M][K] activations, x_dtype BITLINEAR_BF16 or BITLINEAR_F32,
  *            optionally | BITLINEAR_X_RMSNORM;
  *            needs only element alignment (2 or 4 bytes).
@@ -147,7 +150,10 @@ int bitlinear_quant_act(const void *x, int x_dtype, int64_t M, int64_t K, int8_t
                         float *x_ds, int32_t *x_rowsum, void *stream);
 
 /*
- * Absmean ternarization and 2-bit packing of latent fp32 weights.
+ * Absmean ternarization and 2-bit packing of latent fp32 weights ("BitNet /
+ * Ternary / Binary - Les LLMs 1-bit", Apercu de l'entrainement d'un BitLinear:
+ * beta = mean |w|, clamp(round(w / (beta + 1e-8)), -1, 1); "BitNet Technical
+ * Notes", Appendix glossary: 2 bits per ternary weight).
  *   w         [N][K] fp32 latent weights (4-byte aligned).
  *   packed    bitlinear_packed_bytes(N, K) bytes out, the tiled 2-bit format:
  *             tile (nb, kb) of 16 rows x 256 columns is 1024 bytes at byte
@@ -168,7 +174,11 @@ int bitlinear_pack_weights(const float *w, int64_t N, int64_t K, void *packed, f
                            void *workspace, void *stream);
 
 /*
- * Ternary matrix product with dequantization, for few tokens (decode).
+ * Ternary matrix product with dequantization, for few tokens (decode): every
+ * weight adds, subtracts or skips one int8 activation ("BitNet / Ternary /
+ * Binary - Les LLMs 1-bit", TL;DR; Hacker News Reader item 39537919, the reply
+ * on summing activations with weight +1 minus those with weight -1), the int32
+ * sum rescaled by both quantizer scales.
  *   x_q, x_ds  output of bitlinear_quant_act for M tokens and K inputs.
  *   packed, w_beta  output of bitlinear_pack_weights for N x K weights.
  *   y          [M][N] out, y_dtype BITLINEAR_F32 (y = acc * (ds * beta) in
@@ -188,7 +198,9 @@ int bitlinear_gemv(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, c
 
 /*
  * The same product for any number of tokens (prefill), on the int8 matrix
- * cores.  Arguments as bitlinear_gemv; M in [0, BITLINEAR_MAX_M].
+ * cores (same passages as bitlinear_gemv: at many tokens the add / subtract /
+ * skip sum is a dense contraction).  Arguments as bitlinear_gemv; M in
+ * [0, BITLINEAR_MAX_M].
  */
 int bitlinear_gemm(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, const void *packed,
                    const float *w_beta, int64_t N, void *y, int y_dtype, void *workspace,

@@ -101,5 +101,10 @@ PREFILL_2B = Workload("prefill_gemm_2b_m2048", (Linear(2048, 2560, 6912), Linear
 SHAPES_100B = ((8192, 28672), (28672, 8192))
 
 
+# Decode GEMV at batch 1 on the 100B-class shapes (the largest configuration
+# that fits one GPU), activations bf16 N(0, 1).
+DECODE_100B = Workload("decode_gemv_100b_m1", tuple(Linear(1, K, N) for K, N in SHAPES_100B))
+
+
 def workload_100b(M: int) -> Workload:
     return Workload("shapes_100b_m%d" % M, tuple(Linear(M, K, N) for K, N in SHAPES_100B))
