@@ -767,7 +767,8 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS, stash=None):
         res["M%d" % M] = {"tok_s": round(M / t, 1), "us_per_step": round(t * 1e6, 1),
                           "weight_GB_s": round(wbytes / t / 1e9, 1),
                           "frac_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
-                          "path": "fused" if stack.fused else "quant_act + gemv",
+                          "path": "fused" if stack.fused else ("requantizing GEMV epilogues" if stack.requant
+                                                               else "quant_act + gemm"),
                           "oracle_match": "bit-exact" if exact else "rel %.2g" % rel}
         del stack, x, src
     del layers

@@ -58,6 +58,7 @@ EXPORTS = (
     "bitlinear_gemv_b1", "bitlinear_gemm_b1", "bitlinear_packed_bytes_b3", "bitlinear_pack_weights_b3",
     "bitlinear_gemv_b3", "bitlinear_train_forward", "bitlinear_train_backward_input",
     "bitlinear_train_backward_weight", "bitlinear_gemv_read_extent", "bitlinear_gemv_noalloc",
+    "bitlinear_decode_rq",
 )
 MULTI_MAX = 4
 DECODE_MAX_ACT_BYTES = 58368
@@ -136,6 +137,8 @@ def lib() -> ctypes.CDLL:
     L.bitlinear_gemv_glu.argtypes = [p, p, i64, i64, p, p, p, p, i64, p, p]
     L.bitlinear_forward_decode_glu.restype = i32
     L.bitlinear_forward_decode_glu.argtypes = [p, i32, i64, i64, p, p, p, p, i64, p, p]
+    L.bitlinear_decode_rq.restype = i32
+    L.bitlinear_decode_rq.argtypes = [p, p, i64, i64, i32, i32, p, p, p, p, i32, p, p, i32, p, sz, p]
     L.bitlinear_gemv_noalloc.restype = i32
     L.bitlinear_gemv_noalloc.argtypes = [p, p, i64, i64, p, p, i64, p, i32, p]
     L.bitlinear_gemv_read_extent.restype = i32
@@ -371,6 +374,31 @@ def bitlinear_forward_decode_glu(x, packed_gate, beta_gate, packed_up, beta_up, 
     _check(lib().bitlinear_forward_decode_glu(_ptr(x), _xdtype(x, rmsnorm), M, K, _ptr(packed_gate),
                                               _ptr(beta_gate), _ptr(packed_up), _ptr(beta_up), N, _ptr(h),
                                               _stream(stream)))
+
+
+def bitlinear_decode_rq(x_q, x_ds, K, packed, w_beta, N, y, next_q, next_ds, workspace, stream=None,
+                        accumulate: bool = False, glu: bool = False, next_rmsnorm: bool = False) -> None:
+    """Products of bitlinear_gemv_multi (or the gated pair when ``glu``: packed = [gate, up],
+    y = [h]) whose last workgroup quantizes y[0] (or h) into next_q / next_ds for the next
+    BitLinear (RMS-normalized first with ``next_rmsnorm``)."""
+    count = len(packed)
+    P = ctypes.c_void_p * count
+    Bp = ctypes.c_void_p * count
+    Np = ctypes.c_int64 * count
+    ys = list(y)
+    if glu:
+        assert count == 2 and len(ys) == 1
+        Ns = [N, N] if isinstance(N, int) else list(N)
+        ys = [ys[0], ys[0]]
+    else:
+        Ns = list(N)
+    Y = ctypes.c_void_p * count
+    ydt = _ydtype(ys[0], accumulate)
+    _check(lib().bitlinear_decode_rq(_ptr(x_q), _ptr(x_ds), x_ds.shape[0], K, count, int(glu),
+                                     P(*[t.data_ptr() for t in packed]), Bp(*[t.data_ptr() for t in w_beta]),
+                                     Np(*Ns), Y(*[t.data_ptr() for t in ys]), ydt, _ptr(next_q), _ptr(next_ds),
+                                     X_RMSNORM if next_rmsnorm else 0, _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def bitlinear_relu2_mul(g, u, h, stream=None) -> None:

@@ -356,6 +356,38 @@ int bitlinear_forward_decode_multi(const void* x, int x_dtype, int64_t M, int64_
                     fn);
 }
 
+int bitlinear_decode_rq(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, int count, int glu,
+                        const void* const* packed, const float* const* w_beta, const int64_t* N, void* const* y,
+                        int y_dtype, int8_t* next_q, float* next_ds, int next_flags, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  const char* fn = "bitlinear_decode_rq";
+  if (glu != 0 && glu != 1) return fail(BITLINEAR_ERR_ARG, "%s: glu must be 0 or 1", fn);
+  if (glu && count != 2) return fail(BITLINEAR_ERR_ARG, "%s: a gated pair has count 2", fn);
+  if (next_flags != 0 && next_flags != BITLINEAR_X_RMSNORM)
+    return fail(BITLINEAR_ERR_ARG, "%s: next_flags must be 0 or BITLINEAR_X_RMSNORM", fn);
+  if (!glu && y_dtype != BITLINEAR_F32 && y_dtype != BITLINEAR_F32_ADD)
+    return fail(BITLINEAR_ERR_ARG, "%s: the requantized output must be fp32 (BITLINEAR_F32 or BITLINEAR_F32_ADD)", fn);
+  void* hy[2] = {nullptr, nullptr};
+  if (glu) {
+    if (!y || !y[0]) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+    hy[0] = hy[1] = y[0];
+  }
+  int st = check_multi(fn, M, K, count, packed, w_beta, N, glu ? hy : y, glu ? BITLINEAR_F32 : y_dtype);
+  if (st == BITLINEAR_OK && glu && N[0] != N[1]) st = fail(BITLINEAR_ERR_SHAPE, "%s: gate and up differ in N", fn);
+  if (st == BITLINEAR_OK) st = check_q(fn, x_q, x_ds, M);
+  if (st != BITLINEAR_OK) return st;
+  if (M == 0) return ok();
+  if (!next_q || !next_ds || !workspace) return fail(BITLINEAR_ERR_ARG, "%s: null pointer argument", fn);
+  if (!aligned(next_q, 16) || !aligned(next_ds, 4) || !aligned(workspace, 16) || !aligned(y[0], 16))
+    return fail(BITLINEAR_ERR_ALIGN, "%s: next_q, workspace and y[0] must be 16-byte aligned, next_ds 4-byte", fn);
+  if (workspace_bytes < 16) return fail(BITLINEAR_ERR_ARG, "%s: workspace of %zu bytes, 16 needed", fn, workspace_bytes);
+  return hip_status(bl::launch_decode_rq(x_q, act_stride(K), x_ds, M, K, count, as_bytes(packed), w_beta, N,
+                                         glu ? hy : y, glu ? BITLINEAR_F32 : y_dtype, glu != 0, next_q,
+                                         act_stride(N[0]), next_ds, next_flags != 0, workspace,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int bitlinear_gemv_glu(const int8_t* x_q, const float* x_ds, int64_t M, int64_t K, const void* packed_gate,
                        const float* beta_gate, const void* packed_up, const float* beta_up, int64_t N, float* h,
                        void* stream) {

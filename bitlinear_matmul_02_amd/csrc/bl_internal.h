@@ -57,6 +57,15 @@ hipError_t noalloc_scratch(hipStream_t s, void** ptr);
 // After a failed launch that used the array: clear it before its next use.
 void noalloc_mark_dirty();
 
+// Decode product of 1-4 BitLinears sharing int8 inputs (or a gated pair)
+// whose last workgroup requantizes output 0 (or h) for the next BitLinear:
+// as launch_gemv_multi followed by launch_quant_act of y[0] (fp32 rows).
+// `ws` holds a zeroed 4-byte arrival counter, left zero.
+hipError_t launch_decode_rq(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, int count,
+                            const uint8_t* const* packed, const float* const* beta, const int64_t* N, void* const* y,
+                            int y_dtype, bool glu, int8_t* next_q, int64_t next_ldq, float* next_ds, bool next_norm,
+                            void* ws, hipStream_t s);
+
 // Fused decode: per-token quantization of x inside the product kernel.
 bool decode_fused_fits(int64_t M, int64_t K);
 hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
@@ -221,6 +230,73 @@ __device__ inline void store_out_t(void* y, int64_t idx, int acc64, float scale)
     else
       static_cast<uint16_t*>(y)[idx] = f32_to_bf16_rne(v);
   }
+}
+
+// ---------------------------------------------------- row requantization
+// Per-token absmax quantization of one fp32 row of K values by one wave, with
+// the standalone quantizer's arithmetic ("Key Technologies Enabling the BitNET
+// Family", Advanced Quantization Methodologies): gamma = max |x| on the
+// sign-cleared bit patterns (exact in any order); with `norm` the row is
+// RMS-normalized first (S = sum x^2 in fp64, each square exact, summed per
+// lane in index order then across the wave by a fixed butterfly;
+// r = 1 / sqrt((float)(S / K) + 1e-5); the quantizer sees fl(x * r), whose
+// maximum is fl(gamma * r)); g = max(gamma, 1e-5), q = rint(fl(x * (127 / g)))
+// by the 1.5 * 2^23 magic add (|x * qs| <= 127 (1 + 2^-23), so no clamp acts),
+// padding columns [K, ldq) written 0, ds = g / 127.  Rows whose length is a
+// multiple of 4 and 16-byte aligned are read as 16-byte pieces (two passes:
+// statistics, then codes), others element by element.
+__device__ inline uint32_t rq_qbyte(float x, float qs) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(x, qs), 12582912.0f)) & 0xffu;
+}
+
+__device__ inline void wave_quant_row_f32(const float* x, int K, bool norm, int8_t* q, int64_t ldq, float* ds) {
+  const int lane = threadIdx.x & 63;
+  const bool vec = (K % 4 == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0);
+  const int n4 = vec ? K / 4 : 0;
+  const float4* x4 = reinterpret_cast<const float4*>(x);
+  uint32_t amax = 0;
+  double s2 = 0.0;
+#pragma unroll 8
+  for (int i = lane; i < n4; i += 64) {
+    const float4 v = x4[i];
+    amax = max(max(amax, __float_as_uint(v.x) & 0x7fffffffu), __float_as_uint(v.y) & 0x7fffffffu);
+    amax = max(max(amax, __float_as_uint(v.z) & 0x7fffffffu), __float_as_uint(v.w) & 0x7fffffffu);
+    if (norm) {
+      s2 += (double)v.x * (double)v.x;
+      s2 += (double)v.y * (double)v.y;
+      s2 += (double)v.z * (double)v.z;
+      s2 += (double)v.w * (double)v.w;
+    }
+  }
+  for (int k = 4 * n4 + lane; k < K; k += 64) {  // element path (rows that are not 16-byte pieces)
+    const float v = x[k];
+    amax = max(amax, __float_as_uint(v) & 0x7fffffffu);
+    if (norm) s2 += (double)v * (double)v;
+  }
+  amax = wave_max_u32(amax);
+  float gamma = __uint_as_float(amax), rn = 1.0f;
+  if (norm) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+    rn = 1.0f / sqrtf((float)(s2 / (double)K) + 1e-5f);
+    gamma = __fmul_rn(gamma, rn);
+  }
+  const float g = fmaxf(gamma, 1e-5f);
+  const float qs = 127.0f / g;  // IEEE division
+  auto code = [&](float v) { return rq_qbyte(norm ? __fmul_rn(v, rn) : v, qs); };
+#pragma unroll 8
+  for (int i = lane; i < n4; i += 64) {
+    const float4 v = x4[i];
+    *reinterpret_cast<uint32_t*>(q + 4 * (int64_t)i) = code(v.x) | (code(v.y) << 8) | (code(v.z) << 16) | (code(v.w) << 24);
+  }
+  for (int64_t k = 4 * (int64_t)n4 + 4 * lane; k < ldq; k += 256) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k + j < K) w |= code(x[k + j]) << (8 * j);
+    *reinterpret_cast<uint32_t*>(q + k) = w;
+  }
+  if (lane == 0) *ds = g / 127.0f;
 }
 
 }  // namespace bl

@@ -206,7 +206,42 @@ struct GemvArgs {
   int y_dtype;
   int32_t* ws_acc;
   uint32_t* ws_cnt;
+  // requantization of output 0 (or h) for the next BitLinear by the last
+  // workgroup to finish (RQ instantiations only)
+  const float* rq_src;  // fp32 rows [M][rq_k]
+  int rq_k, rq_norm;
+  int8_t* rq_q;         // [M][rq_ldq]
+  int64_t rq_ldq;
+  float* rq_ds;         // [M]
+  uint32_t* rq_cnt;     // arrival counter, zero on entry and on return
 };
+
+// Tail of a requantizing launch, reached by every wave of every workgroup
+// after its output stores: each wave waits for its own stores, then one
+// thread releases the workgroup's outputs at agent scope and counts its
+// arrival; the last workgroup to arrive acquires everyone's outputs and
+// quantizes rows m < M of rq_src (optionally RMS-normalized) into
+// rq_q / rq_ds, one row per wave, then resets the counter.  No workgroup
+// waits for another.
+__device__ void rq_tail(const GemvArgs& a) {
+  __shared__ uint32_t last;
+  const int wave = threadIdx.x >> 6, waves = blockDim.x >> 6;
+  // The outputs were written with agent-coherent stores (written through the
+  // compute die's L2); waiting for their completion makes them visible to
+  // every die before the arrival is counted, without an L2 writeback.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    last = __hip_atomic_fetch_add(a.rq_cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1;
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale lines of this die's caches
+  }
+  __syncthreads();
+  if (!last) return;
+  for (int m = wave; m < a.M; m += waves)
+    wave_quant_row_f32(a.rq_src + (int64_t)m * a.rq_k, a.rq_k, a.rq_norm != 0, a.rq_q + (int64_t)m * a.rq_ldq,
+                       a.rq_ldq, a.rq_ds + m);
+  if (threadIdx.x == 0) __hip_atomic_store(a.rq_cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // a.seg[si] for a uniform si, field by field through selects over the fixed
 // offsets of every segment
@@ -604,7 +639,7 @@ __host__ __device__ inline int64_t act_col(int kt, int i, int g4, int KT, int64_
   return clamp && c > row_bytes - 16 ? row_bytes - 16 : c;
 }
 
-template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT)>
+template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT), bool RQ = false>
 __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int KT = tile_cols(FMT), NS = KT / 64;  // columns and MFMA steps per k-tile
   constexpr int E = MB * NB * 4;  // accumulator values per lane
@@ -773,7 +808,10 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
 #pragma unroll
         for (int r = 0; r < 4; ++r) atomicAdd(&red[(mb * NB + j) * 4 + r][lane], acc[mb][j][r]);
     __syncthreads();
-    if (wave != 0) return;
+    if (wave != 0) {
+      if constexpr (RQ) rq_tail(a);
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -836,8 +874,13 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
         const float yg = (float)(acc[mb][0][r] >> 6) * (dsm * bg);
         const float yu = (float)(acc[mb][NB - 1][r] >> 6) * (dsm * bu);
         const float rg = yg > 0.0f ? yg : 0.0f;
-        static_cast<float*>(sg.y)[(int64_t)m * sg.N + n] = __fmul_rn(__fmul_rn(rg, rg), yu);
+        float* dst = static_cast<float*>(sg.y) + (int64_t)m * sg.N + n;
+        if constexpr (RQ)
+          __hip_atomic_store(dst, __fmul_rn(__fmul_rn(rg, rg), yu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *dst = __fmul_rn(__fmul_rn(rg, rg), yu);
       }
+    if constexpr (RQ) rq_tail(a);
     return;
   }
   const float bt = *sg.beta;
@@ -891,7 +934,17 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
             // sum q * c - rowsum; both scaled as the T2 sums (64 t)
             const int v = FMT == 1 ? (2 * acc[mb][j][r] - rsv[mb][r]) * 64
                                    : (FMT == 2 ? (acc[mb][j][r] - rsv[mb][r]) * 64 : acc[mb][j][r]);
-            if (n < sg.N) store_out_t<YD>(sg.y, (int64_t)m * sg.N + n, v, scale[mb][r]);
+            if (n < sg.N) {
+              if constexpr (RQ && (YD == BITLINEAR_F32 || YD == BITLINEAR_F32_ADD)) {
+                // agent-coherent store: the last workgroup requantizes these rows
+                float* dst = static_cast<float*>(sg.y) + (int64_t)m * sg.N + n;
+                float val = (float)(v >> 6) * scale[mb][r];
+                if constexpr (YD == BITLINEAR_F32_ADD) val = __fadd_rn(*dst, val);
+                __hip_atomic_store(dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              } else {
+                store_out_t<YD>(sg.y, (int64_t)m * sg.N + n, v, scale[mb][r]);
+              }
+            }
           }
         }
     };
@@ -902,27 +955,29 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
       default: emit(std::integral_constant<int, BITLINEAR_BF16>{}); break;
     }
   }
+  if constexpr (RQ) rq_tail(a);
 }
 
-template <int MB, int NB, int AM, bool NORM, int FMT = 0>
+template <int MB, int NB, int AM, bool NORM, int FMT = 0, bool RQ = false>
 hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
+  constexpr int KU = ring_depth(MB, NB, AM, FMT);
   if constexpr (AM != AGLOBAL) {
     // static LDS plus the largest activation rows can pass the default 64 KB
     // per workgroup: raise the limit (once per device)
     static LdsLimit lim;
-    const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT>),
-                                             (int)kDecodeLdsBytes);
+    const hipError_t attr = ensure_lds_limit(
+        lim, reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT, KU, RQ>), (int)kDecodeLdsBytes);
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM, FMT>), dim3((unsigned)(p.Ng * p.SB)), dim3(64 * p.waves),
-                     (size_t)p.lds_bytes, s, a);
+  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM, FMT, KU, RQ>), dim3((unsigned)(p.Ng * p.SB)),
+                     dim3(64 * p.waves), (size_t)p.lds_bytes, s, a);
   return hipGetLastError();
 }
 
-template <int AM, bool NORM = false, int FMT = 0>
+template <int AM, bool NORM = false, int FMT = 0, bool RQ = false>
 hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
 #define BL_GEMV_CASE(mb, nb) \
-  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM, NORM, FMT>(p, a, s)
+  if (p.MB == mb && p.NB == nb) return launch_t<mb, nb, AM, NORM, FMT, RQ>(p, a, s)
   // the (MB, NB) pairs make_plan can produce for this mode
   BL_GEMV_CASE(1, 1);
   BL_GEMV_CASE(1, 2);
@@ -932,7 +987,7 @@ hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   BL_GEMV_CASE(4, 1);
   BL_GEMV_CASE(3, 2);  // AGLOBAL, and gated pairs in every mode
   BL_GEMV_CASE(4, 2);
-  if constexpr (AM == AGLOBAL && FMT == 0) BL_GEMV_CASE(2, 4);
+  if constexpr (AM == AGLOBAL && FMT == 0 && !RQ) BL_GEMV_CASE(2, 4);
 #undef BL_GEMV_CASE
   return hipErrorInvalidValue;
 }
@@ -1029,6 +1084,39 @@ hipError_t launch_decode_multi(const void* x, int x_dtype, int64_t M, int64_t K,
     return hipErrorInvalidValue;
   set_x(a, x, x_dtype, K);
   return dispatch(p, a, s);
+}
+
+hipError_t launch_decode_rq(const int8_t* q, int64_t ldq, const float* ds, int64_t M, int64_t K, int count,
+                            const uint8_t* const* packed, const float* const* beta, const int64_t* N, void* const* y,
+                            int y_dtype, bool glu, int8_t* next_q, int64_t next_ldq, float* next_ds, bool next_norm,
+                            void* ws, hipStream_t s) {
+  GemvPlan p;
+  GemvArgs a;
+  if (!make_multi(M, K, count, packed, beta, N, y, y_dtype, glu, false, 0, p, a)) return hipErrorInvalidValue;
+  if (p.NB > 2) {  // the requantizing instantiations cover NB <= 2
+    p.NB = 2;
+    if (!glu) {
+      int g = 0;
+      for (int i = 0; i < count; ++i) {
+        a.seg[i].g0 = g;
+        g += (int)ceil_div(a.seg[i].Nt, 2);
+      }
+      p.Ng = g;
+    }
+  }
+  a.q = q;
+  a.ldq = ldq;
+  a.ds = ds;
+  a.rq_src = static_cast<const float*>(y[0]);
+  a.rq_k = (int)N[0];
+  a.rq_norm = next_norm;
+  a.rq_q = next_q;
+  a.rq_ldq = next_ldq;
+  a.rq_ds = next_ds;
+  a.rq_cnt = static_cast<uint32_t*>(ws);
+  if (p.amode == ALDS_Q) return dispatch_mb_nb<ALDS_Q, false, 0, true>(p, a, s);
+  if (p.amode == AGLOBAL) return dispatch_mb_nb<AGLOBAL, false, 0, true>(p, a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemv_b1(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M,

@@ -26,12 +26,22 @@ most ``FUSED_MAX_M`` tokens the activation quantization (and normalization)
 runs inside each product's prologue, so a layer is four launches; beyond that
 each input is quantized once by its own launch.  Past 64 tokens the products
 run on the matrix-core GEMM, one BitLinear per launch.
+
+With ``requant=True`` (up to 64 tokens, past the fused limit) each product's
+last workgroup instead quantizes the next product's input
+(bitlinear_decode_rq: q for o, RMSNorm(x) for gate/up and for the next
+layer's q/k/v, h for down), so a layer is four launches and a step adds one
+quantizer launch for its input.  The results are the same; on MI355X it is
+slower than the separate quantizer at every batch (the last workgroup's
+reads of the finished rows run on one compute unit and wait on memory round
+trips, while the quantizer spreads the rows over as many workgroups), so it
+is not the default.
 """
 from __future__ import annotations
 
 import torch
 
-from . import (GEMV_MAX_M, act_stride, bitlinear_forward_decode, bitlinear_forward_decode_glu,
+from . import (GEMV_MAX_M, act_stride, bitlinear_decode_rq, bitlinear_forward_decode, bitlinear_forward_decode_glu,
                bitlinear_forward_decode_multi, bitlinear_gemm, bitlinear_gemv, bitlinear_gemv_glu,
                bitlinear_gemv_multi, bitlinear_quant_act, bitlinear_relu2_mul, decode_fits,
                gemm_workspace_bytes, gemv_workspace_bytes)
@@ -48,8 +58,9 @@ class PackedLinear:
 
 
 class DecoderStack:
-    def __init__(self, layers: list[dict], M: int, device):
-        """layers: one dict per layer mapping each of NAMES to a PackedLinear."""
+    def __init__(self, layers: list[dict], M: int, device, requant: bool = False):
+        """layers: one dict per layer mapping each of NAMES to a PackedLinear;
+        requant: quantize each product's output in its epilogue (see above)."""
         self.layers = layers
         self.M = M
         dev = torch.device(device)
@@ -65,12 +76,23 @@ class DecoderStack:
         self.q, self.k, self.v, self.g, self.u, self.h = z(qn), z(kn), z(vn), z(f), z(f), z(f)
         self.fused = M <= FUSED_MAX_M and all(decode_fits(M, K) for K in (d, qn, f))
         self.gemv = M <= GEMV_MAX_M
+        # requantizing epilogues: batches past the fused limit up to 64 tokens, on request
+        self.requant = requant and self.gemv and not self.fused
         if not self.fused:
             self.xq = {K: torch.zeros((M, act_stride(K)), dtype=torch.int8, device=dev) for K in {d, qn, f}}
             self.xds = {K: torch.zeros((M,), dtype=torch.float32, device=dev) for K in {d, qn, f}}
             wsf = gemv_workspace_bytes if self.gemv else gemm_workspace_bytes
             ws = max(wsf(M, L[n].N, L[n].K) for L in layers for n in NAMES)
             self.ws = torch.zeros((max(ws, 1),), dtype=torch.uint8, device=dev)
+        if self.requant:
+            # the next products' int8 inputs: x (RMS-normalized), q and h
+            self.rq_x = (torch.zeros((M, act_stride(d)), dtype=torch.int8, device=dev),
+                         torch.zeros((M,), dtype=torch.float32, device=dev))
+            self.rq_q = (torch.zeros((M, act_stride(qn)), dtype=torch.int8, device=dev),
+                         torch.zeros((M,), dtype=torch.float32, device=dev))
+            self.rq_h = (torch.zeros((M, act_stride(f)), dtype=torch.int8, device=dev),
+                         torch.zeros((M,), dtype=torch.float32, device=dev))
+            self.rq_ws = torch.zeros((256,), dtype=torch.uint8, device=dev)  # arrival counter
 
     # one BitLinear on an input already quantized into self.xq / self.xds
     def _product(self, lin: PackedLinear, y, accumulate, stream):
@@ -90,8 +112,35 @@ class DecoderStack:
         for lin, y in zip(lins, outs):
             self._product(lin, y, accumulate, stream)
 
+    def _layer_rq(self, i: int, x: torch.Tensor, stream, last: bool) -> None:
+        """Layer i with requantizing epilogues; self.rq_x holds the quantized
+        RMSNorm(x) on entry and (unless ``last``) on return."""
+        L = self.layers[i]
+        qkv = [L[n] for n in ("q", "k", "v")]
+        d, ws = self.d, self.rq_ws
+        xq, xds = self.rq_x
+        bitlinear_decode_rq(xq, xds, d, [l.packed for l in qkv], [l.beta for l in qkv], [l.N for l in qkv],
+                            [self.q, self.k, self.v], self.rq_q[0], self.rq_q[1], ws, stream)
+        o = L["o"]
+        bitlinear_decode_rq(self.rq_q[0], self.rq_q[1], o.K, [o.packed], [o.beta], [o.N], [x], xq, xds, ws, stream,
+                            accumulate=True, next_rmsnorm=True)
+        g, u = L["gate"], L["up"]
+        bitlinear_decode_rq(xq, xds, d, [g.packed, u.packed], [g.beta, u.beta], g.N, [self.h], self.rq_h[0],
+                            self.rq_h[1], ws, stream, glu=True)
+        dn = L["down"]
+        if last:
+            bitlinear_gemv(self.rq_h[0], self.rq_h[1], dn.K, dn.packed, dn.beta, dn.N, x, self.ws, stream,
+                           accumulate=True)
+        else:
+            bitlinear_decode_rq(self.rq_h[0], self.rq_h[1], dn.K, [dn.packed], [dn.beta], [dn.N], [x], xq, xds, ws,
+                                stream, accumulate=True, next_rmsnorm=True)
+
     def layer(self, i: int, x: torch.Tensor, stream=None) -> None:
         L = self.layers[i]
+        if self.requant:
+            bitlinear_quant_act(x, self.rq_x[0], self.rq_x[1], None, stream, rmsnorm=True)
+            self._layer_rq(i, x, stream, last=True)
+            return
         if not self.gemv:  # prefill-sized batches: one GEMM per BitLinear
             self._linears(x, (L["q"], L["k"], L["v"]), (self.q, self.k, self.v), False, stream, rmsnorm=True)
             self._linears(self.q, (L["o"],), (x,), True, stream)
@@ -120,5 +169,10 @@ class DecoderStack:
     def step(self, x: torch.Tensor, stream=None) -> None:
         """One decode step: x [M][d] fp32 (the residual stream) is updated in place."""
         assert x.dtype == torch.float32 and tuple(x.shape) == (self.M, self.d) and x.is_contiguous()
+        if self.requant:
+            bitlinear_quant_act(x, self.rq_x[0], self.rq_x[1], None, stream, rmsnorm=True)
+            for i in range(len(self.layers)):
+                self._layer_rq(i, x, stream, last=i == len(self.layers) - 1)
+            return
         for i in range(len(self.layers)):
             self.layer(i, x, stream)

@@ -347,6 +347,36 @@ int bitlinear_forward_decode_glu(const void *x, int x_dtype, int64_t M, int64_t 
                                  void *stream);
 
 /*
+ * Decode product with the next BitLinear's activation quantization in its
+ * epilogue ("Key Technologies Enabling the BitNET Family", Advanced
+ * Quantization Methodologies: the next layer's input is quantized per token
+ * by absmax; Architectural Innovations and Optimizations: RMSNorm before it).
+ * The same products as bitlinear_gemv_multi (glu = 0: count 1 .. 4
+ * BitLinears sharing x_q) or bitlinear_gemv_glu (glu = 1: count 2, packed[0]
+ * the gate and packed[1] the up matrix, y[0] receives h); then the last
+ * workgroup to finish quantizes the M fp32 rows of y[0] (or h), RMS-normalized
+ * first when next_flags is BITLINEAR_X_RMSNORM, into next_q
+ * [M][bitlinear_act_stride(N[0])] and next_ds [M], with the arithmetic of
+ * bitlinear_quant_act(y[0], BITLINEAR_F32 | next_flags): identical codes and
+ * scales, except that the fp64 sum of squares of the normalization is taken
+ * in another fixed order (its last bits can differ, which changes the fp32
+ * mean square only at an fp32 rounding boundary).
+ * This saves the quantizer's launch between two BitLinears of a decode step.
+ *   y_dtype    for glu = 0: BITLINEAR_F32 or BITLINEAR_F32_ADD (the residual
+ *              sum, y[0] += ...); y[0] is 16-byte aligned.
+ *   next_q     16-byte aligned, must not overlap x_q, y or h.
+ *   workspace  16 bytes, 16-byte aligned, zero before the first call; every
+ *              successful call leaves it zero (an arrival counter).  Calls
+ *              sharing a workspace must not overlap.
+ * Errors: as bitlinear_gemv_multi / bitlinear_gemv_glu, and ERR_ARG for
+ * next_flags, a non-fp32 y_dtype, or a short workspace.
+ */
+int bitlinear_decode_rq(const int8_t *x_q, const float *x_ds, int64_t M, int64_t K, int count, int glu,
+                        const void *const *packed, const float *const *w_beta, const int64_t *N,
+                        void *const *y, int y_dtype, int8_t *next_q, float *next_ds, int next_flags,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Feed-forward activation between the gate / up and down BitLinears of a
  * decoder layer ("Key Technologies Enabling the BitNET Family", Architectural
  * Innovations and Optimizations: squared ReLU in the feed-forward layers):

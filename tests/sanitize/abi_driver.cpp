@@ -140,6 +140,29 @@ int main() {
   EXPECT(bitlinear_relu2_mul(nullptr, f, 4, fo, nullptr), BITLINEAR_ERR_ARG);
   EXPECT(bitlinear_relu2_mul(f, f, 0, fo, nullptr), BITLINEAR_OK);
 
+  // products with the next BitLinear's quantization in the epilogue
+  {
+    const void* pk[2] = {p, p};
+    const float* bt[2] = {f, f};
+    int64_t ns[2] = {64, 64};
+    void* ys[2] = {p, p};
+    EXPECT(bitlinear_decode_rq(q, f, 1, 256, 1, 0, pk, bt, ns, ys, BITLINEAR_BF16, (int8_t*)p, fo, 0, p, 16, nullptr),
+           BITLINEAR_ERR_ARG);
+    EXPECT(bitlinear_decode_rq(q, f, 1, 256, 1, 1, pk, bt, ns, ys, f32, (int8_t*)p, fo, 0, p, 16, nullptr),
+           BITLINEAR_ERR_ARG);
+    EXPECT(bitlinear_decode_rq(q, f, 1, 256, 1, 0, pk, bt, ns, ys, f32, (int8_t*)p, fo, 7, p, 16, nullptr),
+           BITLINEAR_ERR_ARG);
+    EXPECT(bitlinear_decode_rq(q, f, 1, 256, 1, 0, pk, bt, ns, ys, f32, (int8_t*)p, fo, 0, p, 4, nullptr),
+           BITLINEAR_ERR_ARG);
+    EXPECT(bitlinear_decode_rq(q, f, 1, 256, 1, 0, pk, bt, ns, ys, f32, (int8_t*)odd, fo, 0, p, 16, nullptr),
+           BITLINEAR_ERR_ALIGN);
+    ns[1] = 32;
+    EXPECT(bitlinear_decode_rq(q, f, 1, 256, 2, 1, pk, bt, ns, ys, f32, (int8_t*)p, fo, 0, p, 16, nullptr),
+           BITLINEAR_ERR_SHAPE);
+    EXPECT(bitlinear_decode_rq(q, f, 0, 256, 2, 0, pk, bt, ns, ys, f32, (int8_t*)p, fo, 0, p, 16, nullptr),
+           BITLINEAR_OK);
+  }
+
   // training products
   EXPECT(bitlinear_train_forward(p, 1, 16, p, f, 0, fo, nullptr), BITLINEAR_ERR_SHAPE);
   EXPECT(bitlinear_train_backward_input(nullptr, 1, 16, p, f, 16, fo, nullptr), BITLINEAR_ERR_ARG);

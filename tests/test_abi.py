@@ -328,3 +328,25 @@ def test_noalloc_validation():
     bad = list(args)
     bad[2] = 0
     assert L.bitlinear_gemv_noalloc(*bad) == bl.OK  # empty batch: nothing enqueued
+
+
+def test_decode_rq_validation():
+    L = bl.lib()
+    p = ctypes.c_void_p(1 << 20)
+    one = (ctypes.c_void_p * 2)(1 << 20, 1 << 20)
+    n = (ctypes.c_int64 * 2)(64, 64)
+
+    def call(M=1, K=256, count=1, glu=0, y_dtype=bl.F32, flags=0, ws=p, wsb=16, nq=p):
+        return L.bitlinear_decode_rq(p, p, M, K, count, glu, one, one, n, one, y_dtype, nq, p, flags, ws, wsb, None)
+    assert call(M=0) == bl.OK  # empty batch: nothing enqueued
+    assert call(M=65) == bl.ERR_SHAPE
+    assert call(count=0) == bl.ERR_ARG
+    assert call(glu=1, count=1) == bl.ERR_ARG
+    assert call(glu=2) == bl.ERR_ARG
+    assert call(flags=3) == bl.ERR_ARG
+    assert call(y_dtype=bl.BF16) == bl.ERR_ARG
+    assert call(y_dtype=bl.I32) == bl.ERR_ARG
+    assert call(ws=None) == bl.ERR_ARG
+    assert call(wsb=8) == bl.ERR_ARG
+    assert call(nq=ctypes.c_void_p((1 << 20) + 4)) == bl.ERR_ALIGN
+    assert call(nq=None) == bl.ERR_ARG

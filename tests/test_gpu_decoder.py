@@ -179,6 +179,71 @@ def test_glu_parity(M, K, N, path):
     assert_f32_parity(h.cpu().numpy(), ref)
 
 
+# ------------------------------------------------ requantization in the producer's epilogue
+RQ_CASES = [(1, 2560, (2560, 640, 640)), (8, 2560, (2560, 640, 640)), (8, 6912, (2560,)), (8, 2560, (2560,)),
+            (3, 700, (333, 40)), (33, 512, (300, 17)), (64, 256, (64,)), (12, 8192, (1000,)), (2, 13, (21,))]
+
+
+@pytest.mark.parametrize("M,K,Ns", RQ_CASES)
+@pytest.mark.parametrize("norm,accumulate", [(False, False), (True, True), (True, False)])
+def test_decode_rq_parity(M, K, Ns, norm, accumulate):
+    """Products of 1-3 BitLinears on int8 inputs, then the last workgroup
+    quantizes output 0 (RMS-normalized when norm) for the next BitLinear: the
+    outputs, the next int8 rows and scales equal the oracle's, and the arrival
+    counter is zero again."""
+    x, xf = norm_inputs(M, K, "f32", seed=M * 7 + K)
+    ws = [workloads.gen_weights(N, K, seed=N * 5 + i) for i, N in enumerate(Ns)]
+    packs = [bl.pack_weights(torch.from_numpy(w).to(DEV)) for w in ws]
+    rng = np.random.default_rng(M + K)
+    y0 = [rng.standard_normal((M, N)).astype(np.float32) for N in Ns]
+    ys = [torch.from_numpy(v).to(DEV) for v in y0]
+    x_q, x_ds = bl.quant_act(x)
+    nq = torch.full((M, bl.act_stride(Ns[0])), 7, dtype=torch.int8, device=DEV)
+    nds = torch.zeros((M,), dtype=torch.float32, device=DEV)
+    cnt = torch.zeros((64,), dtype=torch.uint8, device=DEV)
+    for rep in range(2):  # the counter is reused: it must come back zero
+        if rep:
+            for y, v in zip(ys, y0):
+                y.copy_(torch.from_numpy(v))
+        bl.bitlinear_decode_rq(x_q, x_ds, K, [p for p, _ in packs], [b for _, b in packs], list(Ns), ys, nq, nds, cnt,
+                               accumulate=accumulate, next_rmsnorm=norm)
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(cnt)) == 0
+        outs = []
+        for w, v, y in zip(ws, y0, ys):
+            yr = oracle_acc_y(xf, w, False)[1]
+            if accumulate:
+                yr = oracle.add_f32(v, yr)
+            assert_f32_parity(y.cpu().numpy(), yr)
+            outs.append(yr)
+        q_ref, ds_ref, _ = oracle.quant_act(oracle.rmsnorm(outs[0]) if norm else outs[0])
+        got = nq.cpu().numpy()
+        np.testing.assert_array_equal(got[:, :Ns[0]], q_ref)
+        assert not got[:, Ns[0]:].any(), "padding columns must be zero"
+        np.testing.assert_array_equal(nds.cpu().numpy(), ds_ref)
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 2560, 6912), (8, 2560, 6912), (3, 700, 333), (64, 256, 48)])
+def test_decode_rq_glu_parity(M, K, N):
+    x, xf = norm_inputs(M, K, "f32", seed=M + 2 * K + N)
+    wg = workloads.gen_weights(N, K, seed=N + 21)
+    wu = workloads.gen_weights(N, K, seed=N + 22)
+    (pg, bg), (pu, bu) = (bl.pack_weights(torch.from_numpy(w).to(DEV)) for w in (wg, wu))
+    h = torch.full((M, N), 5.0, dtype=torch.float32, device=DEV)
+    x_q, x_ds = bl.quant_act(x)
+    nq = torch.full((M, bl.act_stride(N)), 7, dtype=torch.int8, device=DEV)
+    nds = torch.zeros((M,), dtype=torch.float32, device=DEV)
+    cnt = torch.zeros((64,), dtype=torch.uint8, device=DEV)
+    bl.bitlinear_decode_rq(x_q, x_ds, K, [pg, pu], [bg, bu], N, [h], nq, nds, cnt, glu=True)
+    torch.cuda.synchronize()
+    ref = oracle.relu2_mul(oracle_acc_y(xf, wg, False)[1], oracle_acc_y(xf, wu, False)[1])
+    assert_f32_parity(h.cpu().numpy(), ref)
+    q_ref, ds_ref, _ = oracle.quant_act(ref)
+    np.testing.assert_array_equal(nq.cpu().numpy()[:, :N], q_ref)
+    np.testing.assert_array_equal(nds.cpu().numpy(), ds_ref)
+    assert int(torch.count_nonzero(cnt)) == 0
+
+
 # ------------------------------------------------ residual sum in the epilogue
 def oracle_linear_f32(x, w):
     beta = oracle.absmean(w)
@@ -230,7 +295,7 @@ def stack_inputs(n_layers):
     return lat
 
 
-def gpu_stack(lat, M):
+def gpu_stack(lat, M, requant=False):
     layers = []
     for L in lat:
         d = {}
@@ -238,7 +303,7 @@ def gpu_stack(lat, M):
             packed, beta = bl.pack_weights(torch.from_numpy(w).to(DEV))
             d[name] = PackedLinear(packed, beta, w.shape[0], w.shape[1])
         layers.append(d)
-    return DecoderStack(layers, M, DEV)
+    return DecoderStack(layers, M, DEV, requant=requant)
 
 
 def oracle_layer(x, L, cache):
@@ -283,6 +348,23 @@ def test_decode_step_layers_match_oracle(four_layers, M):
         assert_f32_parity(x.cpu().numpy(), xr)
         for name in ("q", "k", "v", "h"):
             assert_f32_parity(getattr(stack, name).cpu().numpy(), parts[name])
+
+
+@pytest.mark.parametrize("M", [8, 33])
+def test_decode_step_requant_matches_oracle(two_layers, M):
+    """The decode step with the next input quantized in each product's
+    epilogue (bitlinear_decode_rq) equals the oracle's chain over two layers."""
+    x0 = workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, workloads.D_MODEL, seed=workloads.DECODER_X0_SEED))
+    stack = gpu_stack(two_layers, M, requant=True)
+    assert stack.requant
+    x = torch.from_numpy(x0).to(DEV)
+    stack.step(x)
+    torch.cuda.synchronize()
+    xr = x0
+    for L in two_layers:
+        xr, _ = oracle_layer(xr, L, {})
+    assert_f32_parity(x.cpu().numpy(), xr)
+    assert int(torch.count_nonzero(stack.rq_ws)) == 0
 
 
 @pytest.mark.parametrize("M", [1, 8])
