@@ -69,6 +69,7 @@ HEADLINE = workloads.DECODE_100B
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_decode_100b_m1.txt")
 KERNEL_SOURCES = ("bitlinear_matmul_02_amd/csrc/gemv.hip", "bitlinear_matmul_02_amd/csrc/bl_internal.h")
 CAL_BYTES = 64 << 20  # calibration copy
+CAL_COPIES = 3  # calibration copies, the first copy dispatches of a counter run
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0  # dense int8 MFMA, MI355X
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, MI355X
@@ -370,7 +371,7 @@ def counters_run(dev):
     # three copies of 64 MiB, each from a source no cache holds: a 1 GiB fill
     # (4x the Infinity Cache) runs before each, so the copy's reads all leave L2
     flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)
-    for _ in range(3):
+    for _ in range(CAL_COPIES):
         src = torch.ones(CAL_BYTES // 4, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
         flush.fill_(1)
@@ -462,13 +463,16 @@ def counter_summary(fetch_csv, write_csv):
     labels = ["%dx%d->%d" % (l.M, l.K, l.N) for l in lins]
     modes = ["fused" if (l.M <= 4 and bl.decode_fits(l.M, l.K)) else "gemv" for l in lins]
     algo = [algorithmic_bytes(l.M, l.K, l.N, m) for l, m in zip(lins, modes)]  # packed + x + fp32 y
-    factors, med, names = {}, {}, {}
+    factors, med, names, cal_kib = {}, {}, {}, {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
-        cal = [v for _, name, _, v in rows if "copyBuffer" in name and v * 1024 > CAL_BYTES / 4]
-        if not cal:
-            raise SystemExit("no calibration copy dispatch in %s" % path)
+        # the calibration copies are the first CAL_COPIES copy dispatches; the
+        # weight rotation copies made later are copies too, of another size
+        cal = [v for _, name, _, v in rows if "copyBuffer" in name][:CAL_COPIES]
+        if len(cal) != CAL_COPIES:
+            raise SystemExit("expected %d calibration copies in %s, found %d" % (CAL_COPIES, path, len(cal)))
         factors[counter] = CAL_BYTES / (float(np.median(cal)) * 1024)
+        cal_kib[counter] = cal
         gemv = [(name, grid, v) for _, name, grid, v in rows if "gemv_t2_kernel" in name]
         if len(gemv) != COUNTER_LAUNCHES * len(lins):
             raise SystemExit("expected %d kernel dispatches in %s, found %d" % (COUNTER_LAUNCHES * len(lins), path, len(gemv)))
@@ -502,8 +506,10 @@ def counter_summary(fetch_csv, write_csv):
         "",
         "calibration: 64 MiB device copies (__amd_rocclr_copyBuffer) in the same run, each after a 1 GiB fill",
         "  so that no cache holds its source;",
-        "  FETCH_SIZE factor %.5f (the counter reads %.0f KiB for 65536 KiB moved)" % (factors["FETCH_SIZE"], 65536 / factors["FETCH_SIZE"]),
-        "  WRITE_SIZE factor %.5f" % factors["WRITE_SIZE"],
+        "  FETCH_SIZE factor %.5f (the copies read %s KiB for 65536 KiB moved each)"
+        % (factors["FETCH_SIZE"], ", ".join("%.1f" % v for v in cal_kib["FETCH_SIZE"])),
+        "  WRITE_SIZE factor %.5f (the copies read %s KiB)"
+        % (factors["WRITE_SIZE"], ", ".join("%.1f" % v for v in cal_kib["WRITE_SIZE"])),
         "",
     ] + lines + [
         "",
@@ -768,6 +774,7 @@ def decode_step(Ms, dev, steps=50, n_layers=workloads.N_LAYERS, stash=None):
                           "weight_GB_s": round(wbytes / t / 1e9, 1),
                           "frac_hbm": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
                           "path": "fused" if stack.fused else ("requantizing GEMV epilogues" if stack.requant
+                                                               else "quant_act + gemv" if stack.gemv
                                                                else "quant_act + gemm"),
                           "oracle_match": "bit-exact" if exact else "rel %.2g" % rel}
         del stack, x, src
