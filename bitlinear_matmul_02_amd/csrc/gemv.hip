@@ -90,12 +90,19 @@ constexpr int tile_steps(int fmt) { return fmt == 1 ? 8 : (fmt == 2 ? 5 : 4); }
 constexpr int tile_cols(int fmt) { return 64 * tile_steps(fmt); }
 
 // Formats with more steps per tile carry more activation operands per tile.
+// Wide plans (4 or more output blocks) keep one k-step of NB tiles in flight:
+// measured on 28672 x 8192 (7 blocks), 12.6 us against 14.2 us with two.
 constexpr int ring_depth(int mb, int nb, int amode, int fmt = 0) {
   return amode == AGLOBAL ? ((tile_steps(fmt) * mb + nb) * 4 <= 24 ? 4 : ((tile_steps(fmt) * mb + nb) * 4 <= 40 ? 2 : 1))
-                          : (nb == 1 ? 8 : (nb == 2 ? 4 : 2));
+                          : (nb == 1 ? 8 : (nb == 2 ? 4 : (nb >= 4 ? 1 : 2)));
 }
 // Largest workgroup, in waves, for MB token blocks.
 constexpr int max_waves(int mb) { return mb <= 2 ? 16 : 8; }
+// The same for MB token blocks and NB output blocks: 4 or more output blocks
+// with one token block are the wide plans, at most kWideWaves waves, which
+// leaves each wave the register file of two waves per SIMD.
+constexpr int kWideWaves = 8;
+constexpr int max_waves(int mb, int nb) { return mb == 1 && nb >= 4 ? kWideWaves : max_waves(mb); }
 
 int64_t lds_row(int64_t K, int fmt = 0) { return ceil_div(K, tile_cols(fmt)) * tile_cols(fmt) + kLdsPad; }
 
@@ -104,15 +111,26 @@ struct GemvPlan {
   int Nt, Kt, Ng;  // output blocks, k-tiles, output groups (Nt / NB)
   int waves, SB;   // waves per workgroup, workgroups per output group
   int tps;         // k-tiles per wave
+  int kint;        // 1: wave w takes k-tiles w, w + waves, ... (else a run of tps)
   int amode;       // where activation operands come from
   int64_t lds_bytes;
   int64_t ws_acc_bytes, ws_bytes;
 };
 
+// Wide plans (one token block, 2-bit tiles, activation rows in LDS, a single
+// matrix of kWideMinNt..kWideMaxNB * 256 output blocks): one workgroup per
+// compute unit owns ceil(Nt / 256) consecutive output blocks, and its
+// kWideWaves waves take interleaved k-tiles (wave w: w, w + 8, ...), so the
+// workgroup sweeps its contiguous range of tiles in address order.  Measured
+// on 28672 x 8192 (1792 blocks of 32 k-tiles): a plain read in this order
+// takes 10.1 us against 11.2 us with 896 workgroups of two blocks (3.5 per
+// unit) and per-wave k-runs.
+constexpr int kWideMinNt = 1024, kWideMaxNB = 8;
+
 // xpieces: 16-byte activation pieces of a fused launch whose rows are whole
-// pieces (0 otherwise).
+// pieces (0 otherwise).  wide: a single matrix, so wide plans may be used.
 GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split = true, int64_t xpieces = 0,
-                   int fmt = 0) {
+                   int fmt = 0, bool wide = false) {
   GemvPlan p{};
   p.MB = (int)ceil_div(M < 1 ? 1 : M, 16);
   p.Nt = (int)ceil_div(N, kTileN);
@@ -120,6 +138,22 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   const int64_t lds = M * lds_row(K, fmt);
   p.amode = fuse ? ALDS_X : (lds <= kDecodeLdsBytes ? ALDS_Q : AGLOBAL);
   p.lds_bytes = p.amode == AGLOBAL ? 0 : lds;
+  p.SB = 1;
+  if (wide && fmt == 0 && p.MB == 1 && p.amode != AGLOBAL && p.Nt >= kWideMinNt &&
+      p.Nt <= (int64_t)kWideMaxNB * kResidentCUs) {
+    p.NB = (int)ceil_div(p.Nt, kResidentCUs);
+    p.Ng = (int)ceil_div(p.Nt, p.NB);
+    // enough threads to hold the activation rows in registers, within the
+    // wide instantiations' launch bound of kWideWaves waves
+    const int64_t need = ceil_div(xpieces, (int64_t)kXReg * 64);
+    if (need <= kWideWaves) {
+      const int waves = p.Kt < kWideWaves ? p.Kt : kWideWaves;
+      p.waves = (int)(waves < need ? need : waves);
+      p.tps = (int)ceil_div(p.Kt, p.waves);
+      p.kint = 1;
+      return p;
+    }
+  }
   // Output blocks per workgroup: each activation operand is reused over NB
   // weight tiles; N decides how many workgroups remain.  The LDS modes cap
   // MB * NB at 4 (4 KB reduction buffer next to the activation rows).
@@ -136,8 +170,9 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   p.Ng = (int)ceil_div(p.Nt, p.NB);
   if (p.amode == ALDS_Q && p.Ng > kResidentCUs * (kLdsPerCU / (lds + kGemvStaticLds))) {
     // the staged rows would leave too few workgroups resident for one
-    // round: read the operands from global memory instead (measured:
-    // 6 x 8192 -> 28672 in 16.4 us against 21.2 us)
+    // round: read the operands from global memory instead (measured on
+    // 6 x 8192 -> 28672 with two-block workgroups: 16.4 us against 21.2 us;
+    // that shape now takes a wide plan, 14.1 us)
     p.amode = AGLOBAL;
     p.lds_bytes = 0;
     p.NB = p.NB > (p.MB > 2 ? 2 : 4) ? (p.MB > 2 ? 2 : 4) : p.NB;
@@ -640,8 +675,10 @@ __host__ __device__ inline int64_t act_col(int kt, int i, int g4, int KT, int64_
 }
 
 template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT), bool RQ = false>
-__global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int KT = tile_cols(FMT), NS = KT / 64;  // columns and MFMA steps per k-tile
+  // wide plans (one token block, 4 or more output blocks): interleaved k-tiles
+  constexpr bool KINT = MB == 1 && NB >= 4 && FMT == 0 && AM != AGLOBAL;
   constexpr int E = MB * NB * 4;  // accumulator values per lane
   constexpr int UA = AM == AGLOBAL ? kU : 1;
   __shared__ int red[E][64];
@@ -658,6 +695,9 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   const int split = sb * waves + wave;
   const int k0 = split * a.tps;
   const int k1 = min(k0 + a.tps, a.Kt);
+  // wide plans: k-tiles wave, wave + waves, ... (ns of them)
+  const int ns = KINT ? (a.Kt > wave ? (a.Kt - wave + waves - 1) / waves : 0) : 0;
+  auto kof = [&](int s) { return wave + s * waves; };
   // Segment of this workgroup (uniform).  The segment fields come from fixed
   // argument offsets and a select on the index, so no argument load waits
   // for the index (each such wait is one more round trip before the first
@@ -731,7 +771,7 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
       }
   };
 
-  const bool has_work = k0 < k1;
+  const bool has_work = KINT ? ns > 0 : k0 < k1;
   // activation pieces first (few, cache-resident), then the weight stream.
   // Rows the threads cannot hold in registers (and rows that are not whole
   // pieces) are quantized completely before the weight loads are issued: a
@@ -756,9 +796,14 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
   // Unconditional, so the wait for the staged pieces never has to assume a
   // path without weight loads (a wave without k-tiles reads tile 0 of its
   // first block, in bounds, and never uses it).
-  const int kfirst = has_work ? k0 : 0, klast = has_work ? k1 - 1 : 0;
+  if constexpr (KINT) {
 #pragma unroll
-  for (int u = 0; u < kU; ++u) load_w(u, min(kfirst + u, klast));
+    for (int u = 0; u < kU; ++u) load_w(u, has_work ? kof(min(u, ns - 1)) : 0);
+  } else {
+    const int kfirst = has_work ? k0 : 0, klast = has_work ? k1 - 1 : 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) load_w(u, min(kfirst + u, klast));
+  }
   // keep the compiler from hoisting work on the staged pieces above the
   // weight loads (that would wait for the pieces before the stream starts)
   __builtin_amdgcn_sched_barrier(0);
@@ -775,7 +820,40 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
     }
   }
 
-  if (has_work) {
+  if (KINT && has_work) {
+    // ring of kU k-steps of NB tiles; each tile is re-loaded right after its
+    // last use, and only while k-steps remain (no re-loads past the end)
+    auto step = [&](int slot, int kt, int ktn, auto reload) {
+      load_a(0, kt);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int i = 0; i < NS; ++i) acc[0][j] = mfma16(abuf[0][0][i], t2_field(wbuf[slot][j], i), acc[0][j]);
+        if constexpr (decltype(reload)::value) {
+          wbuf[slot][j] = __builtin_nontemporal_load(bptr[j] + (int64_t)ktn * 64);
+          // keep the re-load here: scheduled after the whole step, the wave
+          // would wait for every tile in flight before issuing the next ones
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    int s = 0;
+    for (; s + 2 * kU <= ns; s += kU) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) step(u, kof(s + u), kof(s + u + kU), std::true_type{});
+    }
+    const int rem = ns - s;  // k-steps left, in [kU, 2 kU) once ns >= kU
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (u + kU < rem)
+        step(u, kof(s + u), kof(s + u + kU), std::true_type{});
+      else if (u < rem)
+        step(u, kof(s + u), 0, std::false_type{});
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (u + kU < rem) step(u, kof(s + kU + u), 0, std::false_type{});
+  } else if (has_work) {
     // ring of kU k-tiles in flight; re-loads past the end read tile k1-1
     // again (in bounds) and are never used
     if constexpr (AM == AGLOBAL) {
@@ -806,7 +884,8 @@ __global__ __launch_bounds__(64 * max_waves(MB)) void gemv_t2_kernel(const GemvA
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) atomicAdd(&red[(mb * NB + j) * 4 + r][lane], acc[mb][j][r]);
+        for (int r = 0; r < 4; ++r)  // rows mb * 16 + 4 g4 + r: none below M once mb * 16 + r >= M
+          if (mb * 16 + r < M) atomicAdd(&red[(mb * NB + j) * 4 + r][lane], acc[mb][j][r]);
     __syncthreads();
     if (wave != 0) {
       if constexpr (RQ) rq_tail(a);
@@ -988,6 +1067,13 @@ hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   BL_GEMV_CASE(3, 2);  // AGLOBAL, and gated pairs in every mode
   BL_GEMV_CASE(4, 2);
   if constexpr (AM == AGLOBAL && FMT == 0 && !RQ) BL_GEMV_CASE(2, 4);
+  if constexpr (AM != AGLOBAL && FMT == 0 && !RQ) {  // wide plans
+    BL_GEMV_CASE(1, 4);
+    BL_GEMV_CASE(1, 5);
+    BL_GEMV_CASE(1, 6);
+    BL_GEMV_CASE(1, 7);
+    BL_GEMV_CASE(1, 8);
+  }
 #undef BL_GEMV_CASE
   return hipErrorInvalidValue;
 }
@@ -1155,7 +1241,7 @@ bool gemv_prefers_gemm(int64_t M, int64_t N, int64_t K) {
 }
 
 int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  return gemv_prefers_gemm(M, N, K) ? gemm_ws_bytes(M, N, K) : make_plan(M, N, K, false).ws_bytes;
+  return gemv_prefers_gemm(M, N, K) ? gemm_ws_bytes(M, N, K) : make_plan(M, N, K, false, true, 0, 0, true).ws_bytes;
 }
 
 // Host model of the decode kernel's global reads for bitlinear_gemv(_b1,_b3)
@@ -1164,26 +1250,30 @@ int64_t gemv_ws_bytes(int64_t M, int64_t N, int64_t K) {
 // kernel's own offset function, and returns one past the last byte any lane
 // reads of the activations and of the packed weights.
 void gemv_read_extent(int64_t M, int64_t N, int64_t K, int fmt, int64_t ldq, int64_t* act_end, int64_t* w_end) {
-  const GemvPlan p = make_plan(M, N, K, false, fmt == 0, M * (ldq / 16), fmt);
+  const GemvPlan p = make_plan(M, N, K, false, fmt == 0, M * (ldq / 16), fmt, fmt == 0);
   const int KT = tile_cols(fmt), NS = KT / 64;
   int64_t ae = 0, we = 0;
   for (int grp = 0; grp < p.Ng; ++grp)
     for (int sb = 0; sb < p.SB; ++sb)
       for (int wave = 0; wave < p.waves; ++wave) {
-        const int k0 = (sb * p.waves + wave) * p.tps, k1 = std::min(k0 + p.tps, p.Kt);
-        // the prologue's unconditional ring loads read [kfirst, klast]; the
-        // loop's re-loads are clamped to k1 - 1
-        const int kf = k0 < k1 ? k0 : 0, kl = k0 < k1 ? k1 - 1 : 0;
-        for (int j = 0; j < p.NB; ++j) {
-          const int64_t nb = std::min(grp * p.NB + j, p.Nt - 1);
-          we = std::max(we, (nb * p.Kt + kl) * kTileBytes + kTileBytes);
-        }
-        if (p.amode != AGLOBAL || k0 >= k1) continue;
-        const int64_t row = std::min<int64_t>(p.MB * 16 - 1, M - 1) * ldq;
-        for (int kt = kf; kt <= kl; ++kt)
+        // the kernel's k-tiles of this wave: kof(s), s < ns
+        const int split = sb * p.waves + wave;
+        const int kst = p.kint ? p.waves : 1, kb = p.kint ? wave : split * p.tps;
+        const int ns = p.kint ? (p.Kt > wave ? (p.Kt - wave + p.waves - 1) / p.waves : 0)
+                              : std::max(0, std::min(p.tps, p.Kt - kb));
+        // the prologue's unconditional ring loads read kof(0 .. ns - 1) (tile
+        // 0 without work); the loop's re-loads are clamped to kof(ns - 1)
+        for (int s = 0; s < std::max(ns, 1); ++s) {
+          const int kt = ns > 0 ? kb + s * kst : 0;
+          for (int j = 0; j < p.NB; ++j) {
+            const int64_t nb = std::min(grp * p.NB + j, p.Nt - 1);
+            we = std::max(we, (nb * p.Kt + kt) * kTileBytes + kTileBytes);
+          }
+          if (p.amode != AGLOBAL || ns == 0) continue;
+          const int64_t row = std::min<int64_t>(p.MB * 16 - 1, M - 1) * ldq;
           for (int i = 0; i < NS; ++i)
-            for (int g4 = 0; g4 < 4; ++g4)
-              ae = std::max(ae, row + act_col(kt, i, g4, KT, ldq, fmt == 2) + 16);
+            for (int g4 = 0; g4 < 4; ++g4) ae = std::max(ae, row + act_col(kt, i, g4, KT, ldq, fmt == 2) + 16);
+        }
       }
   if (p.amode != AGLOBAL) ae = M * ldq;  // rows staged whole: pieces < M * ldq / 16
   *act_end = ae;
@@ -1198,7 +1288,7 @@ hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t
                           const uint8_t* packed, const float* beta, int64_t N, void* y,
                           int y_dtype, void* ws, hipStream_t s) {
   if (gemv_prefers_gemm(M, N, K)) return launch_gemm_t2(q, ldq, ds, M, K, packed, beta, N, y, y_dtype, ws, s);
-  const GemvPlan p = make_plan(M, N, K, false, true, M * (ldq / 16));
+  const GemvPlan p = make_plan(M, N, K, false, true, M * (ldq / 16), 0, true);
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, ws);
   a.q = q;
   a.ldq = ldq;
@@ -1208,7 +1298,7 @@ hipError_t launch_gemv_t2(const int8_t* q, int64_t ldq, const float* ds, int64_t
 
 hipError_t launch_decode_t2(const void* x, int x_dtype, int64_t M, int64_t K, const uint8_t* packed,
                             const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s) {
-  const GemvPlan p = make_plan(M, N, K, true, true, x_pieces(x, x_dtype, M, K));
+  const GemvPlan p = make_plan(M, N, K, true, true, x_pieces(x, x_dtype, M, K), 0, true);
   GemvArgs a = make_args(p, M, K, N, packed, beta, y, y_dtype, nullptr);
   set_x(a, x, x_dtype, K);
   return dispatch(p, a, s);

@@ -285,7 +285,8 @@ def test_train_validation():
 @pytest.mark.parametrize("fmt", [0, 1, 2])
 @pytest.mark.parametrize("M", [1, 2, 8, 16, 17, 33, 64])
 @pytest.mark.parametrize("N,K", [(16, 256), (40, 700), (512, 512), (100, 3000), (256, 2048), (2560, 6912),
-                                 (28672, 8192), (8192, 28672), (16, 131072), (300, 7), (64, 1000)])
+                                 (28672, 8192), (8192, 28672), (16, 131072), (300, 7), (64, 1000),
+                                 (20000, 8200), (32768, 1000), (17000, 300), (16384, 4096)])
 def test_gemv_reads_stay_in_bounds(fmt, M, N, K):
     size = {0: bl.packed_bytes, 1: bl.packed_bytes_b1, 2: bl.packed_bytes_b3}[fmt]
     act_end, w_end = bl.gemv_read_extent(M, N, K, fmt)

@@ -85,8 +85,11 @@ def test_quant_act_rmsnorm_parity(M, K, src):
     np.testing.assert_array_equal(rs.cpu().numpy(), rs_ref)
 
 
+# (1, 8192, 28672), (3, 1000, 20000) and (2, 1001, 17000) take wide plans (one
+# workgroup per compute unit, interleaved k-tiles); the last with rows that
+# are not whole 16-byte pieces.
 @pytest.mark.parametrize("M,K,N", [(1, 2560, 2560), (1, 6912, 640), (3, 13, 40), (4, 100, 33), (8, 2560, 512),
-                                   (2, 6912, 2560)])
+                                   (2, 6912, 2560), (1, 8192, 28672), (3, 1000, 20000), (2, 1001, 17000)])
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_forward_decode_rmsnorm_parity(M, K, N, src):
     if not bl.decode_fits(M, K):

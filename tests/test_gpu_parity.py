@@ -230,6 +230,23 @@ def test_gemv_large_plans_parity(M, N, K, mode):
                   ref=oracle.bitlinear_forward(xb, w, threads=16))
 
 
+# Wide decode plans: one token block and 1024..2048 output blocks on 2-bit
+# tiles, activation rows staged in LDS (fused, or int8 rows of up to 7 tokens
+# of 8192): one workgroup per compute unit owns ceil(Nt / 256) output blocks
+# and its waves take interleaved k-tiles.  Ragged N (last group clamps its
+# blocks), ragged K (waves with one k-tile more), fewer k-tiles than waves,
+# and 4..8 blocks per workgroup.
+@pytest.mark.parametrize("M,N,K,mode", [(3, 20000, 8200, "gemv"), (7, 16384, 4096, "gemv"), (1, 32768, 1000, "fused"),
+                                        (2, 23000, 6000, "fused"), (5, 17000, 300, "gemv"), (1, 24576, 8192, "gemv"),
+                                        (4, 28672, 8192, "gemv"), (6, 28000, 2000, "fused")])
+def test_gemv_wide_plans_parity(M, N, K, mode):
+    assert 1024 <= -(-N // 16) <= 2048
+    w = workloads.gen_weights(N, K, seed=3300 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=4300 + M, outliers=True)
+    check_product(xb, w, use_gemm=mode if mode == "fused" else False,
+                  ref=oracle.bitlinear_forward(xb, w, threads=16))
+
+
 # ----------------------------------- up to 64 tokens on the int8 matrix cores
 @pytest.mark.parametrize("M,N,K,split", [(1, 1000, 4096, True), (37, 333, 6925, True), (64, 6912, 2560, True),
                                          (24, 130, 2048, True), (17, 2560, 6912, True), (64, 64, 512, False),
@@ -258,8 +275,8 @@ def test_gemm_small_batch_parity(M, N, K, split):
 def test_gemv_large_batches(M, N, K):
     """bitlinear_gemv hands larger batches to the small-batch matrix-core path
     (from 12 tokens on 2^27 weights, 33 on 2^24, 49 on any); results are the
-    same.  6 x 8192 -> 28672 reads its rows from global memory: staged in LDS
-    they would leave too few workgroups resident."""
+    same.  6 x 8192 -> 28672 stages its rows in LDS with one workgroup per
+    compute unit (a wide plan)."""
     w = workloads.gen_weights(N, K, seed=9000 + N)
     xb = workloads.gen_acts_bf16(M, K, seed=9500 + M)
     check_product(xb, w, use_gemm=False, dtypes=("i32", "f32"))
