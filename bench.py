@@ -893,10 +893,22 @@ def prefill_extra(M, shapes, dev, reps=20):
         nq = 100
         elq, _ = timed(L.quant, nq, nq // 4)
         tops = 2.0 * M * N * K / d / 1e12
+        # context, not this library: the platform's int8 GEMM (torch._int_mm,
+        # hipBLASLt) on the same shape with dense int8 weights [N][K] (ternary
+        # values, one byte each) read as B^T, int32 out
+        g = torch.Generator(device=dev).manual_seed(900 + i)
+        a8 = torch.randint(-127, 128, (M, K), generator=g, device=dev, dtype=torch.int8)
+        w8 = torch.randint(-1, 2, (N, K), generator=g, device=dev, dtype=torch.int8)
+        elv, _ = timed(lambda: torch._int_mm(a8, w8.t()), reps, reps)
+        tv = 2.0 * M * N * K / (elv / reps) / 1e12
         res["%dx%d->%d" % (M, K, N)] = {"gemm_us": round(d * 1e6, 1), "TOPS": round(tops, 1),
                                         "frac_mfma": round(tops / INT8_PEAK_TOPS, 4),
-                                        "quant_us": round(elq / nq * 1e6, 2)}
-        del L, packed
+                                        "quant_us": round(elq / nq * 1e6, 2),
+                                        "platform_int8_gemm": {"us": round(elv / reps * 1e6, 1), "TOPS": round(tv, 1),
+                                                               "frac_mfma": round(tv / INT8_PEAK_TOPS, 4),
+                                                               "what": "torch._int_mm (hipBLASLt), dense int8 "
+                                                                       "weights, int32 out"}}
+        del L, packed, a8, w8
         torch.cuda.empty_cache()
     return res
 

@@ -166,6 +166,17 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _record(stream, *tensors):
+    """Tensors allocated on the current stream but used by work enqueued on
+    ``stream``: mark them as used there, so that the caching allocator does
+    not hand their memory out again before that stream's work is done."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 # --------------------------------------------------------------- size helpers
 def act_stride(K: int) -> int:
     return int(lib().bitlinear_act_stride(K))
@@ -416,8 +427,10 @@ def decode_fits(M: int, K: int) -> bool:
 _ws_cache: dict = {}
 
 
-def workspace(nbytes: int, device) -> torch.Tensor | None:
-    """A zero-filled workspace of at least nbytes, cached per device (not stream safe)."""
+def workspace(nbytes: int, device, stream=None) -> torch.Tensor | None:
+    """A zero-filled workspace of at least nbytes, cached per device.  The
+    products leave it zero again; calls on different streams must not overlap
+    (they share it).  ``stream``: the stream the caller's kernels use it on."""
     if nbytes <= 0:
         return None
     key = torch.device(device)
@@ -425,6 +438,7 @@ def workspace(nbytes: int, device) -> torch.Tensor | None:
     if buf is None or buf.numel() < nbytes:
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=key)
         _ws_cache[key] = buf
+    _record(stream, buf)
     return buf
 
 
@@ -434,6 +448,7 @@ def quant_act(x, with_rowsum: bool = False, stream=None, rmsnorm: bool = False):
     x_ds = torch.empty((M,), dtype=torch.float32, device=x.device)
     rs = torch.empty((M,), dtype=torch.int32, device=x.device) if with_rowsum else None
     bitlinear_quant_act(x, x_q, x_ds, rs, stream, rmsnorm=rmsnorm)
+    _record(stream, x_q, x_ds, rs)
     return (x_q, x_ds, rs) if with_rowsum else (x_q, x_ds)
 
 
@@ -443,6 +458,7 @@ def pack_weights(w, stream=None):
     beta = torch.empty((1,), dtype=torch.float32, device=w.device)
     ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
     bitlinear_pack_weights(w, packed, beta, ws, stream)
+    _record(stream, packed, beta, ws)
     return packed, beta
 
 
@@ -452,6 +468,7 @@ def pack_weights_b1(w, stream=None):
     beta = torch.empty((1,), dtype=torch.float32, device=w.device)
     ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
     bitlinear_pack_weights_b1(w, packed, beta, ws, stream)
+    _record(stream, packed, beta, ws)
     return packed, beta
 
 
@@ -461,6 +478,7 @@ def pack_weights_b3(w, stream=None):
     beta = torch.empty((1,), dtype=torch.float32, device=w.device)
     ws = torch.empty((pack_workspace_bytes(N, K),), dtype=torch.uint8, device=w.device)
     bitlinear_pack_weights_b3(w, packed, beta, ws, stream)
+    _record(stream, packed, beta, ws)
     return packed, beta
 
 
@@ -468,14 +486,15 @@ def linear(x, packed, w_beta, N: int, out_dtype=torch.float32, stream=None):
     """BitLinear forward: quantize x [M][K], then gemv (M <= 64) or gemm."""
     M, K = x.shape
     y = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    _record(stream, y)
     if M <= 4 and decode_fits(M, K):
         bitlinear_forward_decode(x, packed, w_beta, N, y, stream)
         return y
     x_q, x_ds = quant_act(x, stream=stream)
     if M <= GEMV_MAX_M:
-        ws = workspace(gemv_workspace_bytes(M, N, K), x.device)
+        ws = workspace(gemv_workspace_bytes(M, N, K), x.device, stream)
         bitlinear_gemv(x_q, x_ds, K, packed, w_beta, N, y, ws, stream)
     else:
-        ws = workspace(gemm_workspace_bytes(M, N, K), x.device)
+        ws = workspace(gemm_workspace_bytes(M, N, K), x.device, stream)
         bitlinear_gemm(x_q, x_ds, K, packed, w_beta, N, y, ws, stream)
     return y

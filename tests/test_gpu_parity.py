@@ -367,3 +367,28 @@ def test_runs_on_a_side_stream():
         y = bl.linear(to_dev_bf16(xb), packed, beta, N, torch.int32)
     s.synchronize()
     np.testing.assert_array_equal(y.cpu().numpy(), ref["acc"])
+
+
+@pytest.mark.parametrize("M", [2, 8, 100])
+def test_stream_argument_keeps_temporaries_alive(M):
+    """Conveniences given a stream other than the current one enqueue there,
+    while their outputs and temporaries come from the current stream's pool:
+    these are recorded on the given stream, so memory freed on return (the
+    pack workspace) or reused by the current stream right after is not handed
+    out while that stream still works on it."""
+    N, K = 512, 2048
+    w = workloads.gen_weights(N, K, seed=14 + M)
+    xb = workloads.gen_acts_bf16(M, K, seed=15 + M)
+    ref = oracle.bitlinear_forward(xb, w)
+    s = torch.cuda.Stream()
+    wd, xd = torch.from_numpy(w).to(DEV), to_dev_bf16(xb)
+    s.wait_stream(torch.cuda.current_stream())
+    packed, beta = bl.pack_weights(wd, stream=s)
+    # the current stream allocates and writes while s may still be packing
+    junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device=DEV) for _ in range(8)]
+    y = bl.linear(xd, packed, beta, N, torch.int32, stream=s)
+    junk += [torch.full((1 << 20,), 9, dtype=torch.int32, device=DEV) for _ in range(8)]
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert beta.cpu().numpy()[0] == ref["beta"]
+    np.testing.assert_array_equal(y.cpu().numpy(), ref["acc"])
