@@ -112,6 +112,7 @@ struct GemvPlan {
   int waves, SB;   // waves per workgroup, workgroups per output group
   int tps;         // k-tiles per wave
   int kint;        // 1: wave w takes k-tiles w, w + waves, ... (else a run of tps)
+  int bigx;        // wide plan whose int8 rows exceed kXReg pieces per thread
   int amode;       // where activation operands come from
   int64_t lds_bytes;
   int64_t ws_acc_bytes, ws_bytes;
@@ -126,6 +127,15 @@ struct GemvPlan {
 // takes 10.1 us against 11.2 us with 896 workgroups of two blocks (3.5 per
 // unit) and per-wave k-runs.
 constexpr int kWideMinNt = 1024, kWideMaxNB = 8;
+// Int8 rows a wide plan may stage in LDS: one workgroup per compute unit
+// leaves the unit's 160 KB to it, less the static reduction buffer (<= 10.5 KB).
+constexpr int64_t kWideLdsBytes = 144 * 1024;
+
+// A single matrix that wide plans cover with rows of lds bytes in LDS.
+bool wide_shape(int64_t M, int64_t Nt, int64_t lds, int fmt, bool fuse) {
+  return fmt == 0 && M >= 1 && M <= 16 && Nt >= kWideMinNt && Nt <= (int64_t)kWideMaxNB * kResidentCUs &&
+         (fuse ? lds <= kDecodeLdsBytes : lds <= kWideLdsBytes);
+}
 
 // xpieces: 16-byte activation pieces of a fused launch whose rows are whole
 // pieces (0 otherwise).  wide: a single matrix, so wide plans may be used.
@@ -139,18 +149,21 @@ GemvPlan make_plan(int64_t M, int64_t N, int64_t K, bool fuse, bool allow_split 
   p.amode = fuse ? ALDS_X : (lds <= kDecodeLdsBytes ? ALDS_Q : AGLOBAL);
   p.lds_bytes = p.amode == AGLOBAL ? 0 : lds;
   p.SB = 1;
-  if (wide && fmt == 0 && p.MB == 1 && p.amode != AGLOBAL && p.Nt >= kWideMinNt &&
-      p.Nt <= (int64_t)kWideMaxNB * kResidentCUs) {
-    p.NB = (int)ceil_div(p.Nt, kResidentCUs);
-    p.Ng = (int)ceil_div(p.Nt, p.NB);
-    // enough threads to hold the activation rows in registers, within the
-    // wide instantiations' launch bound of kWideWaves waves
-    const int64_t need = ceil_div(xpieces, (int64_t)kXReg * 64);
+  if (wide && wide_shape(M, p.Nt, lds, fmt, fuse)) {
+    // fused: enough threads to hold the activation rows in registers, within
+    // the wide instantiations' launch bound of kWideWaves waves (int8 rows
+    // beyond the registers are copied to LDS by a loop instead)
+    const int64_t need = fuse ? ceil_div(xpieces, (int64_t)kXReg * 64) : 1;
     if (need <= kWideWaves) {
+      p.amode = fuse ? ALDS_X : ALDS_Q;
+      p.lds_bytes = lds;
+      p.NB = (int)ceil_div(p.Nt, kResidentCUs);
+      p.Ng = (int)ceil_div(p.Nt, p.NB);
       const int waves = p.Kt < kWideWaves ? p.Kt : kWideWaves;
       p.waves = (int)(waves < need ? need : waves);
       p.tps = (int)ceil_div(p.Kt, p.waves);
       p.kint = 1;
+      p.bigx = !fuse && xpieces > (int64_t)kXReg * 64 * p.waves;
       return p;
     }
   }
@@ -308,20 +321,25 @@ __device__ inline float x_at(const void* x, int dt, int64_t i) {
 // bf16/fp32 rows) goes to v[r] for c = tid + r * blockDim.x.  Threads past
 // the last piece load a duplicate of the last piece (never stored, and a
 // duplicate cannot change a maximum).
-__device__ inline void stage_load(const u4* src, int npieces, u4 (&v)[kXReg]) {
+// With more than kXReg slots, slots wholly past the last piece are skipped
+// (a uniform test): short rows do not issue XR loads per thread.
+template <int XR>
+__device__ inline void stage_load(const u4* src, int npieces, u4 (&v)[XR]) {
   const int tid = threadIdx.x, nthr = blockDim.x;
 #pragma unroll
-  for (int r = 0; r < kXReg; ++r) v[r] = src[min(tid + r * nthr, npieces - 1)];
+  for (int r = 0; r < XR; ++r)
+    if (XR <= kXReg || r * nthr < npieces) v[r] = src[min(tid + r * nthr, npieces - 1)];
 }
 
-// Part 2 for int8 rows: write the held pieces (and any beyond kXReg per
+// Part 2 for int8 rows: write the held pieces (and any beyond XR per
 // thread) to the padded LDS rows.
-__device__ void stage_store_q(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* lds) {
+template <int XR>
+__device__ void stage_store_q(const GemvArgs& a, const u4 (&v)[XR], int8_t* lds) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int cpr = (int)(a.ldq / 16), npieces = a.M * cpr;
   const int rowp = (int)((a.ldl - kLdsPad) / 16);  // pieces of a row the kernel reads
 #pragma unroll
-  for (int r = 0; r < kXReg; ++r) {
+  for (int r = 0; r < XR; ++r) {
     const int c = tid + r * nthr;
     if (c < npieces) {
       const int m = c / cpr, pc = c - m * cpr;
@@ -674,7 +692,8 @@ __host__ __device__ inline int64_t act_col(int kt, int i, int g4, int KT, int64_
   return clamp && c > row_bytes - 16 ? row_bytes - 16 : c;
 }
 
-template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT), bool RQ = false>
+template <int MB, int NB, int AM, bool NORM, int FMT = 0, int kU = ring_depth(MB, NB, AM, FMT), bool RQ = false,
+          bool BIGX = false>
 __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const GemvArgs a) {
   constexpr int KT = tile_cols(FMT), NS = KT / 64;  // columns and MFMA steps per k-tile
   // wide plans (one token block, 4 or more output blocks): interleaved k-tiles
@@ -777,7 +796,10 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
   // pieces) are quantized completely before the weight loads are issued: a
   // loop of activation loads after them would make every later wait cover
   // the whole weight stream.
-  u4 stage[kXReg];
+  // wide plans with long int8 rows (BIGX) hold twice the pieces: those rows
+  // may use most of the unit's LDS, and 8 waves leave the registers for it
+  constexpr int XR = BIGX ? 2 * kXReg : kXReg;
+  u4 stage[XR];
   const int xpieces = a.M * (a.K / (a.x_dtype == BITLINEAR_BF16 ? 8 : 4));
   const bool held = xpieces <= kXReg * (int)blockDim.x;
   if constexpr (AM == ALDS_X) {
@@ -788,7 +810,7 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
   }
   if constexpr (AM == ALDS_XS) quantize_rows_scalar<NORM>(a, act_lds, sq_slots, row_g, row_qs, row_r);
   if constexpr (AM == ALDS_Q) {
-    if (a.M * (int)(a.ldq / 16) <= kXReg * (int)blockDim.x)
+    if (a.M * (int)(a.ldq / 16) <= XR * (int)blockDim.x)
       stage_load(reinterpret_cast<const u4*>(a.q), a.M * (int)(a.ldq / 16), stage);
     else
       copy_rows_q(a, act_lds);
@@ -808,7 +830,7 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
   // weight loads (that would wait for the pieces before the stream starts)
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (AM == ALDS_Q) {
-    if (a.M * (int)(a.ldq / 16) <= kXReg * (int)blockDim.x) stage_store_q(a, stage, act_lds);
+    if (a.M * (int)(a.ldq / 16) <= XR * (int)blockDim.x) stage_store_q(a, stage, act_lds);
   }
   if constexpr (AM == ALDS_X) {
     if (held) {
@@ -1037,18 +1059,20 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
   if constexpr (RQ) rq_tail(a);
 }
 
-template <int MB, int NB, int AM, bool NORM, int FMT = 0, bool RQ = false>
+template <int MB, int NB, int AM, bool NORM, int FMT = 0, bool RQ = false, bool BIGX = false>
 hipError_t launch_t(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   constexpr int KU = ring_depth(MB, NB, AM, FMT);
   if constexpr (AM != AGLOBAL) {
     // static LDS plus the largest activation rows can pass the default 64 KB
     // per workgroup: raise the limit (once per device)
     static LdsLimit lim;
-    const hipError_t attr = ensure_lds_limit(
-        lim, reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT, KU, RQ>), (int)kDecodeLdsBytes);
+    constexpr bool wide = MB == 1 && NB >= 4 && FMT == 0;
+    const hipError_t attr =
+        ensure_lds_limit(lim, reinterpret_cast<const void*>(&gemv_t2_kernel<MB, NB, AM, NORM, FMT, KU, RQ, BIGX>),
+                         (int)(wide ? kWideLdsBytes : kDecodeLdsBytes));
     if (attr != hipSuccess) return attr;
   }
-  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM, FMT, KU, RQ>), dim3((unsigned)(p.Ng * p.SB)),
+  hipLaunchKernelGGL((gemv_t2_kernel<MB, NB, AM, NORM, FMT, KU, RQ, BIGX>), dim3((unsigned)(p.Ng * p.SB)),
                      dim3(64 * p.waves), (size_t)p.lds_bytes, s, a);
   return hipGetLastError();
 }
@@ -1067,6 +1091,16 @@ hipError_t dispatch_mb_nb(const GemvPlan& p, const GemvArgs& a, hipStream_t s) {
   BL_GEMV_CASE(3, 2);  // AGLOBAL, and gated pairs in every mode
   BL_GEMV_CASE(4, 2);
   if constexpr (AM == AGLOBAL && FMT == 0 && !RQ) BL_GEMV_CASE(2, 4);
+  if constexpr (AM == ALDS_Q && FMT == 0 && !RQ) {  // wide plans with long int8 rows
+    if (p.bigx) {
+      if (p.NB == 4) return launch_t<1, 4, AM, NORM, FMT, RQ, true>(p, a, s);
+      if (p.NB == 5) return launch_t<1, 5, AM, NORM, FMT, RQ, true>(p, a, s);
+      if (p.NB == 6) return launch_t<1, 6, AM, NORM, FMT, RQ, true>(p, a, s);
+      if (p.NB == 7) return launch_t<1, 7, AM, NORM, FMT, RQ, true>(p, a, s);
+      if (p.NB == 8) return launch_t<1, 8, AM, NORM, FMT, RQ, true>(p, a, s);
+      return hipErrorInvalidValue;
+    }
+  }
   if constexpr (AM != AGLOBAL && FMT == 0 && !RQ) {  // wide plans
     BL_GEMV_CASE(1, 4);
     BL_GEMV_CASE(1, 5);
@@ -1236,6 +1270,7 @@ hipError_t launch_gemv_b3(const int8_t* q, int64_t ldq, const float* ds, const i
 // beats this kernel: from 49 tokens; from 33 on matrices of 2^24 weights or
 // more; from 12 on 2^27 or more (measured on the 2B- and 100B-class shapes).
 bool gemv_prefers_gemm(int64_t M, int64_t N, int64_t K) {
+  if (wide_shape(M, ceil_div(N, kTileN), M * lds_row(K), 0, false)) return false;  // a wide plan
   const int64_t w = N * K;
   return M > 48 || (M > 32 && w >= (int64_t(1) << 24)) || (M >= 12 && w >= (int64_t(1) << 27));
 }

@@ -236,9 +236,12 @@ def test_gemv_large_plans_parity(M, N, K, mode):
 # and its waves take interleaved k-tiles.  Ragged N (last group clamps its
 # blocks), ragged K (waves with one k-tile more), fewer k-tiles than waves,
 # and 4..8 blocks per workgroup.
+# From 9 tokens of 8192 the int8 rows take 16 pieces per thread (its own
+# instantiation); up to 16 tokens and 144 KB of rows stay on this kernel.
 @pytest.mark.parametrize("M,N,K,mode", [(3, 20000, 8200, "gemv"), (7, 16384, 4096, "gemv"), (1, 32768, 1000, "fused"),
                                         (2, 23000, 6000, "fused"), (5, 17000, 300, "gemv"), (1, 24576, 8192, "gemv"),
-                                        (4, 28672, 8192, "gemv"), (6, 28000, 2000, "fused")])
+                                        (4, 28672, 8192, "gemv"), (6, 28000, 2000, "fused"), (16, 28672, 8192, "gemv"),
+                                        (10, 20000, 8200, "gemv"), (13, 32768, 2048, "gemv"), (9, 16384, 16000, "gemv")])
 def test_gemv_wide_plans_parity(M, N, K, mode):
     assert 1024 <= -(-N // 16) <= 2048
     w = workloads.gen_weights(N, K, seed=3300 + N)
@@ -270,13 +273,15 @@ def test_gemm_small_batch_parity(M, N, K, split):
         assert not ws[:need].any().item()
 
 
-@pytest.mark.parametrize("M,N,K", [(12, 16384, 8192), (24, 16384, 8192), (33, 4096, 4096), (49, 300, 1000),
-                                   (32, 2560, 2560), (11, 16384, 8192), (6, 28672, 8192)])
+@pytest.mark.parametrize("M,N,K", [(12, 8192, 16384), (24, 16384, 8192), (33, 4096, 4096), (49, 300, 1000),
+                                   (32, 2560, 2560), (11, 8192, 16384), (6, 28672, 8192), (12, 16384, 8192),
+                                   (17, 28672, 8192)])
 def test_gemv_large_batches(M, N, K):
     """bitlinear_gemv hands larger batches to the small-batch matrix-core path
-    (from 12 tokens on 2^27 weights, 33 on 2^24, 49 on any); results are the
-    same.  6 x 8192 -> 28672 stages its rows in LDS with one workgroup per
-    compute unit (a wide plan)."""
+    (from 12 tokens on 2^27 weights, 33 on 2^24, 49 on any) unless a wide plan
+    covers them (up to 16 tokens, 1024..2048 output blocks, rows within 144 KB
+    of LDS: 6 and 12 x 8192 -> 16384 / 28672 stay on this kernel, 17 tokens
+    do not); results are the same either way."""
     w = workloads.gen_weights(N, K, seed=9000 + N)
     xb = workloads.gen_acts_bf16(M, K, seed=9500 + M)
     check_product(xb, w, use_gemm=False, dtypes=("i32", "f32"))
