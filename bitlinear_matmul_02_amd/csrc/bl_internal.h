@@ -159,6 +159,31 @@ __device__ inline uint32_t wave_max_u32(uint32_t v) {
   const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
   return max(max(r0, r1), max(r2, r3));
 }
+// fp64 sum over the 64 lanes of a wave by the same DPP pattern (each double
+// moved as two dwords), returned to every lane.  Unlike the integer forms the
+// result depends on the association order; the order is fixed: within each
+// row of 16 lanes, lane 0's ((quad sums 0 + 3) + (2 + 1)) after the quad
+// swaps, then rows 0 + 1 + 2 + 3 in that order.
+template <int CTRL>
+__device__ inline double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline double readlane_f64(double v, int lane) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline double wave_sum_f64(double v) {
+  v += dpp_f64<0xB1>(v);
+  v += dpp_f64<0x4E>(v);
+  v += dpp_f64<0x124>(v);
+  v += dpp_f64<0x128>(v);
+  return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
 __device__ inline int wave_sum_i32(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);
   v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);
@@ -276,8 +301,7 @@ __device__ inline void wave_quant_row_f32(const float* x, int K, bool norm, int8
   amax = wave_max_u32(amax);
   float gamma = __uint_as_float(amax), rn = 1.0f;
   if (norm) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+    s2 = wave_sum_f64(s2);
     rn = 1.0f / sqrtf((float)(s2 / (double)K) + 1e-5f);
     gamma = __fmul_rn(gamma, rn);
   }

@@ -473,22 +473,29 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
     *reinterpret_cast<uint32_t*>(lds + (int64_t)m * a.ldl + a.K + 4 * (i - m * padw)) = 0u;
   }
   constexpr bool norm = NORM;
+  // row of each held piece (-1 past the last piece), and its maximum
+  int prow[kXReg];
+  uint32_t pmax[kXReg];
+#pragma unroll
+  for (int r = 0; r < kXReg; ++r) {
+    const int c = tid + r * nthr;
+    prow[r] = c < npieces ? piece_row(c, M, inv_cpr) : -1;
+    pmax[r] = piece_absmax_bits(v[r], bf16);
+  }
   for (int m = 0; m < M; ++m) {
     uint32_t amax = 0;
     double s2 = 0.0;
 #pragma unroll
     for (int r = 0; r < kXReg; ++r) {
-      const int c = tid + r * nthr;
-      if (c < npieces && piece_row(c, M, inv_cpr) == m) {
-        amax = max(amax, piece_absmax_bits(v[r], bf16));
+      if (prow[r] == m) {
+        amax = max(amax, pmax[r]);
         if (norm) s2 += piece_sumsq(v[r], bf16);
       }
     }
     amax = wave_max_u32(amax);
     if (lane == 0) slots[wave * M + m] = amax;
     if (norm) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+      s2 = wave_sum_f64(s2);
       if (lane == 0) sq[wave * M + m] = s2;
     }
   }
@@ -509,8 +516,7 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
     row_qs[tid] = 127.0f / gm;  // IEEE division, as the standalone quantizer
   }
   __syncthreads();
-  auto quant = [&](const u4 p, int c) {
-    const int m = piece_row(c, M, inv_cpr);
+  auto quant = [&](const u4 p, int c, int m) {
     int8_t* dst = lds + (int64_t)m * a.ldl + (c - m * cpr) * per16;
     if (norm)
       piece_quant_store_norm(p, bf16, row_r[m], row_qs[m], dst);
@@ -518,10 +524,8 @@ __device__ void stage_store_x(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* l
       piece_quant_store(p, bf16, row_qs[m], dst);
   };
 #pragma unroll
-  for (int r = 0; r < kXReg; ++r) {
-    const int c = tid + r * nthr;
-    if (c < npieces) quant(v[r], c);
-  }
+  for (int r = 0; r < kXReg; ++r)
+    if (prow[r] >= 0) quant(v[r], tid + r * nthr, prow[r]);
   __syncthreads();
 }
 
@@ -550,8 +554,7 @@ __device__ void stage_store_x1(const GemvArgs& a, const u4 (&v)[kXReg], int8_t* 
   }
   amax = wave_max_u32(amax);
   if (NORM) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+    s2 = wave_sum_f64(s2);
   }
   if (lane == 0) {
     slots[wave] = amax;
@@ -607,13 +610,11 @@ __device__ void quantize_rows_scalar(const GemvArgs& a, int8_t* lds, double* sq,
       amax = fmaxf(amax, fabsf(xv));
       if (norm) s2 += (double)xv * (double)xv;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    amax = __uint_as_float(wave_max_u32(__float_as_uint(amax)));  // amax >= 0: bits order like values
     // |x| >= 0, so the fp32 bit patterns order like the values
     if (lane == 0) atomicMax(reinterpret_cast<unsigned int*>(&row_g[m]), __float_as_uint(amax));
     if (norm) {
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+      s2 = wave_sum_f64(s2);
       if (lane == 0) sq[wave * M + m] = s2;
     }
   }

@@ -134,8 +134,7 @@ __device__ inline int block_sum(int v, int* slots) {
 
 template <int NT>
 __device__ inline double block_sum_f64(double v, double* slots) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_sum_f64(v);
   if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = v;
   __syncthreads();
   double r = 0.0;
