@@ -17,7 +17,11 @@
 // per lane of each of its NB weight tiles (one coalesced 1 KB load each, kU
 // k-tiles ahead of use), expands each 2-bit field into an MFMA operand and
 // issues 4 * MB * NB MFMA 16x16x64 steps.  The waves add their partial sums
-// with LDS atomics; wave 0 dequantizes and stores.
+// with LDS atomics; wave 0 dequantizes and stores.  Wide plans (one token
+// block, 1024..2048 output blocks) run one workgroup per compute unit over
+// ceil(Nt / 256) blocks instead, with interleaved k-tiles (wave w takes w,
+// w + waves, ...), so that the workgroup reads its tile range in address
+// order; their int8 rows may use most of the unit's LDS.
 //
 // Activation operands (the int8 token rows) come from one of three places:
 //   ALDS_Q  the workgroup copies the int8 rows into LDS once (16-byte loads,
