@@ -357,10 +357,16 @@ def decode_workload(wl, args, dev, roofline=True):
 
 # ------------------------------------------------------- HBM traffic counters
 def kernel_source_hash():
+    """Hash of the decode kernel's sources with comments and whitespace
+    removed: an edit of a comment does not make the measured traffic stale."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -89,3 +89,22 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=300)
     assert r.returncode != 0
     assert "one GPU" in r.stderr
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    def tree(extra_comment, code_change):
+        d = tmp_path / ("t%d%d" % (extra_comment, code_change))
+        for rel in bench.KERNEL_SOURCES:
+            src = open(os.path.join(ROOT, rel)).read()
+            if extra_comment:
+                src = "// a new comment line\n" + src.replace("\n", "\n  /* and a block */ ", 1)
+            if code_change:
+                src += "\nint added_symbol;\n"
+            p = d / rel
+            p.parent.mkdir(parents=True, exist_ok=True)
+            p.write_text(src)
+        monkeypatch.setattr(bench, "ROOT", str(d))
+        return bench.kernel_source_hash()
+    base = tree(False, False)
+    assert tree(True, False) == base
+    assert tree(False, True) != base
