@@ -241,13 +241,23 @@ def test_gemv_large_plans_parity(M, N, K, mode):
 @pytest.mark.parametrize("M,N,K,mode", [(3, 20000, 8200, "gemv"), (7, 16384, 4096, "gemv"), (1, 32768, 1000, "fused"),
                                         (2, 23000, 6000, "fused"), (5, 17000, 300, "gemv"), (1, 24576, 8192, "gemv"),
                                         (4, 28672, 8192, "gemv"), (6, 28000, 2000, "fused"), (16, 28672, 8192, "gemv"),
-                                        (10, 20000, 8200, "gemv"), (13, 32768, 2048, "gemv"), (9, 16384, 16000, "gemv")])
+                                        (10, 20000, 8200, "gemv"), (13, 32768, 2048, "gemv"), (9, 16384, 16000, "gemv"),
+                                        (16, 16384, 8192, "gemv"), (1, 32768, 8192, "fused"), (2, 16383, 4096, "gemv")])
 def test_gemv_wide_plans_parity(M, N, K, mode):
     assert 1024 <= -(-N // 16) <= 2048
     w = workloads.gen_weights(N, K, seed=3300 + N)
     xb = workloads.gen_acts_bf16(M, K, seed=4300 + M, outliers=True)
     check_product(xb, w, use_gemm=mode if mode == "fused" else False,
                   ref=oracle.bitlinear_forward(xb, w, threads=16))
+
+
+def test_gemv_just_past_the_wide_plans():
+    """2049 output blocks (N = 32784) take the two-block plan again; results
+    are the same."""
+    M, N, K = 3, 32784, 1024
+    w = workloads.gen_weights(N, K, seed=3400)
+    xb = workloads.gen_acts_bf16(M, K, seed=4400, outliers=True)
+    check_product(xb, w, use_gemm=False, dtypes=("i32", "f32"), ref=oracle.bitlinear_forward(xb, w, threads=16))
 
 
 # ----------------------------------- up to 64 tokens on the int8 matrix cores
