@@ -393,6 +393,18 @@ __device__ inline uint32_t piece_absmax_bits(const u4 v, bool bf16) {
 __device__ inline uint32_t qbyte(float x, float qs) {
   return __float_as_uint(__fadd_rn(__fmul_rn(x, qs), 12582912.0f)) & 0xffu;
 }
+// The same word before the mask (the code is its low byte), and the low
+// bytes of four such words packed in order by byte permutes (v_perm_b32
+// picks bytes of {S0, S1}, S1 bytes 0..3, S0 bytes 4..7, selector 12 = zero):
+// three operations per four codes instead of masks and shifts.
+__device__ inline uint32_t qword(float x, float qs) {
+  return __float_as_uint(__fadd_rn(__fmul_rn(x, qs), 12582912.0f));
+}
+__device__ inline uint32_t pack_low_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);  // a0, b0, 0, 0
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);  // c0, d0, 0, 0
+  return __builtin_amdgcn_perm(cd, ab, 0x05040100u);              // a0, b0, c0, d0
+}
 
 // Quantize one 16-byte piece (8 bf16 or 4 fp32 values) into LDS at dst.
 __device__ inline void piece_quant_store(const u4 v, bool bf16, float qs, int8_t* dst) {
@@ -400,14 +412,13 @@ __device__ inline void piece_quant_store(const u4 v, bool bf16, float qs, int8_t
     uint32_t w[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      w[h] = qbyte(__uint_as_float(v[2 * h] << 16), qs) | (qbyte(__uint_as_float(v[2 * h] & 0xffff0000u), qs) << 8) |
-             (qbyte(__uint_as_float(v[2 * h + 1] << 16), qs) << 16) |
-             (qbyte(__uint_as_float(v[2 * h + 1] & 0xffff0000u), qs) << 24);
+      w[h] = pack_low_bytes(qword(__uint_as_float(v[2 * h] << 16), qs), qword(__uint_as_float(v[2 * h] & 0xffff0000u), qs),
+                            qword(__uint_as_float(v[2 * h + 1] << 16), qs),
+                            qword(__uint_as_float(v[2 * h + 1] & 0xffff0000u), qs));
     *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
   } else {
-    *reinterpret_cast<uint32_t*>(dst) = qbyte(__uint_as_float(v[0]), qs) | (qbyte(__uint_as_float(v[1]), qs) << 8) |
-                                        (qbyte(__uint_as_float(v[2]), qs) << 16) |
-                                        (qbyte(__uint_as_float(v[3]), qs) << 24);
+    *reinterpret_cast<uint32_t*>(dst) = pack_low_bytes(qword(__uint_as_float(v[0]), qs), qword(__uint_as_float(v[1]), qs),
+                                                       qword(__uint_as_float(v[2]), qs), qword(__uint_as_float(v[3]), qs));
   }
 }
 
