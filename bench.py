@@ -327,6 +327,18 @@ def decode_workload(wl, args, dev, roofline=True):
     per_w = sum(L.weight_bytes() for L in linears)
     per_alg = sum(L.traffic_bytes() for L in linears)
     durs = [kernel_duration(L) for L in linears]
+    # one BitLinear call as the host sees it: enqueue, then wait for it
+    # (eager, median of 50, each call on the next weight copy)
+    single = []
+    for L in linears:
+        ts = []
+        for _ in range(50):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            L.step()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        single.append(float(np.median(ts)))
     # the same step with the standalone quantizer (two launches per BitLinear)
     split = [Linear(L.M, L.K, L.N, L.packed, L.beta, L.x, mode="gemv") for L in linears]
     el_split, _ = timed(lambda: [L.step() for L in split], args.steps, args.warmup)
@@ -337,6 +349,7 @@ def decode_workload(wl, args, dev, roofline=True):
         "rotation_bytes_per_shape": [len(L.packed) * L.weight_bytes() for L in linears],
         "unfused_us_per_step": round(el_split / args.steps * 1e6, 2),
         "kernel_us": {"%dx%d->%d" % (L.M, L.K, L.N): round(d * 1e6, 3) for L, d in zip(linears, durs)},
+        "single_call_us": {"%dx%d->%d" % (L.M, L.K, L.N): round(t * 1e6, 2) for L, t in zip(linears, single)},
         "mode": linears[0].mode,
     }
     if roofline:
@@ -970,6 +983,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": head["roofline"],
         "kernel_us": head["kernel_us"],
+        "single_call_us": head["single_call_us"],
         "unfused_us_per_step": head["unfused_us_per_step"],
     }
     shapes_2b = [(l.K, l.N) for l in workloads.DECODE_2B.linears]
