@@ -567,15 +567,17 @@ def host_cpu():
     return {"os_cpu_count": os.cpu_count(), "model": model, "threads_used": THREADS}
 
 
-def time_reps(fn, budget, min_reps=1):
-    """(reps, seconds) of repeated fn() calls until `budget` seconds have passed."""
-    reps, t0 = 0, time.perf_counter()
+def time_reps(fn, budget, min_reps=3):
+    """(reps, seconds, median seconds per call) of repeated fn() calls until
+    `budget` seconds have passed and at least min_reps calls were made."""
+    ts, t0 = [], time.perf_counter()
     while True:
+        t1 = time.perf_counter()
         fn()
-        reps += 1
+        ts.append(time.perf_counter() - t1)
         el = time.perf_counter() - t0
-        if reps >= min_reps and el >= budget:
-            return reps, el
+        if len(ts) >= min_reps and el >= budget:
+            return len(ts), el, float(np.median(ts))
 
 
 def oracle_decode(prepared, threads):
@@ -626,13 +628,13 @@ def cpu_baseline(head_prepared, stash):
     thread where the sample is small): decode in GB/s of packed weights, the
     decoder step in tokens/s, prefill in int8 TOPS (2 M N K per product)."""
     per_w = sum(t.size // 4 for t, _, _ in head_prepared)
-    reps, el = time_reps(oracle_decode(head_prepared, THREADS), 6.0)
-    reps1, el1 = time_reps(oracle_decode(head_prepared, 1), 3.0)
-    res = {"value": round(per_w * reps / el / 1e9, 3), "unit": "GB/s", "cores": THREADS, "kind": "oracle",
-           "sample": "%d decode steps (quantize + int32 product + dequant, both 100B shapes, M=1) in %.1f s"
-                     % (reps, el),
-           "value_1thread": round(per_w * reps1 / el1 / 1e9, 3),
-           "sample_1thread": "%d steps on one thread in %.1f s" % (reps1, el1),
+    reps, el, med = time_reps(oracle_decode(head_prepared, THREADS), 6.0)
+    reps1, el1, med1 = time_reps(oracle_decode(head_prepared, 1), 3.0)
+    res = {"value": round(per_w / med / 1e9, 3), "unit": "GB/s", "cores": THREADS, "kind": "oracle",
+           "sample": "median of %d decode steps (quantize + int32 product + dequant, both 100B shapes, M=1), "
+                     "%.1f s in all" % (reps, el),
+           "value_1thread": round(per_w / med1 / 1e9, 3),
+           "sample_1thread": "median of %d steps on one thread, %.1f s in all" % (reps1, el1),
            "host": host_cpu()}
     cfg = {}
 
@@ -641,13 +643,13 @@ def cpu_baseline(head_prepared, stash):
         prep = [(t, b, workloads.gen_acts_bf16(M, K, seed=seed + 50 + i, outliers=outliers))
                 for i, ((t, b), (K, N)) in enumerate(zip(codes, shapes))]
         wbytes = sum(N * K // 4 for K, N in shapes)
-        r, e = time_reps(oracle_decode(prep, THREADS), budget)
-        row = {"GB_s": round(wbytes * r / e / 1e9, 3), "us_per_step": round(e / r * 1e6, 1),
-               "sample": "%d steps of M=%d in %.2f s" % (r, M, e)}
+        r, e, m = time_reps(oracle_decode(prep, THREADS), budget)
+        row = {"GB_s": round(wbytes / m / 1e9, 3), "us_per_step": round(m * 1e6, 1),
+               "sample": "median of %d steps of M=%d, %.2f s in all" % (r, M, e)}
         if one_thread:
-            r1, e1 = time_reps(oracle_decode(prep, 1), budget)
-            row["GB_s_1thread"] = round(wbytes * r1 / e1 / 1e9, 3)
-            row["us_per_step_1thread"] = round(e1 / r1 * 1e6, 1)
+            r1, e1, m1 = time_reps(oracle_decode(prep, 1), budget)
+            row["GB_s_1thread"] = round(wbytes / m1 / 1e9, 3)
+            row["us_per_step_1thread"] = round(m1 * 1e6, 1)
         cfg[name] = row
 
     def prefill_cfg(name, shapes, M, sample_m, seed, codes=None):
@@ -670,13 +672,14 @@ def cpu_baseline(head_prepared, stash):
     if "terns" in stash:
         x0s = stash["x0"]
         for M, one in ((1, True), (8, False)):
-            r, e = time_reps(lambda: oracle_chain(stash["terns"], x0s[M], THREADS), 1.0)
-            row = {"tok_s": round(M * r / e, 2), "us_per_step": round(e / r * 1e6, 1),
-                   "sample": "%d steps of the %d-layer chain, M=%d, in %.2f s" % (r, len(stash["terns"]), M, e)}
+            r, e, m = time_reps(lambda: oracle_chain(stash["terns"], x0s[M], THREADS), 1.0)
+            row = {"tok_s": round(M / m, 2), "us_per_step": round(m * 1e6, 1),
+                   "sample": "median of %d steps of the %d-layer chain, M=%d, %.2f s in all"
+                             % (r, len(stash["terns"]), M, e)}
             if one:
-                r1, e1 = time_reps(lambda: oracle_chain(stash["terns"], x0s[M], 1), 1.0)
-                row["tok_s_1thread"] = round(M * r1 / e1, 3)
-                row["us_per_step_1thread"] = round(e1 / r1 * 1e6, 1)
+                r1, e1, m1 = time_reps(lambda: oracle_chain(stash["terns"], x0s[M], 1), 1.0)
+                row["tok_s_1thread"] = round(M / m1, 3)
+                row["us_per_step_1thread"] = round(m1 * 1e6, 1)
             cfg["decode_step_2b_30l_m%d" % M] = row
     prefill_cfg("prefill_2b_m2048", shapes_2b, 2048, 256, 9200)
     codes_100b = [(t, b) for t, b, _ in head_prepared]
