@@ -5,6 +5,11 @@
 Every source is compiled by hipcc for gfx950 with no fast-math, no floating
 point contraction, correctly rounded fp32 division, and packed-fp32 ALU ops
 disabled; the objects are linked into bitlinear_matmul_02_amd/lib/.
+
+A second library, libbitlinear_lds_poison.so, is the same sources built with
+-DBL_LDS_POISON: its kernels poison their LDS before first use (and the
+prefill GEMM each consumed staging buffer), a self-test of the barriers and
+offsets that the GPU tests run against the oracle.  Nothing else loads it.
 """
 from __future__ import annotations
 
@@ -20,6 +25,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIB_DIR, "libbitlinear.so")
+POISON_LIB = os.path.join(LIB_DIR, "libbitlinear_lds_poison.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -32,30 +38,41 @@ FLAGS = [
 SOURCES = ["abi.cpp", "quant_act.hip", "pack.hip", "gemv.hip", "gemm.hip", "glue.hip", "train.hip", "noalloc.hip"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra: tuple = ()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs: list, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, poison: bool = True) -> str:
+    """Build libbitlinear.so and (poison=True) the LDS self-test library."""
+    variants = [(BUILD, (), LIB)]
+    if poison:
+        variants.append((BUILD + "_lds_poison", ("-DBL_LDS_POISON",), POISON_LIB))
+    for d, _, _ in variants:
+        os.makedirs(d, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    jobs = max(1, min(8, os.cpu_count() or 1))
+    work = [(src, d, extra) for d, extra, _ in variants for src in SOURCES]
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda w: _compile(*w), work))
+    for i, (_, _, lib) in enumerate(variants):
+        _link(objs[i * len(SOURCES):(i + 1) * len(SOURCES)], lib)
+        if verbose:
+            print("built", lib)
     return LIB
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, poison="--no-poison" not in sys.argv)
     sys.exit(0)

@@ -193,6 +193,28 @@ __device__ inline int wave_sum_i32(int v) {
          __builtin_amdgcn_readlane(v, 48);
 }
 
+// LDS race self-test.  A build compiled with -DBL_LDS_POISON (the library's
+// own build never defines it) fills the LDS of every kernel that stages data
+// there with a poison pattern before the first use, and the prefill GEMM
+// poisons each staging buffer again once it has been consumed.  A read of LDS
+// that no thread of the workgroup wrote in this launch and stage (a missing
+// barrier, a wrong offset) then returns the pattern instead of a previous
+// launch's or stage's bytes, which can be the right ones when the same call
+// repeats, and the result no longer matches.
+#ifdef BL_LDS_POISON
+constexpr bool kLdsPoison = true;
+#else
+constexpr bool kLdsPoison = false;
+#endif
+constexpr uint32_t kLdsPoisonWord = 0xA5A5A5A5u;  // int8 -91; fp32 about -2.9e-16
+
+// Poison `bytes` (a multiple of 4) of LDS at p, strided over the workgroup's
+// threads; the caller adds the barrier.
+__device__ inline void lds_poison(void* p, int bytes) {
+  uint32_t* w = static_cast<uint32_t*>(p);
+  for (int i = threadIdx.x; i < bytes / 4; i += blockDim.x) w[i] = kLdsPoisonWord;
+}
+
 // Raises a kernel's dynamic LDS limit on the current device, once per device
 // (the attribute belongs to the device that is current when it is set).
 struct LdsLimit {

@@ -223,6 +223,28 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
     }
   };
 
+  // LDS self-test builds: poison both halves before the first stage, and each
+  // half again (this thread's own staging slots, so in program order before
+  // its next data) once the barrier after its k-step has passed
+  if constexpr (kLdsPoison) {
+    lds_poison(lds, G::LDS);
+    __syncthreads();
+  }
+  auto repoison = [&](int buf) {
+    if constexpr (kLdsPoison) {
+#pragma unroll
+      for (int i = 0; i < G::PA; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          reinterpret_cast<uint32_t*>(slabA(buf) + (i * G::NT + tid) * 16)[w] = kLdsPoisonWord;
+#pragma unroll
+      for (int i = 0; i < G::PB; ++i)
+#pragma unroll
+        for (int w = 0; w < G::BP / 4; ++w)
+          reinterpret_cast<uint32_t*>(slabB(buf) + (i * G::NT + tid) * G::BP)[w] = kLdsPoisonWord;
+    }
+  };
+
   // prologue: k-steps 0 .. D-1 requested (indices past the end re-read the
   // last k-step, in bounds, never used); k-step 0 into LDS half 0
 #pragma unroll
@@ -240,6 +262,7 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
       load(u, kt0 + min(kt + D, nk - 1));  // slot u (k-step kt) went to LDS during the previous k-step
       compute(kt & 1, true, (u + 1) % D);
       __syncthreads();
+      repoison(kt & 1);
     }
   }
   // the last 1..D k-steps (already requested)
@@ -249,6 +272,7 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
     if (kt < nk) {  // uniform
       compute(kt & 1, kt + 1 < nk, (u + 1) % D);
       __syncthreads();
+      repoison(kt & 1);
     }
   }
 
@@ -274,6 +298,10 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
   // last k-step ended with a barrier), loaded once before any output store:
   // a global load between the stores would wait for every store issued
   // before it (vmcnt retires in order).
+  if constexpr (kLdsPoison) {
+    lds_poison(lds, G::LDS);
+    __syncthreads();
+  }
   float* s_ds = reinterpret_cast<float*>(lds);
   int* s_rs = reinterpret_cast<int*>(lds + BM * 4);
   const float bt = *beta;

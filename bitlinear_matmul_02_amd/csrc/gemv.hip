@@ -724,6 +724,15 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
   __shared__ double sq_slots[NORM ? max_waves(MB) * 16 * MB : 1];  // per-wave, per-row sums of squares
   extern __shared__ __attribute__((aligned(16))) int8_t act_lds[];  // [M][ldl]
 
+  if constexpr (kLdsPoison) {  // LDS self-test builds
+    lds_poison(&red[0][0], (int)sizeof(red));
+    lds_poison(row_g, (int)sizeof(row_g));
+    lds_poison(row_qs, (int)sizeof(row_qs));
+    lds_poison(row_r, (int)sizeof(row_r));
+    lds_poison(sq_slots, (int)sizeof(sq_slots));
+    if (AM != AGLOBAL) lds_poison(act_lds, (int)(a.M * a.ldl));
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63, waves = blockDim.x >> 6;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int grp = blockIdx.x / a.SB, sb = blockIdx.x - grp * a.SB;

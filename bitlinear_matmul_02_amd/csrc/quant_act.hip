@@ -161,6 +161,12 @@ __global__ __launch_bounds__(NT) void quant_act_kernel(const void* __restrict__ 
   __shared__ uint32_t slots_max[NT / 64];
   __shared__ int slots_sum[NT / 64];
   __shared__ double slots_sq[NORM ? NT / 64 : 1];
+  if constexpr (kLdsPoison) {  // LDS self-test builds
+    lds_poison(slots_max, (int)sizeof(slots_max));
+    lds_poison(slots_sum, (int)sizeof(slots_sum));
+    lds_poison(slots_sq, (int)sizeof(slots_sq));
+    __syncthreads();
+  }
   const bool bf16 = bf16i != 0;
   const int64_t m = blockIdx.x;
   const int tid = threadIdx.x;

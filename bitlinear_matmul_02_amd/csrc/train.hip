@@ -164,6 +164,10 @@ __global__ __launch_bounds__(TrainTile<BIG>::NT) void train_gemm_kernel(const Tr
   // A (and B) is stored transposed, as [r][row], when its source rows run along r
   constexpr bool AT = MODE == DW, BT = MODE != FWD;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [buffer][A, B][OPND]
+  if constexpr (kLdsPoison) {  // LDS self-test builds
+    lds_poison(lds, G::LDS);
+    __syncthreads();
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wp = wave / G::WQN, wq = wave % G::WQN;

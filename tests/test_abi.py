@@ -27,6 +27,19 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(bl.EXPORTS)
 
 
+def test_lds_self_test_library_exports_the_same_symbols():
+    """The LDS-poisoned build (the same sources with -DBL_LDS_POISON, loaded
+    only by the GPU self-test) is built beside the library and exports the
+    same ABI."""
+    from bitlinear_matmul_02_amd import build as bl_build
+    assert os.path.exists(bl_build.POISON_LIB), bl_build.POISON_LIB
+    L = ctypes.CDLL(bl_build.POISON_LIB)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    L.bitlinear_version.restype = ctypes.c_int
+    assert L.bitlinear_version() == bl.lib().bitlinear_version()
+
+
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     consts = dict(re.findall(r"#define (BITLINEAR_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
