@@ -1010,8 +1010,11 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
     return;
   }
   const float bt = *sg.beta;
-  if constexpr (FUSED) {
-    // the row scales are in LDS: no global load between the stores
+  if constexpr (FUSED && NB < 4) {
+    // one or two output blocks: the row scales are in LDS and a type switch
+    // per element stays a short run of code (measured no slower here than
+    // the single dispatch below; 6912 -> 2560 at one token 4.65 against 4.8
+    // us)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -1030,8 +1033,13 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
       }
   } else {
     // Every row scale is read before the first store (a global load between
-    // stores would wait for all of them: vmcnt retires in order), and the
-    // output type is dispatched once, outside the store loops.
+    // stores would wait for all of them: vmcnt retires in order; fused
+    // launches hold them in LDS), and the output type is dispatched once,
+    // outside the store loops: with many output blocks (the wide plans) a
+    // type switch per element spreads the epilogue over far-apart code
+    // blocks, and every workgroup reaches it with those instruction lines
+    // not yet cached (on 8192 -> 28672 at one token that alone held each
+    // workgroup ~0.4 us after its reduction).
     float scale[MB][4];
     int rsv[MB][4];
 #pragma unroll
@@ -1041,7 +1049,8 @@ __global__ __launch_bounds__(64 * max_waves(MB, NB)) void gemv_t2_kernel(const G
         const int m = mb * 16 + 4 * g4 + r;
         scale[mb][r] = 0.0f, rsv[mb][r] = 0;
         if (m < M) {
-          scale[mb][r] = a.ds[m] * bt;
+          // fused: g of the (normalized) row from the prologue, ds = g / 127
+          scale[mb][r] = (FUSED ? row_g[m] / 127.0f : a.ds[m]) * bt;
           rsv[mb][r] = FMT ? a.rowsum[m] : 0;
         }
       }
