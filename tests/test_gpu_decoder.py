@@ -256,7 +256,10 @@ def oracle_linear_f32(x, w):
 
 
 @pytest.mark.parametrize("path", ["gemv", "gemm", "fused"])
-@pytest.mark.parametrize("M,K,N", [(1, 2560, 2560), (3, 700, 333), (8, 6912, 2560), (130, 512, 300)])
+# (2, 1000, 20000) takes a wide plan (1250 output blocks, one workgroup per
+# compute unit), whose epilogue dispatches the output type once
+@pytest.mark.parametrize("M,K,N", [(1, 2560, 2560), (3, 700, 333), (8, 6912, 2560), (130, 512, 300),
+                                   (2, 1000, 20000)])
 def test_accumulate_output(path, M, K, N):
     if path != "gemm" and M > bl.GEMV_MAX_M:
         pytest.skip("decode paths take at most 64 tokens")
