@@ -50,7 +50,11 @@
 // that leaves fewer workgroups than compute units the k-steps are split
 // across S workgroups per block: each writes its int32 sums to a workspace
 // slice [S][M][N] and a second kernel adds the S slices and dequantizes.
-// Integer sums are exact in any order, so the result equals the unsplit one.
+// Up to 32 tokens on wide outputs, 32 x 128 blocks split each k-step's
+// matrix-core steps between two halves of the workgroup instead (four waves
+// each, one 32 x 32 tile per wave), which add their sums in LDS: no
+// workspace and no second launch.  Integer sums are exact in any order, so
+// every split gives the unsplit result.
 #include <type_traits>
 
 #include "bl_internal.h"
@@ -58,11 +62,13 @@
 namespace bl {
 namespace {
 
-template <int BM, int BN, int FMT = 0>
+template <int BM, int BN, int FMT = 0, int KS = 1>
 struct GemmTile {
+  static constexpr int WGK = KS;                       // waves along k (halves of each k-step's MFMA steps)
   static constexpr int WGM = BM >= 64 ? 2 : 1;         // waves along M
-  static constexpr int WGN = 8 / WGM;                  // waves along N
-  static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
+  static constexpr int WGN = 8 / (WGM * WGK);          // waves along N
+  static constexpr int NT = 64 * WGM * WGN * WGK;     // threads per workgroup
+  static constexpr int SPW = 8 / WGK;                 // MFMA steps per wave per k-step
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave block
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 MFMA tiles per wave
   static constexpr int SLAB_A = BM * kTileK;          // activation slab bytes
@@ -82,7 +88,7 @@ __device__ inline v4i b1_bytes(uint32_t bits16) {
   return r;
 }
 
-template <int BM, int BN, int D, int FMT, bool SPLIT>
+template <int BM, int BN, int D, int FMT, bool SPLIT, int KS = 1>
 __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__ q, int64_t ldq,
                                                       const float* __restrict__ ds,
                                                       const int32_t* __restrict__ rowsum, int M,
@@ -90,7 +96,8 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
                                                       const float* __restrict__ beta, int N, int Nt,
                                                       int Kt, int KtW, int tiles_n, void* __restrict__ y,
                                                       int y_dtype, int splits, int32_t* __restrict__ part) {
-  using G = GemmTile<BM, BN, FMT>;
+  using G = GemmTile<BM, BN, FMT, KS>;
+  static_assert(KS == 1 || !SPLIT, "one split of k at a time");
   using BT = typename std::conditional<FMT != 0, uint2, u4>::type;  // one weight piece
   constexpr int MB = G::MB, NB = G::NB;
   extern __shared__ __attribute__((aligned(16))) int8_t lds[];
@@ -100,7 +107,9 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
-  const int wm = wave / G::WGN, wn = wave % G::WGN;
+  // wave = (wk * WGM + wm) * WGN + wn; wk takes MFMA steps wk * SPW .. of each k-step
+  const int wk = wave / (G::WGM * G::WGN), wmn = wave - wk * (G::WGM * G::WGN);
+  const int wm = wmn / G::WGN, wn = wmn % G::WGN;
   // within an XCD's run of tiles, walk groups of GM token blocks along N
   constexpr int GM = 4;
   // SPLIT: the XCD's run covers consecutive tiles of one split (one k-range),
@@ -193,7 +202,10 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
 
   // One k-step: 8 MFMA steps s = 2f + h, software-pipelined; the next
   // k-step's pieces are written to the other LDS half along the way.
-  auto compute = [&](int buf, bool stage_next, int unext) {
+  // (KS = 2: each half of the workgroup takes 4 of the 8 steps; the step
+  // index must stay a compile-time constant, so the half is dispatched once)
+  auto compute_half = [&](int buf, bool stage_next, int unext, auto half) {
+    constexpr int SPW = G::SPW, ST0 = decltype(half)::value * SPW;
     BT wch[NB][2];
 #pragma unroll
     for (int j = 0; j < NB; ++j)
@@ -201,26 +213,33 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
       for (int h = 0; h < 2; ++h) wch[j][h] = *reinterpret_cast<const BT*>(slabB(buf) + boff[j][h]);
     v4i a[2][MB];
     v4i b[2][NB];
-    read_a(a[0], buf, 0);
+    read_a(a[0], buf, ST0);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) b[0][j] = expand(wch[j], 0);
+    for (int j = 0; j < NB; ++j) b[0][j] = expand(wch[j], ST0);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int cur = st & 1, nx = cur ^ 1;
-      if (st + 1 < 8) {
+    for (int u = 0; u < SPW; ++u) {
+      const int st = ST0 + u, cur = u & 1, nx = cur ^ 1;
+      if (u + 1 < SPW) {
         read_a(a[nx], buf, st + 1);
 #pragma unroll
         for (int j = 0; j < NB; ++j) b[nx][j] = expand(wch[j], st + 1);
       }
       if (stage_next) {
 #pragma unroll
-        for (int i = st * (G::PA + G::PB) / 8; i < (st + 1) * (G::PA + G::PB) / 8; ++i) stage_piece(unext, buf ^ 1, i);
+        for (int i = u * (G::PA + G::PB) / SPW; i < (u + 1) * (G::PA + G::PB) / SPW; ++i)
+          stage_piece(unext, buf ^ 1, i);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) acc[mb][j] = mfma32(a[cur][mb], b[cur][j], acc[mb][j]);
     }
+  };
+  auto compute = [&](int buf, bool stage_next, int unext) {
+    if (KS == 1 || wk == 0)
+      compute_half(buf, stage_next, unext, std::integral_constant<int, 0>{});
+    else
+      compute_half(buf, stage_next, unext, std::integral_constant<int, KS == 1 ? 0 : 1>{});
   };
 
   // LDS self-test builds: poison both halves before the first stage, and each
@@ -310,6 +329,30 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
     if constexpr (FMT != 0) s_rs[tid] = rowsum[min(m0 + tid, M - 1)];
   }
   __syncthreads();
+  if constexpr (KS == 2) {
+    // the second half of the workgroup hands its sums to the first through
+    // LDS (behind the row scales; the slabs are free) and is done
+    constexpr int PW = G::WGM * G::WGN * 64;  // lanes of one half
+    static_assert(1024 + MB * NB * 16 * PW * 4 <= G::LDS && BM * 8 <= 1024, "LDS of the k-split exchange");
+    int* xch = reinterpret_cast<int*>(lds + 1024);
+    const int slot = wmn * 64 + lane;
+    if (wk == 1) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) xch[((mb * NB + j) * 16 + e) * PW + slot] = acc[mb][j][e];
+    }
+    __syncthreads();
+    if (wk == 1) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mb][j][e] += xch[((mb * NB + j) * 16 + e) * PW + slot];
+  }
   // this lane's row scales, all read before the first store
   float scale[MB][16];
   int rsv[MB][16];
@@ -371,19 +414,19 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(int32_t* __restrict__ 
   store_out(y, y_dtype, i, v, scale);
 }
 
-template <int BM, int BN, int D, int FMT, bool SPLIT = false>
+template <int BM, int BN, int D, int FMT, bool SPLIT = false, int KS = 1>
 hipError_t launch_tile(const int8_t* q, int64_t ldq, const float* ds, const int32_t* rowsum, int64_t M, int64_t K,
                        const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
                        int splits = 1, int32_t* part = nullptr) {
-  using G = GemmTile<BM, BN, FMT>;
+  using G = GemmTile<BM, BN, FMT, KS>;
   static LdsLimit lim;
-  const hipError_t attr = ensure_lds_limit(lim, reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT, SPLIT>),
-                                           G::LDS);
+  const hipError_t attr =
+      ensure_lds_limit(lim, reinterpret_cast<const void*>(&gemm_t2_kernel<BM, BN, D, FMT, SPLIT, KS>), G::LDS);
   if (attr != hipSuccess) return attr;
   const int Nt = (int)ceil_div(N, kTileN), Kt = (int)ceil_div(K, kTileK);
   const int KtW = (int)ceil_div(K, FMT ? kTileKB1 : kTileK);
   const int tiles_n = (int)ceil_div(N, BN), tiles_m = (int)ceil_div(M, BM);
-  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D, FMT, SPLIT>), dim3((unsigned)(tiles_m * tiles_n * splits)),
+  hipLaunchKernelGGL((gemm_t2_kernel<BM, BN, D, FMT, SPLIT, KS>), dim3((unsigned)(tiles_m * tiles_n * splits)),
                      dim3(G::NT), G::LDS, s, q, ldq, ds, rowsum, (int)M, packed, beta, (int)N, Nt, Kt, KtW, tiles_n,
                      y, y_dtype, splits, part);
   if (!SPLIT) return hipGetLastError();
@@ -406,7 +449,16 @@ int mid_splits(int64_t M, int64_t N, int64_t K, int bm, int bn) {
   const int64_t per = ceil_div(Kt, S);
   return (int)ceil_div(Kt, per);
 }
+// Up to 32 tokens, when the 32 x 256 blocks would split k across workgroups
+// but 32 x 128 blocks alone occupy at least half of the compute units (N of
+// 16384 and more): 32 x 128 blocks with k split inside the workgroup.
+constexpr int kSmallKsN = 128;
+bool small_ks(int64_t M, int64_t N, int64_t K) {
+  return M <= kSmallM && mid_splits(M, N, K, kSmallM, kSmallN) > 1 &&
+         ceil_div(M, kSmallM) * ceil_div(N, kSmallKsN) * 2 >= kMidGrid;
+}
 int mid_splits(int64_t M, int64_t N, int64_t K) {
+  if (small_ks(M, N, K)) return 1;
   return M <= kSmallM ? mid_splits(M, N, K, kSmallM, kSmallN) : mid_splits(M, N, K, kMidM, kMidN);
 }
 
@@ -426,6 +478,9 @@ hipError_t launch_fmt(const int8_t* q, int64_t ldq, const float* ds, const int32
                       const uint8_t* packed, const float* beta, int64_t N, void* y, int y_dtype, hipStream_t s,
                       void* ws = nullptr) {
   if constexpr (FMT == 0) {
+    if (small_ks(M, N, K))
+      return launch_tile<kSmallM, kSmallKsN, 3, FMT, false, 2>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype,
+                                                               s);
     if (M <= kSmallM)
       return launch_mid<kSmallM, kSmallN, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, ws);
     if (M <= kMidM) return launch_mid<kMidM, kMidN, FMT>(q, ldq, ds, rowsum, M, K, packed, beta, N, y, y_dtype, s, ws);
