@@ -108,8 +108,10 @@ __global__ __launch_bounds__(512) void gemm_t2_kernel(const int8_t* __restrict__
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   // wave = (wk * WGM + wm) * WGN + wn; wk takes MFMA steps wk * SPW .. of each k-step
-  const int wk = wave / (G::WGM * G::WGN), wmn = wave - wk * (G::WGM * G::WGN);
-  const int wm = wmn / G::WGN, wn = wmn % G::WGN;
+  // (KS = 1: the index arithmetic of the unsplit blocks, unchanged)
+  const int wk = KS == 1 ? 0 : wave / (G::WGM * G::WGN);
+  const int wmn = KS == 1 ? wave : wave - wk * (G::WGM * G::WGN);
+  const int wm = (KS == 1 ? wave : wmn) / G::WGN, wn = (KS == 1 ? wave : wmn) % G::WGN;
   // within an XCD's run of tiles, walk groups of GM token blocks along N
   constexpr int GM = 4;
   // SPLIT: the XCD's run covers consecutive tiles of one split (one k-range),
