@@ -257,9 +257,10 @@ def oracle_linear_f32(x, w):
 
 @pytest.mark.parametrize("path", ["gemv", "gemm", "fused"])
 # (2, 1000, 20000) takes a wide plan (1250 output blocks, one workgroup per
-# compute unit), whose epilogue dispatches the output type once
+# compute unit), whose epilogue dispatches the output type once; (20, 2000,
+# 20000) on the product takes 32 x 128 blocks with k split inside the workgroup
 @pytest.mark.parametrize("M,K,N", [(1, 2560, 2560), (3, 700, 333), (8, 6912, 2560), (130, 512, 300),
-                                   (2, 1000, 20000)])
+                                   (2, 1000, 20000), (20, 2000, 20000)])
 def test_accumulate_output(path, M, K, N):
     if path != "gemm" and M > bl.GEMV_MAX_M:
         pytest.skip("decode paths take at most 64 tokens")

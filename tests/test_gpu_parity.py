@@ -283,6 +283,19 @@ def test_gemm_small_batch_parity(M, N, K, split):
         assert not ws[:need].any().item()
 
 
+# Up to 32 tokens on 16384 or more outputs, where the 32 x 256 blocks would
+# split k across workgroups, the blocks are 32 x 128 and each workgroup's two
+# halves take half of every k-step's matrix-core steps, adding their sums in
+# LDS: no workspace.  Ragged N and K, one token, and every output mode.
+@pytest.mark.parametrize("M,N,K", [(1, 17000, 3000), (5, 20000, 2000), (17, 16400, 2048), (32, 16384, 8192),
+                                   (31, 30000, 2100)])
+def test_gemm_small_batch_k_split_in_workgroup(M, N, K):
+    assert bl.gemm_workspace_bytes(M, N, K) == 0
+    w = workloads.gen_weights(N, K, seed=7500 + N)
+    xb = workloads.gen_acts_bf16(M, K, seed=8500 + M, outliers=True)
+    check_product(xb, w, use_gemm=True, ref=oracle.bitlinear_forward(xb, w, threads=16))
+
+
 @pytest.mark.parametrize("M,N,K", [(12, 8192, 16384), (24, 16384, 8192), (33, 4096, 4096), (49, 300, 1000),
                                    (32, 2560, 2560), (11, 8192, 16384), (6, 28672, 8192), (12, 16384, 8192),
                                    (17, 28672, 8192)])
