@@ -47,7 +47,11 @@ from . import (GEMV_MAX_M, act_stride, bitlinear_decode_rq, bitlinear_forward_de
                gemm_workspace_bytes, gemv_workspace_bytes)
 
 NAMES = ("q", "k", "v", "o", "gate", "up", "down")
-FUSED_MAX_M = 4
+# Measured on MI355X (30-layer 2B-class step, fused against standalone
+# quantizer + product): 638 / 854 us at 1 token, 879 / 913 at 2, 974 / 936 at
+# 3, 1169 / 976 at 4: beyond 2 tokens every workgroup re-quantizing the rows
+# costs more than the launch it saves.
+FUSED_MAX_M = 2
 
 
 class PackedLinear:

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import bitlinear_matmul_02_amd as bl
+from bitlinear_matmul_02_amd import decoder
 from bitlinear_matmul_02_amd.decoder import NAMES, DecoderStack, PackedLinear
 import oracle
 import workloads
@@ -341,11 +342,11 @@ def four_layers():
     return stack_inputs(4)
 
 
-@pytest.mark.parametrize("M", list(workloads.DECODE_STEP_BATCHES) + [3, 64, 80])
+@pytest.mark.parametrize("M", list(workloads.DECODE_STEP_BATCHES) + [2, 3, 64, 80])
 def test_decode_step_layers_match_oracle(four_layers, M):
     x0 = workloads.bf16_bits_to_f32(workloads.gen_acts_bf16(M, workloads.D_MODEL, seed=workloads.DECODER_X0_SEED))
     stack = gpu_stack(four_layers, M)
-    assert stack.fused == (M <= 4)
+    assert stack.fused == (M <= decoder.FUSED_MAX_M)
     x = torch.from_numpy(x0).to(DEV)
     xr = x0
     for l, L in enumerate(four_layers):
